@@ -1,0 +1,189 @@
+"""fp64 CPU oracle for paged decode attention and the KV-cache write.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The product path
+(``paged_kv_attention_24_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C99, double precision, built by
+gcc with OpenMP); this module only marshals numpy arrays into it.  What it
+computes, for every sequence b and query head hq with L = context_lens[b]
+(PhotonInfer README, Korean translation, "Technical details > Paged
+attention"; the stable softmax of "Key features > GPU-optimised kernels"):
+
+    out[b, hq] = sum_{t<L} softmax_t(scale * q[b, hq] . K_t) V_t,
+    K_t = k_cache[block_tables[b, t // bs], hq // G, t % bs, :]
+
+with G = num_q_heads // num_kv_heads.  Every function here is pinned by the
+``-m "not gpu"`` tests in ``tests/test_oracle.py`` (closed forms, invariants,
+torch's fp64 scaled-dot-product attention on a contiguous copy, exhaustive
+decoder checks).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+STATUS = {0: "ok", 1: "bad argument", 2: "block id out of range",
+          3: "context length exceeds the block table", 4: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, -O2, OpenMP)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib(path: Optional[str] = None):
+    """Load (building first if absent) and return the ctypes handle."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _declare(h):
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    h.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    h.oracle_f16_to_f64.restype = f64
+    h.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    h.oracle_bf16_to_f64.restype = f64
+    h.oracle_decode_array.argtypes = [P, ctypes.c_int, i64, P]
+    h.oracle_decode_array.restype = None
+    h.oracle_paged_attention_decode.argtypes = [
+        P, P, P, P, ctypes.c_int, P, i32, P, i32, i32, i32, i32, i32, i32, f64, i32,
+        P, i32, i32]
+    h.oracle_paged_attention_decode.restype = ctypes.c_int
+    h.oracle_kv_cache_write.argtypes = [P, P, i64, i64, P, i32, P, P, i32, i32, i32, i32, i32]
+    h.oracle_kv_cache_write.restype = ctypes.c_int
+    return h
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check_stored(a: np.ndarray, dtype: str, what: str):
+    want = np.float32 if dtype == "f32" else np.uint16
+    if a.dtype != want:
+        raise TypeError(f"{what}: expected {np.dtype(want)} storage for {dtype}, got {a.dtype}")
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError(f"{what} must be C-contiguous")
+
+
+def decode_values(bits: np.ndarray, dtype: str, handle=None) -> np.ndarray:
+    """Stored elements -> float64 through the oracle's own decoders."""
+    h = handle or lib()
+    a = np.ascontiguousarray(bits)
+    _check_stored(a, dtype, "bits")
+    out = np.empty(a.size, dtype=np.float64)
+    h.oracle_decode_array(_ptr(a), DTYPE_CODE[dtype], a.size, _ptr(out))
+    return out.reshape(a.shape)
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
+                           num_kv_heads, block_size, dtype, *, rows=None,
+                           partition_size: int = 0, threads: int = 0,
+                           handle=None) -> np.ndarray:
+    """fp64 decode.  Arrays hold stored bits (float32 or uint16).
+
+    q [B, Hq, D]; k_cache, v_cache [NB, Hkv, bs, D]; block_tables int32
+    [B, MB]; context_lens int32 [B].  ``rows`` (optional, int array [n, 2] of
+    (b, hq) pairs) restricts the computation to those rows; the result is then
+    [n, D], else [B, Hq, D].  ``partition_size`` > 0 assembles each row from
+    partitions (the split identity), 0 evaluates the definition directly.
+    ``scale`` is widened to double as given (pass the float32 value the
+    device receives).
+    """
+    h = handle or lib()
+    _check_stored(q, dtype, "q")
+    _check_stored(k_cache, dtype, "k_cache")
+    _check_stored(v_cache, dtype, "v_cache")
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or D2 != D or Hkv != num_kv_heads or bs != block_size:
+        raise ValueError("cache shape does not match the arguments")
+    if bt.ndim != 2 or bt.shape[0] != B or cl.shape != (B,):
+        raise ValueError("block_tables / context_lens do not match q")
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        out = np.empty((r.shape[0], D), dtype=np.float64)
+        rp, nr = _ptr(r), r.shape[0]
+    else:
+        r = None
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    rc = h.oracle_paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), DTYPE_CODE[dtype], _ptr(bt),
+        bt.shape[1], _ptr(cl), B, Hq, Hkv, D, NB, bs, float(scale), int(partition_size),
+        rp, nr, int(threads))
+    if rc != 0:
+        raise OracleError(f"oracle decode failed: {STATUS.get(rc, rc)}")
+    return out
+
+
+def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, dtype, handle=None) -> None:
+    """In-place bitwise write of k, v [T, Hkv, D] (token stride = row length of
+    the given arrays' first axis) into the pools at ``slot_mapping``."""
+    h = handle or lib()
+    for a, w in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        want = np.float32 if dtype == "f32" else np.uint16
+        if a.dtype != want:
+            raise TypeError(f"{w}: expected {np.dtype(want)} storage")
+    if not (k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]):
+        raise ValueError("caches must be C-contiguous")
+    NB, Hkv, bs, D = k_cache.shape
+    T = k.shape[0]
+    item = k.itemsize
+    for a in (k, v):
+        if a.shape[1:] != (Hkv, D) or a.strides[2] != item or a.strides[1] != D * item:
+            raise ValueError("k/v must be [T, Hkv, D] with contiguous heads")
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    rc = h.oracle_kv_cache_write(
+        _ptr(k), _ptr(v), k.strides[0] // item if T else Hkv * D,
+        v.strides[0] // item if T else Hkv * D, _ptr(sm), T, _ptr(k_cache), _ptr(v_cache),
+        NB, bs, Hkv, D, item)
+    if rc != 0:
+        raise OracleError(f"oracle write failed: {STATUS.get(rc, rc)}")
+
+
+def decode_workload(wl, *, rows=None, partition_size=0, threads=0, after_write=True,
+                    handle=None):
+    """Oracle decode of a workloads.Workload; applies its write first (on
+    copies of the pools) when it carries new tokens and after_write is set."""
+    kc, vc = wl.k_cache, wl.v_cache
+    if after_write and wl.new_k is not None:
+        kc, vc = kc.copy(), vc.copy()
+        kv_cache_write(wl.new_k, wl.new_v, wl.slot_mapping, kc, vc, wl.dtype, handle=handle)
+    return paged_attention_decode(
+        wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, wl.num_kv_heads,
+        wl.block_size, wl.dtype, rows=rows, partition_size=partition_size,
+        threads=threads, handle=handle)

@@ -1,0 +1,329 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for batched paged-attention decode and
+ * the multi-sequence KV-cache write.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header
+ * or constant with the HIP library it checks, and it is written to be read,
+ * not to be fast: every output row is computed straight from the definition.
+ *
+ * What is computed (PhotonInfer README, Korean translation, section
+ * "Technical details > Paged attention", and "Key features > GPU-optimised
+ * kernels"): the KV cache lives in fixed-size blocks; each sequence reaches
+ * its tokens through its own block list; one query token per sequence
+ * attends over that sequence's cached tokens; the softmax is the
+ * numerically stable (max-subtracted) one.  The result is the plain
+ * definition
+ *
+ *     out[b, hq, :] = sum_t softmax_t(scale * q[b, hq, :] . K_t) * V_t
+ *
+ * over the first L = context_lens[b] tokens of sequence b, gathered through
+ * block_tables[b, :], evaluated in double precision from the exact values of
+ * the stored bits.
+ *
+ * Pool layout: K and V pools are [num_blocks, num_kv_heads, block_size,
+ * head_dim], row-major.  Token t of sequence b sits in physical block
+ * block_tables[b, t / block_size] at offset t % block_size.
+ * Query head hq reads kv head hq / (num_q_heads / num_kv_heads) (contiguous
+ * grouping of query heads onto kv heads).
+ *
+ * Readings where the pages are silent: L <= 0 yields an all-zero row;
+ * a write slot < 0 is padding and is skipped; a write slot at or beyond
+ * num_blocks * block_size is skipped as well.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_F16 1
+#define ORACLE_BF16 2
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARGUMENT 1
+#define ORACLE_BAD_BLOCK_ID 2
+#define ORACLE_BAD_CONTEXT_LEN 3
+#define ORACLE_NO_MEMORY 4
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Written from the format's definition. */
+double oracle_f16_to_f64(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);              /* subnormal: frac * 2^-24 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/2^10) * 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32: 1 sign bit, 8 exponent
+ * bits (bias 127), 7 fraction bits.  Decoded field by field as well. */
+double oracle_bf16_to_f64(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 7) & 0xff;
+    int frac = bits & 0x7f;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -133);             /* frac * 2^-7 * 2^-126 */
+    else if (expo == 255)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(128 + frac), expo - 134); /* (1 + frac/2^7) * 2^(e-127) */
+    return sign ? -mag : mag;
+}
+
+static double load_elem(const void *base, int dtype, int64_t index)
+{
+    if (dtype == ORACLE_F32) {
+        float f;
+        memcpy(&f, (const char *)base + 4 * index, 4);
+        return (double)f;
+    }
+    uint16_t h;
+    memcpy(&h, (const char *)base + 2 * index, 2);
+    return dtype == ORACLE_F16 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);
+}
+
+/* Decode n stored elements to double (used to check the decoders). */
+void oracle_decode_array(const void *src, int dtype, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = load_elem(src, dtype, i);
+}
+
+typedef struct {
+    const void *q, *k_cache, *v_cache;
+    int dtype;
+    const int32_t *block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+    int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int32_t num_blocks, block_size;
+    double scale;
+} decode_args;
+
+/* Index of element (block, head, offset, d) in a pool. */
+static int64_t pool_index(const decode_args *a, int64_t block, int h, int off, int d)
+{
+    return ((block * a->num_kv_heads + h) * a->block_size + off) * (int64_t)a->head_dim + d;
+}
+
+/* Physical block holding logical token t of sequence b (-1 if invalid). */
+static int64_t block_of(const decode_args *a, int b, int64_t t)
+{
+    int64_t blk = a->block_tables[(int64_t)b * a->max_blocks_per_seq + t / a->block_size];
+    if (blk < 0 || blk >= a->num_blocks)
+        return -1;
+    return blk;
+}
+
+static int check_row(const decode_args *a, int b)
+{
+    int64_t L = a->context_lens[b];
+    if (L > (int64_t)a->max_blocks_per_seq * a->block_size)
+        return ORACLE_BAD_CONTEXT_LEN;
+    for (int64_t t = 0; t < L; t += a->block_size)
+        if (block_of(a, b, t) < 0)
+            return ORACLE_BAD_BLOCK_ID;
+    return ORACLE_OK;
+}
+
+/* scale * (q . K_t) for the tokens [t0, t1) of sequence b, kv head h. */
+static void logits(const decode_args *a, int b, int hq, int h, int64_t t0, int64_t t1,
+                   double *s)
+{
+    int64_t qbase = ((int64_t)b * a->num_q_heads + hq) * a->head_dim;
+    for (int64_t t = t0; t < t1; ++t) {
+        int64_t blk = block_of(a, b, t);
+        int off = (int)(t % a->block_size);
+        double dot = 0.0;
+        for (int d = 0; d < a->head_dim; ++d)
+            dot += load_elem(a->q, a->dtype, qbase + d) *
+                   load_elem(a->k_cache, a->dtype, pool_index(a, blk, h, off, d));
+        s[t - t0] = a->scale * dot;
+    }
+}
+
+/* Softmax-weighted sum of V over the tokens [t0, t1): writes the normalised
+ * row to o[0..D) and returns the max logit and the sum of exp(s - max). */
+static void softmax_v(const decode_args *a, int b, int h, int64_t t0, int64_t t1,
+                      double *s, double *o, double *m_out, double *l_out)
+{
+    int64_t n = t1 - t0;
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i)
+        if (s[i] > m)
+            m = s[i];
+    double l = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        s[i] = exp(s[i] - m); /* s now holds the unnormalised weights */
+        l += s[i];
+    }
+    for (int d = 0; d < a->head_dim; ++d) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t t = t0 + i;
+            int64_t blk = block_of(a, b, t);
+            int off = (int)(t % a->block_size);
+            acc += s[i] * load_elem(a->v_cache, a->dtype, pool_index(a, blk, h, off, d));
+        }
+        o[d] = acc / l;
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+static int decode_row(const decode_args *a, int b, int hq, int32_t partition_size,
+                      double *out_row)
+{
+    int group = a->num_q_heads / a->num_kv_heads;
+    int h = hq / group;
+    int64_t L = a->context_lens[b];
+    if (L <= 0) {
+        for (int d = 0; d < a->head_dim; ++d)
+            out_row[d] = 0.0;
+        return ORACLE_OK;
+    }
+    int rc = check_row(a, b);
+    if (rc != ORACLE_OK)
+        return rc;
+    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    if (!s)
+        return ORACLE_NO_MEMORY;
+    if (partition_size <= 0) {
+        /* The definition itself: one softmax over all L tokens. */
+        double m, l;
+        logits(a, b, hq, h, 0, L, s);
+        softmax_v(a, b, h, 0, L, s, out_row, &m, &l);
+    } else {
+        /* The same result assembled from independent partitions of
+         * partition_size tokens: partition j gives its max m_j, its sum l_j
+         * and its normalised row o_j; with M = max_j m_j and
+         * w_j = l_j exp(m_j - M), out = sum_j w_j o_j / sum_j w_j
+         * (the log-sum-exp identity). */
+        int64_t nparts = (L + partition_size - 1) / partition_size;
+        double *pm = (double *)malloc(sizeof(double) * (size_t)nparts);
+        double *pl = (double *)malloc(sizeof(double) * (size_t)nparts);
+        double *po = (double *)malloc(sizeof(double) * (size_t)nparts * a->head_dim);
+        if (!pm || !pl || !po) {
+            free(pm); free(pl); free(po); free(s);
+            return ORACLE_NO_MEMORY;
+        }
+        double M = -INFINITY;
+        for (int64_t j = 0; j < nparts; ++j) {
+            int64_t t0 = j * partition_size;
+            int64_t t1 = t0 + partition_size < L ? t0 + partition_size : L;
+            logits(a, b, hq, h, t0, t1, s);
+            softmax_v(a, b, h, t0, t1, s, po + j * a->head_dim, &pm[j], &pl[j]);
+            if (pm[j] > M)
+                M = pm[j];
+        }
+        double wsum = 0.0;
+        for (int64_t j = 0; j < nparts; ++j)
+            wsum += pl[j] * exp(pm[j] - M);
+        for (int d = 0; d < a->head_dim; ++d) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < nparts; ++j)
+                acc += pl[j] * exp(pm[j] - M) * po[j * a->head_dim + d];
+            out_row[d] = acc / wsum;
+        }
+        free(pm); free(pl); free(po);
+    }
+    free(s);
+    return ORACLE_OK;
+}
+
+/*
+ * Decode every (sequence, q head) row, or only the rows listed in `rows`
+ * (n_rows pairs b, hq; then out is [n_rows, head_dim]).  out is double.
+ * partition_size <= 0 evaluates the definition in one pass; > 0 assembles it
+ * from partitions (a self-check of the split identity).  num_threads <= 0
+ * leaves the OpenMP default.  Returns ORACLE_OK or the first error seen.
+ */
+int oracle_paged_attention_decode(double *out, const void *q, const void *k_cache,
+                                  const void *v_cache, int dtype,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t num_blocks, int32_t block_size, double scale,
+                                  int32_t partition_size, const int32_t *rows, int32_t n_rows,
+                                  int32_t num_threads)
+{
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16 || num_seqs < 0 || num_kv_heads <= 0 ||
+        num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return ORACLE_BAD_ARGUMENT;
+    decode_args a = {q, k_cache, v_cache, dtype, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     num_blocks, block_size, scale};
+    int64_t n = rows ? n_rows : (int64_t)num_seqs * num_q_heads;
+    if (rows) {
+        for (int64_t r = 0; r < n; ++r)
+            if (rows[2 * r] < 0 || rows[2 * r] >= num_seqs || rows[2 * r + 1] < 0 ||
+                rows[2 * r + 1] >= num_q_heads)
+                return ORACLE_BAD_ARGUMENT;
+    }
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : omp_get_max_threads())
+    for (int64_t r = 0; r < n; ++r) {
+        int b = rows ? rows[2 * r] : (int)(r / num_q_heads);
+        int hq = rows ? rows[2 * r + 1] : (int)(r % num_q_heads);
+        int rc = decode_row(&a, b, hq, partition_size, out + r * head_dim);
+        if (rc != ORACLE_OK) {
+#pragma omp critical
+            status = status == ORACLE_OK ? rc : status;
+        }
+    }
+    return status;
+}
+
+/*
+ * The multi-sequence KV-cache write (same README section: one batched
+ * operation stores the new K/V rows of many sequences).  For each new token
+ * i with slot s = slot_mapping[i] in [0, num_blocks * block_size):
+ * block = s / block_size, offset = s % block_size, and for every kv head h
+ * the head_dim elements k[i, h, :] are copied bit for bit to
+ * k_cache[block, h, offset, :]; the same for v.  Rows of k and v are
+ * token_stride elements apart, heads head_dim apart.  Every other byte of
+ * both caches is left as it was.
+ */
+int oracle_kv_cache_write(const void *k, const void *v, int64_t k_token_stride,
+                          int64_t v_token_stride, const int64_t *slot_mapping,
+                          int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                          int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t elt_bytes)
+{
+    if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || (elt_bytes != 2 && elt_bytes != 4))
+        return ORACLE_BAD_ARGUMENT;
+    if (num_tokens > 0 && (!k || !v || !slot_mapping || !k_cache || !v_cache))
+        return ORACLE_BAD_ARGUMENT;
+    size_t row = (size_t)head_dim * elt_bytes;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int64_t s = slot_mapping[i];
+        if (s < 0 || s >= (int64_t)num_blocks * block_size)
+            continue;
+        int64_t blk = s / block_size, off = s % block_size;
+        for (int h = 0; h < num_kv_heads; ++h) {
+            int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * head_dim;
+            memcpy((char *)k_cache + dst * elt_bytes,
+                   (const char *)k + ((int64_t)i * k_token_stride + (int64_t)h * head_dim) * elt_bytes,
+                   row);
+            memcpy((char *)v_cache + dst * elt_bytes,
+                   (const char *)v + ((int64_t)i * v_token_stride + (int64_t)h * head_dim) * elt_bytes,
+                   row);
+        }
+    }
+    return ORACLE_OK;
+}

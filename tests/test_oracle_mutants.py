@@ -1,0 +1,69 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case copies oracle.c, plants one mistake by a textual substitution
+(a dropped term, a wrong sign, a wrong index, swapped operands, a wrong
+exponent bias), builds the copy with gcc in a temporary directory and runs
+every pin against it: at least one pin must fail.  Nothing here touches the
+committed oracle or a GPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    # query head -> kv head grouping taken as interleaved instead of contiguous
+    "gqa_interleaved": ("int h = hq / group;", "int h = hq % a->num_kv_heads;"),
+    # block-table column taken from the offset
+    "table_index": ("[(int64_t)b * a->max_blocks_per_seq + t / a->block_size]",
+                    "[(int64_t)b * a->max_blocks_per_seq + t % a->max_blocks_per_seq]"),
+    # wrong in-block offset when reading K
+    "k_offset": ("        int off = (int)(t % a->block_size);\n        double dot",
+                 "        int off = (int)((t + 1) % a->block_size);\n        double dot"),
+    # head and offset swapped in the pool index
+    "pool_index_order": ("((block * a->num_kv_heads + h) * a->block_size + off)",
+                         "((block * a->block_size + off) * a->num_kv_heads + h)"),
+    "scale_dropped": ("s[t - t0] = a->scale * dot;", "s[t - t0] = dot;"),
+    "max_sign": ("s[i] = exp(s[i] - m);", "s[i] = exp(m - s[i]);"),
+    "values_from_k": ("acc += s[i] * load_elem(a->v_cache", "acc += s[i] * load_elem(a->k_cache"),
+    "no_normalisation": ("o[d] = acc / l;", "o[d] = acc;"),
+    "last_dim_dropped": ("for (int d = 0; d < a->head_dim; ++d)\n            dot +=",
+                         "for (int d = 0; d < a->head_dim - 1; ++d)\n            dot +="),
+    "one_token_short": ("logits(a, b, hq, h, 0, L, s);\n        softmax_v(a, b, h, 0, L,",
+                        "logits(a, b, hq, h, 0, L - 1, s);\n        softmax_v(a, b, h, 0, L - 1,"),
+    "f16_bias": ("expo - 25", "expo - 24"),
+    "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "bf16_bias": ("expo - 134", "expo - 133"),
+    "split_weight": ("acc += pl[j] * exp(pm[j] - M) * po", "acc += pl[j] * po"),
+    "write_offset": ("int64_t blk = s / block_size, off = s % block_size;",
+                     "int64_t blk = s / block_size, off = (s + 1) % block_size;"),
+    "write_v_from_k": ("(const char *)v + ((int64_t)i * v_token_stride",
+                       "(const char *)k + ((int64_t)i * k_token_stride"),
+    "write_token_stride": ("(const char *)k + ((int64_t)i * k_token_stride + (int64_t)h * head_dim)",
+                           "(const char *)k + ((int64_t)i * num_kv_heads * head_dim + (int64_t)h * head_dim)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(path), "-lm"], check=True)
+    h = oracle.lib(str(so))
+    failed = []
+    for pin_name, pin in oracle_pins.PINS.items():
+        try:
+            pin(h)
+        except (AssertionError, oracle.OracleError, ValueError, FloatingPointError):
+            failed.append(pin_name)
+    assert failed, f"no pin caught mutant {name}"
