@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark: batched paged decode attention + KV-cache write on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step is one pass of the whole hot path over one batch: the batched
+KV-cache write of one new token per sequence, then the paged decode.  The
+default workload is the Llama-3.2-1B decode step at batch 16 (32 query / 8
+kv heads, head_dim 64, block_size 16, fp16 KV, context lengths U[100, 1024]),
+run over 16 layer pools back to back, so one step is one decode step of the
+16-layer model's attention; the 16 pools (~370 MB) exceed the 256 MB
+Infinity Cache.  Inputs are resident in HBM before the timed region; the
+timed region replays a HIP graph of the step (launch overhead of Python and
+the runtime excluded, kernel-to-kernel gaps included).
+
+Prints ONE JSON line: effective KV GB/s (sum_b L_b * 2 * Hkv * D * elt per
+second), microseconds per layer, the roofline of the decode call, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor specification
+METRIC = "paged decode attention effective KV GB/s + % HBM peak; µs/layer at batch 16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="workload (2 = Llama-3.2-1B batch 16, the headline)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="pools per step (default: 16 for workload 2, else enough to exceed 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not a HIP graph")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fill_pool(shape, dtype, seed, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
+                                   "(multi-GPU sharding is described, not built)"}))
+        return 2
+
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+    from paged_kv_attention_24_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pka.load_library()
+
+    cfg = args.config
+    host_pools = cfg in (2, 3)
+    wl = W.make_config(cfg, pools=host_pools, poison=False)
+    tdt = W.torch_dtype(wl.dtype)
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    pool_bytes = 2 * wl.num_blocks * Hkv * bs * D * wl.elt_bytes
+    if args.layers > 0:
+        R = args.layers
+    elif cfg == 2:
+        R = 16
+    else:
+        R = max(1, int(np.ceil(1.0e9 / pool_bytes)))
+    log(f"workload {cfg}: {wl.meta['description']}; pools per step {R} "
+        f"({R * pool_bytes / 1e6:.0f} MB)")
+
+    d0 = W.device_inputs(wl, dev) if host_pools else None
+    q = W.as_torch(wl.q, wl.dtype, dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    new_k = W.as_torch(wl.new_k, wl.dtype, dev)
+    new_v = W.as_torch(wl.new_v, wl.dtype, dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    shape = (wl.num_blocks, Hkv, bs, D)
+    kcs, vcs = [], []
+    for r in range(R):
+        if r == 0 and host_pools:
+            kcs.append(d0["k_cache"])
+            vcs.append(d0["v_cache"])
+        else:
+            kcs.append(fill_pool(shape, tdt, 1000 + 2 * r, dev))
+            vcs.append(fill_pool(shape, tdt, 1001 + 2 * r, dev))
+    P = wl.partition_size or pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
+    ws_bytes = pka.decode_workspace_bytes(B, Hq, D, wl.max_context_len, P)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
+    torch.cuda.synchronize()
+
+    def decode(r):
+        pka.paged_attention_decode(q, kcs[r], vcs[r], bt, cl, float(wl.scale), Hkv, bs,
+                                   out=outs[r], partition_size=P,
+                                   max_context_len=wl.max_context_len, workspace=ws)
+
+    def step():
+        for r in range(R):
+            pka.kv_cache_write(new_k, new_v, slots, kcs[r], vcs[r])
+            decode(r)
+
+    def decode_only():
+        for r in range(R):
+            decode(r)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(fn, n, use_graph):
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                fn()  # warm the capture stream
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                fn()
+            run = g.replay
+        else:
+            run = fn
+        for _ in range(max(1, args.warmup)):
+            run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms per call of fn
+
+    use_graph = not args.eager
+    t_wall0 = time.perf_counter()
+    ms_step = timed(step, args.steps, use_graph)
+    t_wall = time.perf_counter() - t_wall0
+    ms_decodes = timed(decode_only, args.steps, use_graph)
+    log(f"step {ms_step * 1e3:.1f} us ({R} pools), decode-only {ms_decodes * 1e3:.1f} us; "
+        f"timed wall {t_wall:.2f} s")
+
+    kv_bytes = wl.kv_bytes()
+    us_per_layer = ms_step * 1e3 / R
+    value = kv_bytes * R / (ms_step * 1e-3) / 1e9  # GB/s over the whole step
+    # decode call: algorithmic bytes = KV + q + out + block ids + lengths
+    nblk = int(np.sum((wl.context_lens.astype(np.int64) + bs - 1) // bs))
+    alg_bytes = kv_bytes + B * Hq * D * (wl.elt_bytes + 4) + nblk * 4 + B * 4
+    us_decode = ms_decodes * 1e3 / R
+    achieved = alg_bytes / (us_decode * 1e-6) / 1e9
+
+    # parity spot check of this exact launch configuration (first pool)
+    parity = None
+    if host_pools:
+        import oracle
+
+        torch.cuda.synchronize()
+        decode(0)
+        torch.cuda.synchronize()
+        kc_h = W.to_numpy_bits(kcs[0], wl.dtype)
+        vc_h = W.to_numpy_bits(vcs[0], wl.dtype)
+        rows = np.array([[b, h] for b in range(0, B, max(1, B // 8)) for h in (0, Hq - 1)],
+                        dtype=np.int32)
+        ref = oracle.paged_attention_decode(wl.q, kc_h, vc_h, wl.block_tables, wl.context_lens,
+                                            wl.scale, Hkv, bs, wl.dtype, rows=rows)
+        got = outs[0].double().cpu().numpy()[rows[:, 0], rows[:, 1]]
+        parity = float(np.max(np.abs(got - ref)))
+        log(f"parity (sampled rows vs fp64 oracle): max-abs {parity:.3g}")
+
+    cpu = None
+    if not args.no_cpu_baseline and host_pools:
+        import oracle
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+        kc_h = W.to_numpy_bits(kcs[0], wl.dtype)
+        vc_h = W.to_numpy_bits(vcs[0], wl.dtype)
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention_decode(wl.q, kc_h, vc_h, wl.block_tables, wl.context_lens,
+                                          wl.scale, Hkv, bs, wl.dtype, threads=threads)
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n_done >= 64:
+                break
+        cpu = {
+            "value": round(kv_bytes * n_done / el / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"full decode of one layer pool ({B} seqs x {Hq} q-heads, "
+                      f"{int(wl.context_lens.sum())} tokens) repeated {n_done}x in {el:.1f} s; "
+                      f"fp64 C oracle, OpenMP; host {platform.processor() or platform.machine()}",
+            "us_per_layer": round(el / n_done * 1e6, 1),
+        }
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) KV/q, shuffled block pool)",
+        "config": {
+            "workload": wl.meta["description"],
+            "global_batch": B,
+            "layers_per_step": R,
+            "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+            "kv_dtype": wl.dtype, "accumulate": "f32", "out_dtype": "f32",
+            "sum_context_tokens": int(wl.context_lens.sum()),
+            "partition_size": int(P),
+            "timing": "hip-graph replay" if use_graph else "eager",
+            "parallelism": "single GPU",
+        },
+        "us_per_layer": round(us_per_layer, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "parity_max_abs_sampled": parity,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (partition + merge kernels)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "us_per_launch": round(us_decode, 3),
+            "algorithmic_bytes_per_launch": int(alg_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+/*
+ * pka.h -- C ABI of the paged KV attention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Two operations, both described in the PhotonInfer README (Korean
+ * translation):
+ *   - "Technical details > Paged attention": the KV cache is managed in
+ *     fixed-size blocks without fragmentation, each sequence keeps its own
+ *     cache offsets, and one kernel performs the K/V writes of many
+ *     sequences at once  ->  pka_kv_cache_write.
+ *   - "Key features > GPU-optimised kernels": batched paged attention over
+ *     that block-wise cache, with a numerically stable softmax
+ *     ->  pka_paged_attention_decode.
+ *
+ * Conventions (same README, "Modern C++20 architecture": explicit error
+ * results instead of exceptions, zero-copy borrowed buffers):
+ *   - Every pointer named "device" is a device (HBM) pointer owned by the
+ *     caller; the library never frees or retains it.  The library allocates
+ *     no device memory: the decode's scratch workspace is passed in.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *     default stream) and returns without synchronising.
+ *   - Every call returns a pka_status.  Argument problems that the host can
+ *     see are reported before anything is launched; a failed launch returns
+ *     PKA_ERR_HIP.  pka_last_error() then gives a thread-local message.
+ *   - The contents of device buffers (block ids, lengths, slots) are the
+ *     caller's contract and are not validated on the hot path; the kernels
+ *     clamp them so that no access ever leaves the buffers described by the
+ *     arguments (see each call).
+ *
+ * KV pool layout (both pools, one layout):
+ *   k_cache, v_cache: [num_blocks][num_kv_heads][block_size][head_dim],
+ *   row-major, contiguous, 16-byte aligned.  Token t of a sequence whose
+ *   block table row is bt[] lives in physical block bt[t / block_size], at
+ *   offset t % block_size.  A slot number names one token position of the
+ *   pool: slot = block * block_size + offset.
+ *
+ * Query heads are grouped contiguously onto kv heads: query head hq reads
+ * kv head hq / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKA_H
+#define PKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKA_ABI_VERSION 1
+
+typedef enum pka_status {
+    PKA_OK = 0,
+    PKA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, shape or alignment */
+    PKA_ERR_UNSUPPORTED = 2,        /* valid but outside the compiled set */
+    PKA_ERR_WORKSPACE_TOO_SMALL = 3,
+    PKA_ERR_HIP = 4                 /* the HIP runtime reported an error */
+} pka_status;
+
+typedef enum pka_dtype {
+    PKA_F32 = 0,
+    PKA_F16 = 1,   /* IEEE binary16 */
+    PKA_BF16 = 2   /* bfloat16 */
+} pka_dtype;
+
+/*
+ * pka_kv_cache_write -- store the K and V rows of num_tokens new tokens,
+ * belonging to any number of sequences, into the block pools in one launch.
+ *
+ * For each token i with s = slot_mapping[i] and 0 <= s < num_blocks *
+ * block_size: for every kv head h, the head_dim elements
+ * k[i * k_token_stride + h * head_dim + d] (d < head_dim) are copied bit for
+ * bit to k_cache[s / block_size][h][s % block_size][d]; likewise v into
+ * v_cache.  No dtype conversion happens.  A negative slot marks padding and
+ * is skipped; a slot at or beyond num_blocks * block_size is skipped as well
+ * (nothing outside the pools is ever written).  Two tokens with the same
+ * slot race: which one lands is unspecified.  Every other byte of both pools
+ * is left untouched.
+ *
+ *   k, v            device, [num_tokens][num_kv_heads][head_dim] with token
+ *                   strides k_token_stride / v_token_stride (in elements,
+ *                   >= num_kv_heads * head_dim); heads are head_dim apart.
+ *                   Base pointers 16-byte aligned; token strides times the
+ *                   element size multiples of 16 bytes.
+ *   slot_mapping    device, int64 [num_tokens].
+ *   k_cache,v_cache device, written in place (layout above).
+ *   dtype           element type of k, v and both pools.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32}; any num_kv_heads
+ * >= 1; num_tokens >= 0 (0 launches nothing).
+ */
+pka_status pka_kv_cache_write(const void *k, const void *v, int64_t k_token_stride,
+                              int64_t v_token_stride, const int64_t *slot_mapping,
+                              int32_t num_tokens, void *k_cache, void *v_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_dim, pka_dtype dtype, void *stream);
+
+/*
+ * pka_decode_partition_size -- the partition length (tokens, a multiple of
+ * block_size) pka_paged_attention_decode uses when its partition_size
+ * argument is 0.  Pure host function of the shapes.
+ */
+int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t max_context_len);
+
+/*
+ * pka_decode_workspace_bytes -- bytes of device scratch the decode needs for
+ * these shapes and this partition length (already resolved, > 0).  0 when
+ * every sequence fits one partition (max_context_len <= partition_size);
+ * then the workspace pointer may be NULL.
+ */
+size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pka_paged_attention_decode -- one query token per sequence attends over
+ * that sequence's cached tokens, for the whole batch:
+ *
+ *   out[b][hq][:] = sum_{t < L_b} softmax_t(scale * q[b][hq][:] . K_t) V_t
+ *
+ * with L_b = context_lens[b], K_t/V_t the rows of token t of sequence b in
+ * kv head hq / (num_q_heads / num_kv_heads), found through block_tables[b].
+ * Softmax is computed stably (running max subtracted, fp32 throughout);
+ * products and sums accumulate in fp32.  L_b <= 0 yields a zero row.
+ *
+ * Long sequences are split into partitions of partition_size tokens that
+ * are processed independently; each writes its running max, sum and
+ * normalised partial output to the workspace, and a second kernel merges
+ * them exactly (log-sum-exp).  The result does not depend on the partition
+ * length beyond fp32 rounding.
+ *
+ *   out             device, [num_seqs][num_q_heads][head_dim], contiguous,
+ *                   of out_dtype (PKA_F32, or the KV dtype: rounded to
+ *                   nearest even).
+ *   q               device, [num_seqs][num_q_heads][head_dim], contiguous,
+ *                   of the KV dtype.
+ *   k_cache,v_cache device pools (layout above), of kv_dtype.
+ *   block_tables    device, int32 [num_seqs][max_blocks_per_seq].  Entries
+ *                   at index >= ceil(L_b / block_size) are never read.  An
+ *                   entry outside [0, num_blocks) is clamped into range (the
+ *                   row's result is then meaningless, but no access leaves
+ *                   the pools).
+ *   context_lens    device, int32 [num_seqs].  Lengths are clamped to
+ *                   [0, min(max_blocks_per_seq * block_size,
+ *                   max_context_len)] on the device.
+ *   scale           multiplier of the dot products (typically 1/sqrt(D)).
+ *   max_context_len host hint: no sequence is longer.  <= 0 means
+ *                   max_blocks_per_seq * block_size.  It sizes the launch
+ *                   without a device-to-host copy.
+ *   partition_size  0: pka_decode_partition_size(); else a positive
+ *                   multiple of block_size.
+ *   workspace       device scratch of workspace_bytes >=
+ *                   pka_decode_workspace_bytes(...), 256-byte aligned; may
+ *                   be NULL when that size is 0.  Its contents are
+ *                   overwritten; calls that share one workspace on
+ *                   different streams race.
+ * Supported: kv_dtype in {F32, F16, BF16}; head_dim in {64, 128};
+ * block_size in {16, 32}; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void *q,
+                                      const void *k_cache, const void *v_cache,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t num_blocks, int32_t block_size, float scale,
+                                      pka_dtype kv_dtype, int32_t max_context_len,
+                                      int32_t partition_size, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* Static English name of a status code. */
+const char *pka_status_string(pka_status status);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * ("" if none).  Valid until the next call on the same thread. */
+const char *pka_last_error(void);
+
+/* PKA_ABI_VERSION of the loaded library. */
+int32_t pka_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKA_H */

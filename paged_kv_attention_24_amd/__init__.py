@@ -1,0 +1,250 @@
+"""Paged KV attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/pka.h`` (``libpka.so``,
+built in this directory).  PyTorch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU or PyTorch fallback: if the library is missing, or a tensor
+is not on a GPU, the calls raise.
+
+Operations (PhotonInfer README, Korean translation, "Technical details >
+Paged attention" and "Key features > GPU-optimised kernels"):
+
+  kv_cache_write(k, v, slot_mapping, k_cache, v_cache)
+      one launch stores the new K/V rows of many sequences into the pools.
+  paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens,
+                         scale, num_kv_heads, block_size)
+      batched one-token attention over the block-wise cache.
+
+Pools are [num_blocks, num_kv_heads, block_size, head_dim].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "PkaError", "kv_cache_write", "paged_attention_decode", "decode_partition_size",
+    "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpka.so")
+
+PKA_OK = 0
+_DTYPE_CODES = None  # filled lazily (needs torch)
+
+
+class PkaError(RuntimeError):
+    """A non-OK pka_status; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpka.so (built by ``paged_kv_attention_24_amd._build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m paged_kv_attention_24_amd._build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pka_kv_cache_write.argtypes = [P, P, i64, i64, P, i32, P, P, i32, i32, i32, i32,
+                                       ctypes.c_int, P]
+    lib.pka_kv_cache_write.restype = ctypes.c_int
+    lib.pka_decode_partition_size.argtypes = [i32, i32, i32, i32]
+    lib.pka_decode_partition_size.restype = i32
+    lib.pka_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pka_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pka_paged_attention_decode.argtypes = [
+        P, ctypes.c_int, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+        ctypes.c_int, i32, i32, P, ctypes.c_size_t, P]
+    lib.pka_paged_attention_decode.restype = ctypes.c_int
+    lib.pka_status_string.argtypes = [ctypes.c_int]
+    lib.pka_status_string.restype = ctypes.c_char_p
+    lib.pka_last_error.argtypes = []
+    lib.pka_last_error.restype = ctypes.c_char_p
+    lib.pka_abi_version.argtypes = []
+    lib.pka_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != PKA_OK:
+        lib = load_library()
+        name = lib.pka_status_string(status).decode()
+        detail = lib.pka_last_error().decode()
+        raise PkaError(status, f"pka: {name}: {detail}")
+
+
+def _dtype_code(dt) -> int:
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if dt not in codes:
+        raise TypeError(f"unsupported dtype {dt}; expected float32, float16 or bfloat16")
+    return codes[dt]
+
+
+def _stream_ptr(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_gpu(*tensors):
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on a GPU; the library has no CPU path")
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
+    """Store k, v [T, Hkv, D] into the pools at slot_mapping (int64 [T]).
+
+    Slot s addresses block s // block_size, offset s % block_size; negative
+    slots are skipped.  Bit-exact copy; mutates k_cache and v_cache.
+    """
+    import torch
+
+    _require_gpu(k, v, slot_mapping, k_cache, v_cache)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    NB, Hkv, bs, D = k_cache.shape
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, D):
+            raise ValueError(f"{name} must be [T, {Hkv}, {D}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} must have contiguous heads (strides [*, {D}, 1])")
+        if t.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+            raise TypeError("k, v and the caches must share one dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k.shape[0],) or \
+            v.shape[0] != k.shape[0]:
+        raise ValueError("slot_mapping must be int64 [T] with T = k.shape[0] = v.shape[0]")
+    slot_mapping = slot_mapping.contiguous()
+    T = k.shape[0]
+    lib = load_library()
+    _check(lib.pka_kv_cache_write(
+        k.data_ptr(), v.data_ptr(), k.stride(0) if T else Hkv * D, v.stride(0) if T else Hkv * D,
+        slot_mapping.data_ptr(), T, k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
+        _dtype_code(k_cache.dtype), _stream_ptr(k_cache.device)))
+
+
+def decode_partition_size(num_seqs: int, num_kv_heads: int, block_size: int,
+                          max_context_len: int) -> int:
+    return int(load_library().pka_decode_partition_size(num_seqs, num_kv_heads, block_size,
+                                                        max_context_len))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                           max_context_len: int, partition_size: int) -> int:
+    return int(load_library().pka_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                         max_context_len, partition_size))
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           num_kv_heads: int, block_size: int, *, out=None, out_dtype=None,
+                           partition_size: int = 0, max_context_len: int = 0,
+                           workspace=None):
+    """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache.
+
+    q [B, Hq, D] (the KV dtype); pools [NB, Hkv, bs, D]; block_tables int32
+    [B, MB]; context_lens int32 [B] (device).  Returns out [B, Hq, D], fp32
+    unless ``out_dtype`` (or ``out``) says the KV dtype.  ``max_context_len``
+    is an optional host hint (no device sync); ``partition_size`` 0 lets the
+    library choose.  ``workspace`` (uint8 device tensor) is allocated when not
+    given.
+    """
+    import torch
+
+    _require_gpu(q, k_cache, v_cache, block_tables, context_lens)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    NB, Hkv, bs, D = k_cache.shape
+    if Hkv != num_kv_heads or bs != block_size:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match num_kv_heads="
+                         f"{num_kv_heads}, block_size={block_size}")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError(f"q must be [B, Hq, {D}]")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    q = q.contiguous()
+    B, Hq, _ = q.shape
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    block_tables = block_tables.contiguous()
+    context_lens = context_lens.contiguous()
+    MB = block_tables.shape[1]
+    if out is None:
+        odt = torch.float32 if out_dtype is None else out_dtype
+        out = torch.empty((B, Hq, D), dtype=odt, device=q.device)
+    else:
+        if tuple(out.shape) != (B, Hq, D) or not out.is_contiguous() or out.device != q.device:
+            raise ValueError("out must be a contiguous [B, Hq, D] tensor on q's device")
+    if B == 0:
+        return out
+    lib = load_library()
+    hint = max_context_len if max_context_len > 0 else MB * bs
+    hint = min(hint, MB * bs)
+    P = partition_size if partition_size > 0 else decode_partition_size(B, Hkv, bs, hint)
+    need = decode_workspace_bytes(B, Hq, D, hint, P)
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    _check(lib.pka_paged_attention_decode(
+        out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), MB, context_lens.data_ptr(), B, Hq, Hkv, D,
+        NB, bs, float(scale), _dtype_code(k_cache.dtype), hint, P, ws_ptr, ws_bytes,
+        _stream_ptr(q.device)))
+    return out
+
+
+class PagedKVCache:
+    """A pair of K/V block pools on one device.
+
+    ``write(k, v, slot_mapping)`` is the three-argument cache write;
+    ``decode(q, block_tables, context_lens, scale)`` attends over it.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 dtype=None, device="cuda"):
+        import torch
+
+        dtype = dtype or torch.float16
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.k_cache = torch.empty(shape, dtype=dtype, device=device)
+        self.v_cache = torch.empty(shape, dtype=dtype, device=device)
+        self.block_size = block_size
+        self.num_kv_heads = num_kv_heads
+
+    def write(self, k, v, slot_mapping) -> None:
+        kv_cache_write(k, v, slot_mapping, self.k_cache, self.v_cache)
+
+    def decode(self, q, block_tables, context_lens, scale: float, **kw):
+        return paged_attention_decode(q, self.k_cache, self.v_cache, block_tables, context_lens,
+                                      scale, self.num_kv_heads, self.block_size, **kw)

@@ -1,0 +1,74 @@
+"""Build libpka.so (HIP kernels for gfx950 + the C ABI) in the package dir.
+
+    python -m paged_kv_attention_24_amd._build
+
+Every HIP translation unit is compiled with packed FP32 instructions
+disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host
+pass prints a harmless warning about that feature.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG, "libpka.so")
+
+ARCH = "gfx950"
+SOURCES = ["paged_decode.hip", "kv_cache_write.hip", "abi.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", INCLUDE, "-I", CSRC, "-Wall"]
+
+
+def _compile_cmd(src: str, obj: str, extra=()):
+    lang = ["-x", "hip"]  # the ABI file includes the HIP runtime headers too
+    return [HIPCC, *lang, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = _compile_cmd(src, obj, extra_flags)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = "\n".join(l for l in out.splitlines()
+                         if "packed-fp32-ops' is not a recognized feature" not in l)
+        if text.strip() and (verbose or p.returncode):
+            print(text, file=sys.stderr)
+        if p.returncode:
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    tmp = LIB_PATH + ".tmp"
+    link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def clean():
+    shutil.rmtree(BUILD_DIR, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,234 @@
+// C ABI of the library (declared in include/pka.h): argument validation,
+// the partition-length heuristic, workspace sizing and dispatch to the
+// kernel launchers.  Everything the host can check is checked here, before
+// any HIP call, and reported as a pka_status with a thread-local message.
+
+#include "pka.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pka_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pka_status fail(pka_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pka_status ok()
+{
+    g_last_error[0] = '\0';
+    return PKA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(pka_dtype d) { return d == PKA_F32 || d == PKA_F16 || d == PKA_BF16; }
+
+pka::DType to_internal(pka_dtype d) { return static_cast<pka::DType>(static_cast<int>(d)); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Fewest workgroups the decode should offer the 256 compute units.
+constexpr int64_t kTargetWorkgroups = 2048;
+
+}  // namespace
+
+extern "C" {
+
+const char *pka_status_string(pka_status s)
+{
+    switch (s) {
+    case PKA_OK: return "ok";
+    case PKA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case PKA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *pka_last_error(void) { return g_last_error; }
+
+int32_t pka_abi_version(void) { return PKA_ABI_VERSION; }
+
+pka_status pka_kv_cache_write(const void *k, const void *v, int64_t k_token_stride,
+                              int64_t v_token_stride, const int64_t *slot_mapping,
+                              int32_t num_tokens, void *k_cache, void *v_cache,
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_dim, pka_dtype dtype, void *stream)
+{
+    if (num_tokens < 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (!valid_dtype(dtype))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (num_blocks <= 0 || num_kv_heads <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_blocks and num_kv_heads must be positive");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+    if (block_size != 16 && block_size != 32)
+        return fail(PKA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+    if (!k_cache || !v_cache)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null cache pointer");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "caches must be 16-byte aligned");
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !slot_mapping)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null k, v or slot_mapping");
+    const int elt = pka::dtype_bytes(to_internal(dtype));
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (k_token_stride < row || v_token_stride < row)
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "token strides (%lld, %lld) must be >= num_kv_heads * head_dim = %lld",
+                    (long long)k_token_stride, (long long)v_token_stride, (long long)row);
+    if (!aligned16(k) || !aligned16(v) || (k_token_stride * elt) % 16 || (v_token_stride * elt) % 16)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "k/v rows must be 16-byte aligned");
+    pka::WriteArgs a{k, v, k_token_stride, v_token_stride, slot_mapping, num_tokens,
+                     k_cache, v_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                     to_internal(dtype)};
+    hipError_t e = pka::launch_kv_cache_write(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t max_context_len)
+{
+    // Largest power-of-two partition (<= the kernels' maximum, >= 64 tokens
+    // and >= one block) that still offers enough workgroups when the
+    // sequences average half the longest one.
+    if (block_size <= 0)
+        return 0;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+    const int64_t lmax = max_context_len > 0 ? max_context_len : 1;
+    int64_t P = pka::kMaxPartition;
+    const int64_t floor_p = block_size > 64 ? block_size : 64;
+    while (P > floor_p && pairs * ceil_div(lmax, P) < 2 * kTargetWorkgroups)
+        P /= 2;
+    if (P < block_size)
+        P = block_size;
+    return (int32_t)(ceil_div(P, block_size) * block_size);
+}
+
+size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size)
+{
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size <= 0 ||
+        max_context_len <= partition_size)
+        return 0;
+    const int64_t parts = ceil_div(max_context_len, partition_size);
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+    const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+    return (size_t)(o_bytes + rows * 2 * 4);
+}
+
+pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void *q,
+                                      const void *k_cache, const void *v_cache,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t num_blocks, int32_t block_size, float scale,
+                                      pka_dtype kv_dtype, int32_t max_context_len,
+                                      int32_t partition_size, void *workspace,
+                                      size_t workspace_bytes, void *stream)
+{
+    if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (out_dtype != PKA_F32 && out_dtype != kv_dtype)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "out dtype must be F32 or the KV dtype");
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "num_seqs >= 0 and positive num_q_heads, num_kv_heads, num_blocks, "
+                    "max_blocks_per_seq required");
+    if (num_q_heads % num_kv_heads)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_q_heads %d not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    const int group = num_q_heads / num_kv_heads;
+    if (!pka::decode_supported(to_internal(kv_dtype), head_dim, block_size, group))
+        return fail(PKA_ERR_UNSUPPORTED,
+                    "head_dim %d / block_size %d / group %d outside {64,128} x {16,32} x {1,2,4,8}",
+                    head_dim, block_size, group);
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return fail(PKA_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535");
+    if (!(scale == scale))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "partition_size %d must be 0 or a positive multiple of block_size %d",
+                    partition_size, block_size);
+    if (partition_size > pka::kMaxPartition)
+        return fail(PKA_ERR_UNSUPPORTED, "partition_size %d exceeds %d", partition_size,
+                    pka::kMaxPartition);
+    if (num_seqs == 0)
+        return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "out, q and the caches must be 16-byte aligned");
+    const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+    int64_t lmax = max_context_len > 0 ? max_context_len : table_cap;
+    if (lmax > table_cap)
+        lmax = table_cap;
+    if (lmax > INT32_MAX)
+        return fail(PKA_ERR_UNSUPPORTED, "context length beyond int32");
+    if (partition_size == 0)
+        partition_size = pka_decode_partition_size(num_seqs, num_kv_heads, block_size, (int32_t)lmax);
+    const int64_t parts = lmax > 0 ? ceil_div(lmax, partition_size) : 1;
+    if (parts > 0x7fffffff)
+        return fail(PKA_ERR_UNSUPPORTED, "too many partitions");
+    const size_t need = pka_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                   (int32_t)lmax, partition_size);
+    if (need > 0) {
+        if (!workspace)
+            return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);
+        if (workspace_bytes < need)
+            return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got %zu",
+                        need, workspace_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(PKA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    }
+    pka::DecodeArgs a{};
+    a.out = out;
+    a.out_dtype = to_internal(out_dtype);
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.scale = scale;
+    a.kv_dtype = to_internal(kv_dtype);
+    a.max_context_len = (int32_t)lmax;
+    a.partition_size = partition_size;
+    a.num_partitions = (int32_t)parts;
+    if (need > 0) {
+        const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+        const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+        a.ws_o = static_cast<float *>(workspace);
+        a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    }
+    hipError_t e = pka::launch_paged_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "paged_attention_decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

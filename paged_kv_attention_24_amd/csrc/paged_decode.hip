@@ -1,0 +1,562 @@
+// Batched paged-attention decode for gfx950 (CDNA4).
+//
+// What is computed (PhotonInfer README, Korean translation, "Key features >
+// GPU-optimised kernels" and "Technical details > Paged attention"): for
+// every sequence b and query head hq, one query row attends over the
+// sequence's L_b cached tokens, found block by block through its block
+// table, with a numerically stable softmax:
+//     out[b,hq,:] = sum_t softmax_t(scale * q[b,hq,:] . K_t) V_t.
+//
+// Design (CDNA4-first; the README's float4 loads and CUB block reductions
+// are prior art for another GPU, not the blueprint):
+//
+//  * Work item = (partition j, kv head h, sequence b): the tokens
+//    [j*P, min((j+1)*P, L_b)) of one kv head.  All G = Hq/Hkv query heads of
+//    the group are served by the same K/V reads, so every KV byte is read
+//    from HBM exactly once.
+//  * One workgroup of NW wave64s per work item.  The partition is cut into
+//    chunks of CT tokens (4 coalesced 1 KiB loads per chunk per tensor);
+//    chunks are dealt round-robin to the waves.
+//  * Lane layout of a load: a (block, kv head) tile is a contiguous
+//    [block_size][head_dim] run, so one wave load of 64 lanes x 16 bytes
+//    covers TPL = 64 / LPR whole token rows, LPR = head_dim*elt/16 lanes per
+//    row.  Lane l holds 16 bytes (VEC elements) of token l / LPR.
+//  * Pass 1 streams K: partial dot products with v_dot2_f32_{f16,bf16} (or
+//    fp32 FMA), a DPP butterfly over the LPR lanes of a row, the scale and
+//    log2(e) folded in; logits go to LDS, a running max stays in registers.
+//  * Pass 2 streams V: p = exp2(s - m_wave) and o += p * V with
+//    v_fma_mix-style mixed-precision FMAs into fp32 accumulators.  Because
+//    each wave knows its maximum before pass 2, nothing is ever rescaled in
+//    the loop.
+//  * Merge: per-lane partial sums (token groups x waves) are combined in LDS
+//    with each wave's maximum (log-sum-exp), once per work item.
+//  * Partitions: with more than one partition per sequence each work item
+//    writes (max, sum, normalised row) to the workspace and a small second
+//    kernel merges them; otherwise the first kernel writes the output.
+//  * Every K/V load is issued one chunk ahead of its use (register double
+//    buffering), so each wave keeps up to 8 KiB in flight.
+//  * Tokens >= L (the tail of the last block) are excluded by selects, never
+//    by multiplying with 0, so stale or NaN slot contents cannot leak.
+
+#include <hip/hip_runtime.h>
+
+#include "pka_internal.h"
+
+namespace pka {
+namespace {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kLoadsPerChunk = 4;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+struct TF32 {
+    static constexpr int kBytes = 4;
+};
+struct TF16 {
+    static constexpr int kBytes = 2;
+};
+struct TBF16 {
+    static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// acc + (16 bytes of q) . (16 bytes of k), fp32 accumulation.
+__device__ __forceinline__ float dot16(TF32, const uint4 &q, const uint4 &k, float acc)
+{
+    acc = fmaf(as_f(q.x), as_f(k.x), acc);
+    acc = fmaf(as_f(q.y), as_f(k.y), acc);
+    acc = fmaf(as_f(q.z), as_f(k.z), acc);
+    acc = fmaf(as_f(q.w), as_f(k.w), acc);
+    return acc;
+}
+__device__ __forceinline__ float dot16(TF16, const uint4 &q, const uint4 &k, float acc)
+{
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.x), __builtin_bit_cast(half2_t, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.y), __builtin_bit_cast(half2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.z), __builtin_bit_cast(half2_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.w), __builtin_bit_cast(half2_t, k.w), acc, false);
+    return acc;
+}
+__device__ __forceinline__ float dot16(TBF16, const uint4 &q, const uint4 &k, float acc)
+{
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.x), __builtin_bit_cast(bf162_t, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.y), __builtin_bit_cast(bf162_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.z), __builtin_bit_cast(bf162_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.w), __builtin_bit_cast(bf162_t, k.w), acc, false);
+    return acc;
+}
+
+// o[0..VEC) += p * (16 bytes of v), fp32 accumulation.
+__device__ __forceinline__ void axpy16(TF32, float p, const uint4 &v, float *o)
+{
+    o[0] = fmaf(p, as_f(v.x), o[0]);
+    o[1] = fmaf(p, as_f(v.y), o[1]);
+    o[2] = fmaf(p, as_f(v.z), o[2]);
+    o[3] = fmaf(p, as_f(v.w), o[3]);
+}
+__device__ __forceinline__ void axpy_h2(float p, uint32_t w, float *o)
+{
+    half2_t h = __builtin_bit_cast(half2_t, w);
+    o[0] = fmaf(p, (float)h.x, o[0]);
+    o[1] = fmaf(p, (float)h.y, o[1]);
+}
+__device__ __forceinline__ void axpy16(TF16, float p, const uint4 &v, float *o)
+{
+    axpy_h2(p, v.x, o + 0);
+    axpy_h2(p, v.y, o + 2);
+    axpy_h2(p, v.z, o + 4);
+    axpy_h2(p, v.w, o + 6);
+}
+__device__ __forceinline__ void axpy_b2(float p, uint32_t w, float *o)
+{
+    o[0] = fmaf(p, as_f(w << 16), o[0]);
+    o[1] = fmaf(p, as_f(w & 0xffff0000u), o[1]);
+}
+__device__ __forceinline__ void axpy16(TBF16, float p, const uint4 &v, float *o)
+{
+    axpy_b2(p, v.x, o + 0);
+    axpy_b2(p, v.y, o + 2);
+    axpy_b2(p, v.z, o + 4);
+    axpy_b2(p, v.w, o + 6);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float swz_xor16(float x)
+{
+    // ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1..32); every lane of
+// the group receives the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
+{
+    if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror: other quad of 8
+    if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror: other half of 16
+    if constexpr (N >= 32) x += swz_xor16(x);  // other row of 32
+    return x;
+}
+
+// Max over the whole wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    x = fmaxf(x, swz_xor16(x));
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    return fmaxf(lo, hi);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void store_out(void *out, int64_t idx, float x, int out_kind)
+{
+    if (out_kind == 0)
+        static_cast<float *>(out)[idx] = x;
+    else if (out_kind == 1)
+        static_cast<_Float16 *>(out)[idx] = (_Float16)x;
+    else
+        static_cast<uint16_t *>(out)[idx] = f32_to_bf16_rne(x);
+}
+
+struct PartitionParams {
+    void *out;
+    int out_kind;  // 0 f32, 1 f16, 2 bf16
+    const char *q, *k_cache, *v_cache;
+    const int32_t *block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+    int32_t num_q_heads, num_kv_heads, num_blocks;
+    float scale_log2;  // scale * log2(e)
+    int32_t partition_size, num_partitions, len_cap;
+    float *ws_o, *ws_ml;
+};
+
+template <class T, int D, int BS, int G>
+struct Shape {
+    static constexpr int ELT = T::kBytes;
+    static constexpr int VEC = 16 / ELT;           // elements per lane load
+    static constexpr int LPR = D / VEC;            // lanes per token row
+    static constexpr int TPL = kWave / LPR;        // tokens per wave load
+    static constexpr int NL = kLoadsPerChunk;      // loads per chunk per tensor
+    static constexpr int CT = NL * TPL;            // tokens per chunk
+    static constexpr int TILE = BS * D * ELT;      // bytes of one (block, head) tile
+    static constexpr int NW = (G * D * TPL * 4 * 4 > 48 * 1024) ? 2 : 4;  // waves per workgroup
+    static_assert(LPR >= 1 && LPR <= 32 && TPL * LPR == kWave, "row must fit a wave");
+    static_assert(BS % TPL == 0, "a wave load must stay inside one block");
+};
+
+template <class T, int D, int BS, int G>
+__host__ __device__ constexpr int chunks_per_wave(int partition_size)
+{
+    using S = Shape<T, D, BS, G>;
+    const int chunks = (partition_size + S::CT - 1) / S::CT;
+    return (chunks + S::NW - 1) / S::NW;
+}
+
+template <class T, int D, int BS, int G>
+__host__ __device__ constexpr size_t lds_bytes(int partition_size)
+{
+    using S = Shape<T, D, BS, G>;
+    const size_t logits = (size_t)S::NW * chunks_per_wave<T, D, BS, G>(partition_size) * S::CT * G * 4;
+    const size_t merge = (size_t)S::NW * S::TPL * G * (D + 1) * 4 + (size_t)S::NW * G * 4;
+    return logits > merge ? logits : merge;
+}
+
+template <class T, int D, int BS, int G>
+__global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_kernel(PartitionParams p)
+{
+    using S = Shape<T, D, BS, G>;
+    constexpr int NW = S::NW, LPR = S::LPR, TPL = S::TPL, NL = S::NL, CT = S::CT, VEC = S::VEC;
+    extern __shared__ float smem[];
+
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int tg = lane / LPR, cl = lane % LPR;
+
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+    const int P = p.partition_size;
+    const int t_begin = j * P;
+    if (t_begin >= L && !(L == 0 && j == 0))
+        return;  // uniform over the workgroup
+    const int t_end = min(t_begin + P, L);
+    const int nchunks = (t_end - t_begin + CT - 1) / CT;
+    const int nk = nchunks > w ? (nchunks - w + NW - 1) / NW : 0;  // chunks of this wave
+
+    // query rows of the group: 16 bytes per lane per head
+    uint4 qr[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        qr[g] = *reinterpret_cast<const uint4 *>(
+            p.q + ((int64_t)(b * p.num_q_heads + h * G + g) * D + cl * VEC) * S::ELT);
+
+    const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+    const int64_t head_off = (int64_t)h * S::TILE;
+    const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
+    const int nb_max = p.num_blocks - 1;
+
+    // load the NL wave loads of chunk k of this wave from `pool` into r
+    auto load_chunk = [&](const char *pool, int k, uint4 *r) {
+        const int tc = t_begin + (w + k * NW) * CT;
+        const bool full = tc + CT <= t_end;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int t0 = tc + i * TPL;
+            if (full || t0 < t_end) {
+                int blk = bt[t0 / BS];
+                blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
+                const char *src = pool + blk * block_stride + head_off +
+                                  (int64_t)(t0 % BS) * (D * S::ELT) + lane * 16;
+                r[i] = *reinterpret_cast<const uint4 *>(src);
+            } else {
+                r[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- pass 1: logits -------------------------------------------------
+    float *lds_s = smem + (size_t)w * chunks_per_wave<T, D, BS, G>(P) * CT * G;
+    float mloc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        mloc[g] = -INFINITY;
+
+    auto logits_chunk = [&](int k, const uint4 *r) {
+        const int tc = t_begin + (w + k * NW) * CT;
+        const bool full = tc + CT <= t_end;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int tok = tc + i * TPL + tg;
+            float s[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                s[g] = group_sum<LPR>(dot16(T{}, qr[g], r[i], 0.0f)) * p.scale_log2;
+                if (!full)
+                    s[g] = tok < t_end ? s[g] : -INFINITY;
+                mloc[g] = fmaxf(mloc[g], s[g]);
+            }
+            if (cl == 0) {
+                float *dst = lds_s + (k * CT + i * TPL + tg) * G;
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    dst[g] = s[g];
+            }
+        }
+    };
+
+    {
+        uint4 ra[NL], rb[NL];
+        if (nk > 0)
+            load_chunk(p.k_cache, 0, ra);
+        for (int k = 0; k < nk; k += 2) {
+            if (k + 1 < nk)
+                load_chunk(p.k_cache, k + 1, rb);
+            logits_chunk(k, ra);
+            if (k + 1 >= nk)
+                break;
+            if (k + 2 < nk)
+                load_chunk(p.k_cache, k + 2, ra);
+            logits_chunk(k + 1, rb);
+        }
+    }
+
+    float mw[G], mref[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        mw[g] = wave_max(mloc[g]);
+        mref[g] = mw[g] == -INFINITY ? 0.0f : mw[g];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- pass 2: softmax weights and values -------------------------------
+    float o[G][VEC];
+    float lsum[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        lsum[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            o[g][e] = 0.0f;
+    }
+
+    auto values_chunk = [&](int k, uint4 *r) {
+        const int tc = t_begin + (w + k * NW) * CT;
+        const bool full = tc + CT <= t_end;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int tok = tc + i * TPL + tg;
+            if (!full && tok >= t_end)
+                r[i] = make_uint4(0, 0, 0, 0);  // select, so NaN bits never reach o
+            const float *src = lds_s + (k * CT + i * TPL + tg) * G;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float pw = __builtin_amdgcn_exp2f(src[g] - mref[g]);
+                lsum[g] += pw;
+                axpy16(T{}, pw, r[i], o[g]);
+            }
+        }
+    };
+
+    {
+        uint4 ra[NL], rb[NL];
+        if (nk > 0)
+            load_chunk(p.v_cache, 0, ra);
+        for (int k = 0; k < nk; k += 2) {
+            if (k + 1 < nk)
+                load_chunk(p.v_cache, k + 1, rb);
+            values_chunk(k, ra);
+            if (k + 1 >= nk)
+                break;
+            if (k + 2 < nk)
+                load_chunk(p.v_cache, k + 2, ra);
+            values_chunk(k + 1, rb);
+        }
+    }
+
+    // ---- merge token groups and waves (log-sum-exp with the wave maxima) --
+    __syncthreads();  // logits area is reused below
+    float *red = smem;                                  // [NW][TPL][G][D]
+    float *lred = red + (size_t)NW * TPL * G * D;       // [NW][TPL][G]
+    float *mred = lred + (size_t)NW * TPL * G;          // [NW][G]
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float *dst = red + ((size_t)(w * TPL + tg) * G + g) * D + cl * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            dst[e] = o[g][e];
+    }
+    if (cl == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            lred[(w * TPL + tg) * G + g] = lsum[g];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            mred[w * G + g] = mw[g];
+    }
+    __syncthreads();
+
+    const int nparts_b = L == 0 ? 1 : (L + P - 1) / P;
+    for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+        const int g = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww)
+            M = fmaxf(M, mred[ww * G + g]);
+        float acc = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mv = mred[ww * G + g];
+            const float sc = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+            float a = 0.0f, l = 0.0f;
+#pragma unroll
+            for (int t = 0; t < TPL; ++t) {
+                a += red[((size_t)(ww * TPL + t) * G + g) * D + d];
+                l += lred[(ww * TPL + t) * G + g];
+            }
+            acc = fmaf(a, sc, acc);
+            den = fmaf(l, sc, den);
+        }
+        const float res = den > 0.0f ? acc / den : 0.0f;
+        const int hq = h * G + g;
+        if (nparts_b == 1) {
+            store_out(p.out, ((int64_t)b * p.num_q_heads + hq) * D + d, res, p.out_kind);
+        } else {
+            const int64_t row = ((int64_t)b * p.num_q_heads + hq) * p.num_partitions + j;
+            p.ws_o[row * D + d] = res;
+            if (d == 0) {
+                p.ws_ml[row * 2 + 0] = M;
+                p.ws_ml[row * 2 + 1] = den;
+            }
+        }
+    }
+}
+
+// Merge the partitions of each (sequence, query head): with m_j in log2
+// units, w_j = l_j * 2^(m_j - max m), out = sum w_j o_j / sum w_j.
+template <int D>
+__global__ __launch_bounds__(D) void reduce_kernel(void *out, int out_kind, const float *ws_o,
+                                                   const float *ws_ml,
+                                                   const int32_t *context_lens,
+                                                   int32_t num_q_heads, int32_t partition_size,
+                                                   int32_t num_partitions, int32_t len_cap)
+{
+    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    int L = context_lens[b];
+    L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
+    const int n = (L + partition_size - 1) / partition_size;
+    if (n <= 1)
+        return;  // written by the partition kernel
+    const int64_t row0 = ((int64_t)b * num_q_heads + hq) * num_partitions;
+    float M = -INFINITY;
+    for (int jj = 0; jj < n; ++jj)
+        M = fmaxf(M, ws_ml[(row0 + jj) * 2]);
+    float acc = 0.0f, den = 0.0f;
+    for (int jj = 0; jj < n; ++jj) {
+        const float wgt = ws_ml[(row0 + jj) * 2 + 1] * __builtin_amdgcn_exp2f(ws_ml[(row0 + jj) * 2] - M);
+        den += wgt;
+        acc = fmaf(wgt, ws_o[(row0 + jj) * D + d], acc);
+    }
+    store_out(out, ((int64_t)b * num_q_heads + hq) * D + d, acc / den, out_kind);
+}
+
+template <class T, int D, int BS, int G>
+hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
+{
+    using S = Shape<T, D, BS, G>;
+    PartitionParams p;
+    p.out = a.out;
+    p.out_kind = (int)a.out_dtype;
+    p.q = static_cast<const char *>(a.q);
+    p.k_cache = static_cast<const char *>(a.k_cache);
+    p.v_cache = static_cast<const char *>(a.v_cache);
+    p.block_tables = a.block_tables;
+    p.max_blocks_per_seq = a.max_blocks_per_seq;
+    p.context_lens = a.context_lens;
+    p.num_q_heads = a.num_q_heads;
+    p.num_kv_heads = a.num_kv_heads;
+    p.num_blocks = a.num_blocks;
+    p.scale_log2 = a.scale * kLog2e;
+    p.partition_size = a.partition_size;
+    p.num_partitions = a.num_partitions;
+    const int64_t cap_table = (int64_t)a.max_blocks_per_seq * a.block_size;
+    const int64_t cap_grid = (int64_t)a.num_partitions * a.partition_size;
+    const int64_t cap = cap_table < cap_grid ? cap_table : cap_grid;
+    p.len_cap = (int32_t)(cap > INT32_MAX ? INT32_MAX : cap);
+    p.ws_o = a.ws_o;
+    p.ws_ml = a.ws_ml;
+
+    const size_t lds = lds_bytes<T, D, BS, G>(a.partition_size);
+    const dim3 grid((unsigned)a.num_partitions, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), lds, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.num_partitions <= 1)
+        return e;
+    hipLaunchKernelGGL((reduce_kernel<D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs),
+                       dim3(D), 0, stream, a.out, (int)a.out_dtype, a.ws_o, a.ws_ml,
+                       a.context_lens, a.num_q_heads, a.partition_size, a.num_partitions,
+                       p.len_cap);
+    return hipGetLastError();
+}
+
+template <class T, int D, int BS>
+hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s)
+{
+    switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_typed<T, D, BS, 1>(a, s);
+    case 2: return launch_typed<T, D, BS, 2>(a, s);
+    case 4: return launch_typed<T, D, BS, 4>(a, s);
+    case 8: return launch_typed<T, D, BS, 8>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T, int D>
+hipError_t dispatch_block(const DecodeArgs &a, hipStream_t s)
+{
+    switch (a.block_size) {
+    case 16: return dispatch_group<T, D, 16>(a, s);
+    case 32: return dispatch_group<T, D, 32>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t dispatch_dim(const DecodeArgs &a, hipStream_t s)
+{
+    switch (a.head_dim) {
+    case 64: return dispatch_block<T, 64>(a, s);
+    case 128: return dispatch_block<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_supported(DType kv, int head_dim, int block_size, int group)
+{
+    (void)kv;
+    return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32) &&
+           (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream)
+{
+    if (a.num_seqs == 0)
+        return hipSuccess;
+    switch (a.kv_dtype) {
+    case DType::F32: return dispatch_dim<TF32>(a, stream);
+    case DType::F16: return dispatch_dim<TF16>(a, stream);
+    case DType::BF16: return dispatch_dim<TBF16>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pka

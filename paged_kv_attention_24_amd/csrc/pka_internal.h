@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the kernel
+// translation units.  Not installed; the public surface is include/pka.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pka {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+inline int dtype_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
+
+struct WriteArgs {
+    const void *k, *v;
+    int64_t k_token_stride, v_token_stride;  // elements
+    const int64_t *slot_mapping;
+    int32_t num_tokens;
+    void *k_cache, *v_cache;
+    int32_t num_blocks, block_size, num_kv_heads, head_dim;
+    DType dtype;
+};
+
+hipError_t launch_kv_cache_write(const WriteArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    void *out;
+    DType out_dtype;
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+    int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int32_t num_blocks, block_size;
+    float scale;
+    DType kv_dtype;
+    int32_t max_context_len;  // resolved (> 0 unless num_seqs == 0)
+    int32_t partition_size;   // resolved, multiple of block_size
+    int32_t num_partitions;   // ceil(max_context_len / partition_size), >= 1
+    float *ws_o;              // [B][Hq][num_partitions][D]    (if num_partitions > 1)
+    float *ws_ml;             // [B][Hq][num_partitions][2]    (max in log2 units, sum)
+};
+
+// Whether (dtype, head_dim, block_size, group) has a compiled kernel.
+bool decode_supported(DType kv, int head_dim, int block_size, int group);
+
+// Largest partition the kernels accept (bounds their LDS use).
+constexpr int kMaxPartition = 1024;
+
+hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace pka

@@ -122,6 +122,7 @@ def make_case(
     max_blocks_per_seq: Optional[int] = None,
     name: str = "case",
     rng: Optional[np.random.Generator] = None,
+    pools: bool = True,
 ) -> Workload:
     """Build a workload with the given context lengths.
 
@@ -159,8 +160,10 @@ def make_case(
         cursor += n
     # 3./4. pools
     shape = (pool_blocks, num_kv_heads, bs, head_dim)
-    k_cache = _round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
-    v_cache = _round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+    k_cache = v_cache = None
+    if pools:
+        k_cache = _round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+        v_cache = _round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
     # 5. q
     q = _round_to_dtype(
         rng.standard_normal((B, num_q_heads, head_dim), dtype=np.float32), dtype
@@ -179,7 +182,7 @@ def make_case(
             if lens[b] > 0:
                 pos = int(lens[b]) - 1
                 slots[b] = int(block_tables[b, pos // bs]) * bs + pos % bs
-    if poison:
+    if poison and pools:
         bad = _poison(k_cache, dtype)
         in_use = np.zeros(pool_blocks, dtype=bool)
         in_use[perm[:used]] = True
@@ -268,14 +271,14 @@ CONFIG_SHAPES = {
 
 
 def make_config(cfg: int, *, seed: Optional[int] = None, poison: bool = True,
-                write: bool = True) -> Workload:
+                write: bool = True, pools: bool = True) -> Workload:
     """Named workload ``cfg`` (1..5); ``seed`` defaults to the workload number."""
     seed = cfg if seed is None else seed
     rng = np.random.default_rng(seed)
     lens = config_lens(cfg, rng)
     shape = dict(CONFIG_SHAPES[cfg])
     wl = make_case(seed, context_lens=lens, poison=poison, write=write, rng=rng,
-                   name=f"cfg{cfg}", **shape)
+                   name=f"cfg{cfg}", pools=pools, **shape)
     wl.meta["config"] = cfg
     wl.meta["description"] = CONFIG_NAMES[cfg]
     return wl

@@ -1,0 +1,123 @@
+"""Host side of the C ABI (no GPU): the library loads, exports every symbol
+the header declares, and rejects bad arguments before any launch."""
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_24_amd as pka
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "pka.h")
+
+# fake, 256-byte aligned, never dereferenced: every call below fails validation
+FAKE = 0x10000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pka_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = pka.load_library()
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pka.h but not exported"
+
+
+def test_abi_version_and_strings():
+    lib = pka.load_library()
+    assert lib.pka_abi_version() == 1
+    assert lib.pka_status_string(0) == b"ok"
+    assert lib.pka_status_string(3) == b"workspace too small"
+    assert lib.pka_status_string(99) == b"unknown status"
+
+
+def write(**over):
+    args = dict(k=FAKE, v=FAKE, ks=512, vs=512, slots=FAKE, T=4, kc=FAKE, vc=FAKE, NB=10,
+                bs=16, H=8, D=64, dt=1)
+    args.update(over)
+    lib = pka.load_library()
+    st = lib.pka_kv_cache_write(args["k"], args["v"], args["ks"], args["vs"], args["slots"],
+                                args["T"], args["kc"], args["vc"], args["NB"], args["bs"],
+                                args["H"], args["D"], args["dt"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-1), 1), (dict(dt=7), 1), (dict(NB=0), 1), (dict(H=0), 1),
+    (dict(D=96), 2), (dict(bs=8), 2), (dict(kc=None), 1), (dict(vc=FAKE + 8), 1),
+    (dict(k=None), 1), (dict(slots=None), 1), (dict(ks=511), 1), (dict(vs=100), 1),
+    (dict(k=FAKE + 4), 1), (dict(ks=516), 1),
+])
+def test_write_rejects(over, status):
+    st, msg = write(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+def test_write_zero_tokens_is_ok_without_launch():
+    st, _ = write(T=0, k=None, v=None, slots=None)
+    assert st == 0
+
+
+def decode(**over):
+    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=64, cl=FAKE, B=16, Hq=32,
+             Hkv=8, D=64, NB=1000, bs=16, scale=0.125, kdt=1, maxl=1024, P=0, ws=FAKE,
+             wsb=1 << 30)
+    a.update(over)
+    lib = pka.load_library()
+    st = lib.pka_paged_attention_decode(a["out"], a["odt"], a["q"], a["kc"], a["vc"], a["bt"],
+                                        a["MB"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                        a["NB"], a["bs"], a["scale"], a["kdt"], a["maxl"], a["P"],
+                                        a["ws"], a["wsb"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(NB=0), 1),
+    (dict(MB=0), 1), (dict(B=-1), 1), (dict(D=80), 2), (dict(bs=64), 2), (dict(Hq=128), 2),
+    (dict(Hq=24), 2), (dict(scale=float("nan")), 1), (dict(P=24), 1), (dict(P=-16), 1),
+    (dict(P=2048), 2), (dict(q=None), 1), (dict(out=FAKE + 2), 1), (dict(ws=None), 3),
+    (dict(wsb=100), 3), (dict(ws=FAKE + 16), 1), (dict(B=70000), 2), (dict(cl=None), 1),
+])
+def test_decode_rejects(over, status):
+    st, msg = decode(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+def test_decode_empty_batch_is_ok_without_launch():
+    st, _ = decode(B=0, out=None, q=None)
+    assert st == 0
+
+
+def test_partition_heuristic():
+    for B, H, bs, L in [(16, 8, 16, 1024), (64, 8, 16, 4096), (128, 8, 16, 8192),
+                        (256, 8, 32, 32768), (1, 1, 32, 5), (4096, 8, 16, 100)]:
+        P = pka.decode_partition_size(B, H, bs, L)
+        assert P % bs == 0 and bs <= P <= 1024, (B, H, bs, L, P)
+    # small batches split finer than large ones
+    assert pka.decode_partition_size(16, 8, 16, 1024) < pka.decode_partition_size(128, 8, 16, 8192)
+
+
+def test_workspace_bytes():
+    assert pka.decode_workspace_bytes(16, 32, 64, 512, 512) == 0  # one partition
+    n = pka.decode_workspace_bytes(16, 32, 64, 1024, 64)
+    rows = 16 * 32 * 16
+    assert n == ((rows * 64 * 4 + 255) // 256) * 256 + rows * 8
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    kc = torch.zeros(4, 2, 16, 64)
+    with pytest.raises(ValueError):
+        pka.kv_cache_write(torch.zeros(1, 2, 64), torch.zeros(1, 2, 64),
+                           torch.zeros(1, dtype=torch.int64), kc, kc.clone())
+    with pytest.raises(ValueError):
+        pka.paged_attention_decode(torch.zeros(1, 4, 64), kc, kc, torch.zeros(1, 1, dtype=torch.int32),
+                                   torch.ones(1, dtype=torch.int32), 0.125, 2, 16)
