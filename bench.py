@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a HIP graph")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="override the library's partition length (tokens)")
     return ap.parse_args()
 
 
@@ -113,7 +115,8 @@ def main():
         else:
             kcs.append(fill_pool(shape, tdt, 1000 + 2 * r, dev))
             vcs.append(fill_pool(shape, tdt, 1001 + 2 * r, dev))
-    P = wl.partition_size or pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
+    P = args.partition_size or wl.partition_size or \
+        pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
     ws_bytes = pka.decode_workspace_bytes(B, Hq, D, wl.max_context_len, P)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
@@ -180,24 +183,6 @@ def main():
     us_decode = ms_decodes * 1e3 / R
     achieved = alg_bytes / (us_decode * 1e-6) / 1e9
 
-    # parity spot check of this exact launch configuration (first pool)
-    parity = None
-    if host_pools:
-        import oracle
-
-        torch.cuda.synchronize()
-        decode(0)
-        torch.cuda.synchronize()
-        kc_h = W.to_numpy_bits(kcs[0], wl.dtype)
-        vc_h = W.to_numpy_bits(vcs[0], wl.dtype)
-        rows = np.array([[b, h] for b in range(0, B, max(1, B // 8)) for h in (0, Hq - 1)],
-                        dtype=np.int32)
-        ref = oracle.paged_attention_decode(wl.q, kc_h, vc_h, wl.block_tables, wl.context_lens,
-                                            wl.scale, Hkv, bs, wl.dtype, rows=rows)
-        got = outs[0].double().cpu().numpy()[rows[:, 0], rows[:, 1]]
-        parity = float(np.max(np.abs(got - ref)))
-        log(f"parity (sampled rows vs fp64 oracle): max-abs {parity:.3g}")
-
     cpu = None
     if not args.no_cpu_baseline and host_pools:
         import oracle
@@ -250,7 +235,6 @@ def main():
         },
         "us_per_layer": round(us_per_layer, 3),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "parity_max_abs_sampled": parity,
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attention_decode (partition + merge kernels)",

@@ -170,8 +170,8 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     [B, MB]; context_lens int32 [B] (device).  Returns out [B, Hq, D], fp32
     unless ``out_dtype`` (or ``out``) says the KV dtype.  ``max_context_len``
     is an optional host hint (no device sync); ``partition_size`` 0 lets the
-    library choose.  ``workspace`` (uint8 device tensor) is allocated when not
-    given.
+    library choose.  ``workspace`` (uint8 device tensor) defaults to a cached
+    one per device.
     """
     import torch
 
@@ -211,8 +211,11 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     P = partition_size if partition_size > 0 else decode_partition_size(B, Hkv, bs, hint)
     need = decode_workspace_bytes(B, Hq, D, hint, P)
     if need > 0:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            workspace = _cached_workspace(q.device, need)
+        elif workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {need} needed")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     else:
         ws_ptr, ws_bytes = None, 0
@@ -222,6 +225,21 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         NB, bs, float(scale), _dtype_code(k_cache.dtype), hint, P, ws_ptr, ws_bytes,
         _stream_ptr(q.device)))
     return out
+
+
+_WORKSPACES = {}
+
+
+def _cached_workspace(device, nbytes: int):
+    """A scratch workspace per device, grown on demand.  Calls that run
+    concurrently on different streams must pass workspaces of their own."""
+    import torch
+
+    ws = _WORKSPACES.get(device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WORKSPACES[device] = ws
+    return ws
 
 
 class PagedKVCache:

@@ -192,7 +192,9 @@ struct PartitionParams {
     int32_t num_q_heads, num_kv_heads, num_blocks;
     float scale_log2;  // scale * log2(e)
     int32_t partition_size, num_partitions, len_cap;
-    float *ws_o, *ws_ml;
+    float *ws_o, *ws_ml;  // per (b, hq, partition): normalised row; (max, sum)
+    const int2 *items;    // work list {b, j} (null: dense grid over (j, h, b))
+    int32_t *wl_header;   // [0] next dynamic item, [1] number of {b, j} items
 };
 
 template <class T, int D, int BS, int G>
@@ -210,177 +212,185 @@ struct Shape {
 };
 
 template <class T, int D, int BS, int G>
-__host__ __device__ constexpr int chunks_per_wave(int partition_size)
+__host__ __device__ constexpr size_t lds_bytes()
 {
     using S = Shape<T, D, BS, G>;
-    const int chunks = (partition_size + S::CT - 1) / S::CT;
-    return (chunks + S::NW - 1) / S::NW;
+    return (size_t)S::NW * S::TPL * G * (D + 1) * 4 + (size_t)S::NW * G * 4;
 }
 
 template <class T, int D, int BS, int G>
-__host__ __device__ constexpr size_t lds_bytes(int partition_size)
+__global__ void partition_kernel(PartitionParams p);
+
+// Workgroups of partition_kernel<...> that fit the device at once.
+template <class T, int D, int BS, int G>
+int resident_workgroups()
 {
-    using S = Shape<T, D, BS, G>;
-    const size_t logits = (size_t)S::NW * chunks_per_wave<T, D, BS, G>(partition_size) * S::CT * G * 4;
-    const size_t merge = (size_t)S::NW * S::TPL * G * (D + 1) * 4 + (size_t)S::NW * G * 4;
-    return logits > merge ? logits : merge;
+    static int cached[64];  // per device ordinal; 0 = not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 1024;
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, partition_kernel<T, D, BS, G>, Shape<T, D, BS, G>::NW * kWave,
+            lds_bytes<T, D, BS, G>() + 16);
+        cached[dev] = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+    }
+    return cached[dev];
 }
 
+// One work item: the tokens [j*P, min((j+1)*P, L_b)) of kv head h of
+// sequence b, for all G query heads of the group.  Called by every thread
+// of the workgroup with the same (b, h, j).
 template <class T, int D, int BS, int G>
-__global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_kernel(PartitionParams p)
+__device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h, int j,
+                                          float *smem)
 {
     using S = Shape<T, D, BS, G>;
     constexpr int NW = S::NW, LPR = S::LPR, TPL = S::TPL, NL = S::NL, CT = S::CT, VEC = S::VEC;
-    extern __shared__ float smem[];
 
-    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    // wave index, provably uniform: block ids and chunk bounds stay scalar
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int tg = lane / LPR, cl = lane % LPR;
-
-    int L = p.context_lens[b];
-    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
     const int P = p.partition_size;
     const int t_begin = j * P;
+    const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+
+    // The partition's block ids (P / BS <= 64 of them), one per lane,
+    // requested together with the length.  Row indices are clamped into the
+    // table and ids into the pool, so every later access stays in bounds.
+    static_assert(kMaxPartition / BS <= kWave, "a partition's block ids must fit one wave");
+    const int pb0 = t_begin / BS;
+    int ids;
+    {
+        const int idx = pb0 + lane;
+        ids = bt[idx < p.max_blocks_per_seq ? idx : p.max_blocks_per_seq - 1];
+        ids = ids < 0 ? 0 : (ids > p.num_blocks - 1 ? p.num_blocks - 1 : ids);
+    }
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
     if (t_begin >= L && !(L == 0 && j == 0))
         return;  // uniform over the workgroup
     const int t_end = min(t_begin + P, L);
     const int nchunks = (t_end - t_begin + CT - 1) / CT;
     const int nk = nchunks > w ? (nchunks - w + NW - 1) / NW : 0;  // chunks of this wave
+    const int last_blk = t_end > 0 ? (t_end - 1) / BS - pb0 : 0;   // partition-relative
 
     // query rows of the group: 16 bytes per lane per head
     uint4 qr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g)
         qr[g] = *reinterpret_cast<const uint4 *>(
-            p.q + ((int64_t)(b * p.num_q_heads + h * G + g) * D + cl * VEC) * S::ELT);
+            p.q + (((int64_t)b * p.num_q_heads + h * G + g) * D + cl * VEC) * S::ELT);
 
-    const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
     const int64_t head_off = (int64_t)h * S::TILE;
     const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
-    const int nb_max = p.num_blocks - 1;
 
-    // load the NL wave loads of chunk k of this wave from `pool` into r
-    auto load_chunk = [&](const char *pool, int k, uint4 *r) {
+    // K and V of chunk k of this wave: NL wave loads each, issued without
+    // conditions (so the compiler's wait counts stay exact).  Loads past the
+    // partition's last token re-read its last block; those tokens are masked
+    // when the chunk is processed.
+    auto load_chunk = [&](int k, uint4 *kr, uint4 *vr) {
         const int tc = t_begin + (w + k * NW) * CT;
-        const bool full = tc + CT <= t_end;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int t0 = tc + i * TPL;
-            if (full || t0 < t_end) {
-                int blk = bt[t0 / BS];
-                blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
-                const char *src = pool + blk * block_stride + head_off +
-                                  (int64_t)(t0 % BS) * (D * S::ELT) + lane * 16;
-                r[i] = *reinterpret_cast<const uint4 *>(src);
-            } else {
-                r[i] = make_uint4(0, 0, 0, 0);
-            }
+            int rb = t0 / BS - pb0;
+            rb = rb < last_blk ? rb : last_blk;
+            const int blk = __builtin_amdgcn_readlane(ids, rb);
+            const int64_t off = blk * block_stride + head_off +
+                                (int64_t)(t0 % BS) * (D * S::ELT) + lane * 16;
+            kr[i] = *reinterpret_cast<const uint4 *>(p.k_cache + off);
+            vr[i] = *reinterpret_cast<const uint4 *>(p.v_cache + off);
         }
     };
 
-    // ---- pass 1: logits -------------------------------------------------
-    float *lds_s = smem + (size_t)w * chunks_per_wave<T, D, BS, G>(P) * CT * G;
-    float mloc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        mloc[g] = -INFINITY;
-
-    auto logits_chunk = [&](int k, const uint4 *r) {
-        const int tc = t_begin + (w + k * NW) * CT;
-        const bool full = tc + CT <= t_end;
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int tok = tc + i * TPL + tg;
-            float s[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                s[g] = group_sum<LPR>(dot16(T{}, qr[g], r[i], 0.0f)) * p.scale_log2;
-                if (!full)
-                    s[g] = tok < t_end ? s[g] : -INFINITY;
-                mloc[g] = fmaxf(mloc[g], s[g]);
-            }
-            if (cl == 0) {
-                float *dst = lds_s + (k * CT + i * TPL + tg) * G;
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    dst[g] = s[g];
-            }
-        }
-    };
-
-    {
-        uint4 ra[NL], rb[NL];
-        if (nk > 0)
-            load_chunk(p.k_cache, 0, ra);
-        for (int k = 0; k < nk; k += 2) {
-            if (k + 1 < nk)
-                load_chunk(p.k_cache, k + 1, rb);
-            logits_chunk(k, ra);
-            if (k + 1 >= nk)
-                break;
-            if (k + 2 < nk)
-                load_chunk(p.k_cache, k + 2, ra);
-            logits_chunk(k + 1, rb);
-        }
-    }
-
-    float mw[G], mref[G];
+    // Online softmax per lane (each lane sees one token of every load).
+    float m[G], l[G], o[G][VEC];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        mw[g] = wave_max(mloc[g]);
-        mref[g] = mw[g] == -INFINITY ? 0.0f : mw[g];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- pass 2: softmax weights and values -------------------------------
-    float o[G][VEC];
-    float lsum[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        lsum[g] = 0.0f;
+        m[g] = -INFINITY;
+        l[g] = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             o[g][e] = 0.0f;
     }
 
-    auto values_chunk = [&](int k, uint4 *r) {
+    auto process = [&](int k, const uint4 *kr, uint4 *vr) {
         const int tc = t_begin + (w + k * NW) * CT;
         const bool full = tc + CT <= t_end;
+        float s[NL][G];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int tok = tc + i * TPL + tg;
-            if (!full && tok >= t_end)
-                r[i] = make_uint4(0, 0, 0, 0);  // select, so NaN bits never reach o
-            const float *src = lds_s + (k * CT + i * TPL + tg) * G;
+            const bool valid = full || tc + i * TPL + tg < t_end;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float pw = __builtin_amdgcn_exp2f(src[g] - mref[g]);
-                lsum[g] += pw;
-                axpy16(T{}, pw, r[i], o[g]);
+                s[i][g] = group_sum<LPR>(dot16(T{}, qr[g], kr[i], 0.0f)) * p.scale_log2;
+                if (!full)
+                    s[i][g] = valid ? s[i][g] : -INFINITY;
+            }
+            if (!full && !valid)
+                vr[i] = make_uint4(0, 0, 0, 0);  // select: NaN bits never reach o
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float cm = s[0][g];
+#pragma unroll
+            for (int i = 1; i < NL; ++i)
+                cm = fmaxf(cm, s[i][g]);
+            const float m_new = fmaxf(m[g], cm);
+            const float mr = m_new == -INFINITY ? 0.0f : m_new;
+            const float corr = __builtin_amdgcn_exp2f(m[g] - mr);
+            l[g] *= corr;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                o[g][e] *= corr;
+            m[g] = m_new;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const float pw = __builtin_amdgcn_exp2f(s[i][g] - mr);
+                l[g] += pw;
+                axpy16(T{}, pw, vr[i], o[g]);
             }
         }
     };
 
-    {
-        uint4 ra[NL], rb[NL];
-        if (nk > 0)
-            load_chunk(p.v_cache, 0, ra);
-        for (int k = 0; k < nk; k += 2) {
-            if (k + 1 < nk)
-                load_chunk(p.v_cache, k + 1, rb);
-            values_chunk(k, ra);
-            if (k + 1 >= nk)
-                break;
-            if (k + 2 < nk)
-                load_chunk(p.v_cache, k + 2, ra);
-            values_chunk(k + 1, rb);
+    // Software pipeline: the loads of chunk k+1 are in flight while chunk k
+    // is processed; the steady-state loop issues its loads unconditionally.
+    if (nk > 0) {
+        uint4 ka[NL], va[NL], kb[NL], vb[NL];
+        load_chunk(0, ka, va);
+        int k = 0;
+        for (; k + 2 < nk; k += 2) {
+            load_chunk(k + 1, kb, vb);
+            process(k, ka, va);
+            load_chunk(k + 2, ka, va);
+            process(k + 1, kb, vb);
+        }
+        if (k + 1 < nk) {
+            load_chunk(k + 1, kb, vb);
+            process(k, ka, va);
+            process(k + 1, kb, vb);
+        } else {
+            process(k, ka, va);
         }
     }
 
+    // Rescale every lane to the wave's maximum.
+    float mw[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        mw[g] = wave_max(m[g]);
+        const float f = __builtin_amdgcn_exp2f(m[g] - (mw[g] == -INFINITY ? 0.0f : mw[g]));
+        l[g] *= f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            o[g][e] *= f;
+    }
+
     // ---- merge token groups and waves (log-sum-exp with the wave maxima) --
-    __syncthreads();  // logits area is reused below
     float *red = smem;                                  // [NW][TPL][G][D]
     float *lred = red + (size_t)NW * TPL * G * D;       // [NW][TPL][G]
     float *mred = lred + (size_t)NW * TPL * G;          // [NW][G]
@@ -394,7 +404,7 @@ __global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_ke
     if (cl == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            lred[(w * TPL + tg) * G + g] = lsum[g];
+            lred[(w * TPL + tg) * G + g] = l[g];
     }
     if (lane == 0) {
 #pragma unroll
@@ -415,14 +425,14 @@ __global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_ke
         for (int ww = 0; ww < NW; ++ww) {
             const float mv = mred[ww * G + g];
             const float sc = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            float a = 0.0f, l = 0.0f;
+            float a = 0.0f, ls = 0.0f;
 #pragma unroll
             for (int t = 0; t < TPL; ++t) {
                 a += red[((size_t)(ww * TPL + t) * G + g) * D + d];
-                l += lred[(ww * TPL + t) * G + g];
+                ls += lred[(ww * TPL + t) * G + g];
             }
             acc = fmaf(a, sc, acc);
-            den = fmaf(l, sc, den);
+            den = fmaf(ls, sc, den);
         }
         const float res = den > 0.0f ? acc / den : 0.0f;
         const int hq = h * G + g;
@@ -436,6 +446,84 @@ __global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_ke
                 p.ws_ml[row * 2 + 1] = den;
             }
         }
+    }
+}
+
+template <class T, int D, int BS, int G>
+__global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_kernel(PartitionParams p)
+{
+    extern __shared__ float smem[];
+    if (p.items == nullptr) {
+        work_item<T, D, BS, G>(p, blockIdx.z, blockIdx.y, blockIdx.x, smem);
+        return;
+    }
+    // Work-list mode (skewed batches): a persistent grid.  Workgroup g starts
+    // with item g and then takes the next unclaimed item from the counter the
+    // plan kernel initialised to the grid size.
+    int *slot = reinterpret_cast<int *>(smem + lds_bytes<T, D, BS, G>() / 4);
+    const int hkv = p.num_kv_heads;
+    const int total = p.wl_header[1] * hkv;
+    int u = blockIdx.x;
+    while (u < total) {
+        int next = 0;
+        if (threadIdx.x == 0)
+            next = atomicAdd(&p.wl_header[0], 1);  // consumed after the item
+        const int sidx = u / hkv;
+        const int2 it = p.items[sidx];
+        work_item<T, D, BS, G>(p, it.x, u - sidx * hkv, it.y, smem);
+        if (threadIdx.x == 0)
+            *slot = next;
+        __syncthreads();
+        u = __builtin_amdgcn_readfirstlane(*slot);
+        __syncthreads();
+    }
+}
+
+// Build the work list of a skewed batch: every sequence b contributes
+// max(1, ceil(L_b / P)) items {b, j}, in batch order.  One workgroup.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *context_lens, int32_t num_seqs,
+                                                    int32_t partition_size, int32_t len_cap,
+                                                    int2 *items, int32_t *header,
+                                                    int32_t first_dynamic)
+{
+    __shared__ int wave_tot[1024 / kWave];
+    __shared__ int wave_off[1024 / kWave];
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    int carry = 0;
+    for (int base = 0; base < num_seqs; base += 1024) {
+        const int i = base + threadIdx.x;
+        int n = 0;
+        if (i < num_seqs) {
+            int L = context_lens[i];
+            L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
+            n = L == 0 ? 1 : (L + partition_size - 1) / partition_size;
+        }
+        int x = n;  // inclusive scan within the wave
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_up(x, off, kWave);
+            if (lane >= off)
+                x += y;
+        }
+        if (lane == kWave - 1)
+            wave_tot[wv] = x;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int acc = 0;
+            for (int k = 0; k < 1024 / kWave; ++k) {
+                wave_off[k] = acc;
+                acc += wave_tot[k];
+            }
+        }
+        __syncthreads();
+        const int start = carry + wave_off[wv] + x - n;
+        for (int jj = 0; jj < n; ++jj)
+            items[start + jj] = make_int2(i, jj);
+        carry += wave_off[1024 / kWave - 1] + wave_tot[1024 / kWave - 1];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        header[0] = first_dynamic;
+        header[1] = carry;
     }
 }
 
@@ -492,11 +580,28 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
     p.len_cap = (int32_t)(cap > INT32_MAX ? INT32_MAX : cap);
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
+    p.items = a.items;
+    p.wl_header = a.wl_header;
 
-    const size_t lds = lds_bytes<T, D, BS, G>(a.partition_size);
-    const dim3 grid((unsigned)a.num_partitions, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), lds, stream, p);
-    hipError_t e = hipGetLastError();
+    const size_t lds = lds_bytes<T, D, BS, G>() + 16;
+    hipError_t e;
+    if (a.items) {
+        const int64_t dense = (int64_t)a.num_partitions * a.num_kv_heads * a.num_seqs;
+        const int64_t res = resident_workgroups<T, D, BS, G>();
+        const int grid = (int)(dense < res ? dense : res);
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
+                           a.num_seqs, a.partition_size, p.len_cap, a.items, a.wl_header, grid);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), dim3(grid), dim3(S::NW * kWave), lds,
+                           stream, p);
+    } else {
+        const dim3 grid((unsigned)a.num_partitions, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+        hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), lds, stream,
+                           p);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess || a.num_partitions <= 1)
         return e;
     hipLaunchKernelGGL((reduce_kernel<D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs),

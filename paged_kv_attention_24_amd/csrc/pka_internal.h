@@ -41,7 +41,23 @@ struct DecodeArgs {
     int32_t num_partitions;   // ceil(max_context_len / partition_size), >= 1
     float *ws_o;              // [B][Hq][num_partitions][D]    (if num_partitions > 1)
     float *ws_ml;             // [B][Hq][num_partitions][2]    (max in log2 units, sum)
+    int2 *items;              // work list {b, j}, [B * num_partitions]; null: dense grid
+    int32_t *wl_header;       // [2]: dynamic-item counter, item count (work-list mode)
 };
+
+// Above this many partitions per sequence the decode builds a work list on
+// the device instead of launching a dense (partition, head, sequence) grid
+// whose workgroups past a short sequence's end would exit empty.
+constexpr int kDenseMaxPartitions = 8;
+
+// Byte offsets of the decode workspace's two regions (256-aligned starts)
+// and its total size; zero when one partition covers every sequence.
+struct WorkspaceLayout {
+    size_t o_offset, ml_offset, header_offset, items_offset, total;
+    bool worklist;
+};
+WorkspaceLayout decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                                        int64_t num_partitions);
 
 // Whether (dtype, head_dim, block_size, group) has a compiled kernel.
 bool decode_supported(DType kv, int head_dim, int block_size, int group);

@@ -100,15 +100,25 @@ def test_partition_heuristic():
                         (256, 8, 32, 32768), (1, 1, 32, 5), (4096, 8, 16, 100)]:
         P = pka.decode_partition_size(B, H, bs, L)
         assert P % bs == 0 and bs <= P <= 1024, (B, H, bs, L, P)
-    # small batches split finer than large ones
-    assert pka.decode_partition_size(16, 8, 16, 1024) < pka.decode_partition_size(128, 8, 16, 8192)
+    assert pka.decode_partition_size(16, 8, 16, 1024) == 512
+    assert pka.decode_partition_size(128, 8, 16, 8192) == 512
+    # one long sequence: split finer so that the work items cover the GPU
+    assert pka.decode_partition_size(1, 8, 16, 4096) == 128
+
+
+def r256(x):
+    return (x + 255) // 256 * 256
 
 
 def test_workspace_bytes():
     assert pka.decode_workspace_bytes(16, 32, 64, 512, 512) == 0  # one partition
-    n = pka.decode_workspace_bytes(16, 32, 64, 1024, 64)
+    # 8 partitions: dense grid, partial rows + (max, sum) pairs
+    rows = 16 * 32 * 8
+    assert pka.decode_workspace_bytes(16, 32, 64, 1024, 128) == r256(rows * 64 * 4) + r256(rows * 8)
+    # 16 partitions: a device-built work list follows (256-byte header, {b, j} items)
     rows = 16 * 32 * 16
-    assert n == ((rows * 64 * 4 + 255) // 256) * 256 + rows * 8
+    n = pka.decode_workspace_bytes(16, 32, 64, 1024, 64)
+    assert n == r256(rows * 64 * 4) + r256(rows * 8) + 256 + r256(16 * 16 * 8)
 
 
 def test_python_binding_refuses_cpu_tensors():

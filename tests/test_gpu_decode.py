@@ -169,6 +169,17 @@ def test_long_single_sequence_many_partitions():
     check_close(got[0], ref, "f16", "32k")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_skewed_work_list(dtype):
+    """Many partitions per sequence (device-built work list, persistent
+    grid): one long sequence among short and empty ones."""
+    lens = [0, 5000, 1, 33, 0, 700, 16, 17] + [100] * 40
+    wl = case(13, dtype, lens, 16, 4, 64, 16)
+    got = gpu_decode(wl, partition_size=64)  # 79 partitions for the longest
+    check_close(got, oracle_full(wl), dtype, "work list")
+    assert np.all(got[0] == 0) and np.all(got[4] == 0)
+
+
 def test_bad_partition_size_is_rejected():
     import paged_kv_attention_24_amd as pka
 
