@@ -118,7 +118,7 @@ def main():
     P = args.partition_size or wl.partition_size or \
         pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
     ws_bytes = pka.decode_workspace_bytes(B, Hq, D, wl.max_context_len, P)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # counters start at 0
     outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
     torch.cuda.synchronize()
 

@@ -170,8 +170,9 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     [B, MB]; context_lens int32 [B] (device).  Returns out [B, Hq, D], fp32
     unless ``out_dtype`` (or ``out``) says the KV dtype.  ``max_context_len``
     is an optional host hint (no device sync); ``partition_size`` 0 lets the
-    library choose.  ``workspace`` (uint8 device tensor) defaults to a cached
-    one per device.
+    library choose.  ``workspace`` (uint8 device tensor, zero-filled before
+    its first use; each call leaves it reusable) defaults to a cached one per
+    device.
     """
     import torch
 
@@ -231,13 +232,17 @@ _WORKSPACES = {}
 
 
 def _cached_workspace(device, nbytes: int):
-    """A scratch workspace per device, grown on demand.  Calls that run
-    concurrently on different streams must pass workspaces of their own."""
+    """A zero-filled workspace per device, grown on demand.
+
+    Its leading completion counters start at zero and every decode leaves
+    them zero, so the buffer is reusable by later calls; calls that run
+    concurrently on different streams must pass workspaces of their own.
+    """
     import torch
 
     ws = _WORKSPACES.get(device)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 2 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[device] = ws
     return ws
 

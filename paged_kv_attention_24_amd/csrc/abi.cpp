@@ -48,12 +48,13 @@ int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 pka::WorkspaceLayout pka::decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads,
                                                   int64_t head_dim, int64_t num_partitions)
 {
-    WorkspaceLayout w{0, 0, 0, 0, 0, false};
+    WorkspaceLayout w{0, 0, 0, 0, 0, 0, false};
     if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_partitions <= 1)
         return w;
     const int64_t rows = num_seqs * num_q_heads * num_partitions;
-    w.o_offset = 0;
-    w.ml_offset = (size_t)round256(rows * head_dim * 4);
+    w.counter_offset = 0;
+    w.o_offset = (size_t)kCounterBytes;
+    w.ml_offset = w.o_offset + (size_t)round256(rows * head_dim * 4);
     w.total = w.ml_offset + (size_t)round256(rows * 2 * 4);
     if (num_partitions > kDenseMaxPartitions) {
         w.worklist = true;
@@ -210,6 +211,11 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
         return fail(PKA_ERR_UNSUPPORTED, "too many partitions");
     const size_t need = pka_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
                                                    (int32_t)lmax, partition_size);
+    if (need > 0 && (int64_t)num_seqs * num_kv_heads * 4 > pka::kCounterBytes)
+        return fail(PKA_ERR_UNSUPPORTED,
+                    "num_seqs * num_kv_heads = %lld exceeds the %lld completion counters of a "
+                    "multi-partition workspace",
+                    (long long)num_seqs * num_kv_heads, (long long)(pka::kCounterBytes / 4));
     if (need > 0) {
         if (!workspace)
             return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);
@@ -243,6 +249,7 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
         const pka::WorkspaceLayout w =
             pka::decode_workspace_layout(num_seqs, num_q_heads, head_dim, parts);
         char *base = static_cast<char *>(workspace);
+        a.counters = reinterpret_cast<int32_t *>(base + w.counter_offset);
         a.ws_o = reinterpret_cast<float *>(base + w.o_offset);
         a.ws_ml = reinterpret_cast<float *>(base + w.ml_offset);
         if (w.worklist) {

@@ -31,8 +31,9 @@
 //  * Merge: per-lane partial sums (token groups x waves) are combined in LDS
 //    with each wave's maximum (log-sum-exp), once per work item.
 //  * Partitions: with more than one partition per sequence each work item
-//    writes (max, sum, normalised row) to the workspace and a small second
-//    kernel merges them; otherwise the first kernel writes the output.
+//    writes (max, sum, normalised row) to the workspace and counts itself
+//    done; the last one of its (sequence, kv head) merges all of them into
+//    the output (log-sum-exp) and resets the counter.  One launch per call.
 //  * Every K/V load is issued one chunk ahead of its use (register double
 //    buffering), so each wave keeps up to 8 KiB in flight.
 //  * Tokens >= L (the tail of the last block) are excluded by selects, never
@@ -182,6 +183,21 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float x, int o
         static_cast<uint16_t *>(out)[idx] = f32_to_bf16_rne(x);
 }
 
+// Agent-scope relaxed accesses: plain loads/stores with the coherence bit,
+// so partial rows written on one XCD are read correctly on another without
+// flushing or invalidating any L2.
+__device__ __forceinline__ void coherent_store(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every store of this
+// wave has been acknowledged.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 struct PartitionParams {
     void *out;
     int out_kind;  // 0 f32, 1 f16, 2 bf16
@@ -195,6 +211,7 @@ struct PartitionParams {
     float *ws_o, *ws_ml;  // per (b, hq, partition): normalised row; (max, sum)
     const int2 *items;    // work list {b, j} (null: dense grid over (j, h, b))
     int32_t *wl_header;   // [0] next dynamic item, [1] number of {b, j} items
+    int32_t *counters;    // per (b, kv head): partitions done; zero between calls
 };
 
 template <class T, int D, int BS, int G>
@@ -439,14 +456,53 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
         if (nparts_b == 1) {
             store_out(p.out, ((int64_t)b * p.num_q_heads + hq) * D + d, res, p.out_kind);
         } else {
+            // coherent (agent-scope) stores: the merging workgroup may run on
+            // another XCD, whose L2 does not see this one's write-back lines
             const int64_t row = ((int64_t)b * p.num_q_heads + hq) * p.num_partitions + j;
-            p.ws_o[row * D + d] = res;
+            coherent_store(&p.ws_o[row * D + d], res);
             if (d == 0) {
-                p.ws_ml[row * 2 + 0] = M;
-                p.ws_ml[row * 2 + 1] = den;
+                coherent_store(&p.ws_ml[row * 2 + 0], M);
+                coherent_store(&p.ws_ml[row * 2 + 1], den);
             }
         }
     }
+    if (nparts_b == 1)
+        return;
+
+    // ---- the last partition of (b, h) to finish merges all of them --------
+    // With m_j in log2 units: w_j = l_j * 2^(m_j - max m),
+    // out = sum_j w_j o_j / sum_j w_j (exact rescaling, log-sum-exp).
+    // Publication without an L2 flush: the rows above were written with
+    // coherent stores; waiting for their acknowledgement before the
+    // workgroup barrier orders them before the counter increment, and the
+    // merging workgroup reads them back with coherent loads.
+    int *flag = reinterpret_cast<int *>(smem + lds_bytes<T, D, BS, G>() / 4) + 1;
+    int32_t *counter = p.counters + (int64_t)b * p.num_kv_heads + h;
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                nparts_b - 1;
+    __syncthreads();
+    if (!*flag)
+        return;
+    for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+        const int g = idx / D, d = idx % D;
+        const int64_t row0 = ((int64_t)b * p.num_q_heads + h * G + g) * p.num_partitions;
+        float M = -INFINITY;
+        for (int jj = 0; jj < nparts_b; ++jj)
+            M = fmaxf(M, coherent_load(&p.ws_ml[(row0 + jj) * 2]));
+        float acc = 0.0f, den = 0.0f;
+        for (int jj = 0; jj < nparts_b; ++jj) {
+            const float wgt = coherent_load(&p.ws_ml[(row0 + jj) * 2 + 1]) *
+                              __builtin_amdgcn_exp2f(coherent_load(&p.ws_ml[(row0 + jj) * 2]) - M);
+            den += wgt;
+            acc = fmaf(wgt, coherent_load(&p.ws_o[(row0 + jj) * D + d]), acc);
+        }
+        store_out(p.out, ((int64_t)b * p.num_q_heads + h * G + g) * D + d, acc / den, p.out_kind);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class T, int D, int BS, int G>
@@ -527,34 +583,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *context_lens,
     }
 }
 
-// Merge the partitions of each (sequence, query head): with m_j in log2
-// units, w_j = l_j * 2^(m_j - max m), out = sum w_j o_j / sum w_j.
-template <int D>
-__global__ __launch_bounds__(D) void reduce_kernel(void *out, int out_kind, const float *ws_o,
-                                                   const float *ws_ml,
-                                                   const int32_t *context_lens,
-                                                   int32_t num_q_heads, int32_t partition_size,
-                                                   int32_t num_partitions, int32_t len_cap)
-{
-    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    int L = context_lens[b];
-    L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
-    const int n = (L + partition_size - 1) / partition_size;
-    if (n <= 1)
-        return;  // written by the partition kernel
-    const int64_t row0 = ((int64_t)b * num_q_heads + hq) * num_partitions;
-    float M = -INFINITY;
-    for (int jj = 0; jj < n; ++jj)
-        M = fmaxf(M, ws_ml[(row0 + jj) * 2]);
-    float acc = 0.0f, den = 0.0f;
-    for (int jj = 0; jj < n; ++jj) {
-        const float wgt = ws_ml[(row0 + jj) * 2 + 1] * __builtin_amdgcn_exp2f(ws_ml[(row0 + jj) * 2] - M);
-        den += wgt;
-        acc = fmaf(wgt, ws_o[(row0 + jj) * D + d], acc);
-    }
-    store_out(out, ((int64_t)b * num_q_heads + hq) * D + d, acc / den, out_kind);
-}
-
 template <class T, int D, int BS, int G>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
 {
@@ -582,6 +610,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
     p.ws_ml = a.ws_ml;
     p.items = a.items;
     p.wl_header = a.wl_header;
+    p.counters = a.counters;
 
     const size_t lds = lds_bytes<T, D, BS, G>() + 16;
     hipError_t e;
@@ -601,13 +630,6 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
         hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), lds, stream,
                            p);
     }
-    e = hipGetLastError();
-    if (e != hipSuccess || a.num_partitions <= 1)
-        return e;
-    hipLaunchKernelGGL((reduce_kernel<D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs),
-                       dim3(D), 0, stream, a.out, (int)a.out_dtype, a.ws_o, a.ws_ml,
-                       a.context_lens, a.num_q_heads, a.partition_size, a.num_partitions,
-                       p.len_cap);
     return hipGetLastError();
 }
 

@@ -43,7 +43,14 @@ struct DecodeArgs {
     float *ws_ml;             // [B][Hq][num_partitions][2]    (max in log2 units, sum)
     int2 *items;              // work list {b, j}, [B * num_partitions]; null: dense grid
     int32_t *wl_header;       // [2]: dynamic-item counter, item count (work-list mode)
+    int32_t *counters;        // [B][Hkv] completion counters; zero before and after a call
 };
+
+// The workspace of a multi-partition decode starts with this many bytes of
+// completion counters (one int32 per (sequence, kv head)).  They must be
+// zero before the first call that uses the workspace; every call leaves
+// them zero.  A fixed size keeps them in place whatever the shapes.
+constexpr int64_t kCounterBytes = 1 << 20;
 
 // Above this many partitions per sequence the decode builds a work list on
 // the device instead of launching a dense (partition, head, sequence) grid
@@ -53,7 +60,7 @@ constexpr int kDenseMaxPartitions = 8;
 // Byte offsets of the decode workspace's two regions (256-aligned starts)
 // and its total size; zero when one partition covers every sequence.
 struct WorkspaceLayout {
-    size_t o_offset, ml_offset, header_offset, items_offset, total;
+    size_t counter_offset, o_offset, ml_offset, header_offset, items_offset, total;
     bool worklist;
 };
 WorkspaceLayout decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,

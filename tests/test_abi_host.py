@@ -113,12 +113,14 @@ def r256(x):
 def test_workspace_bytes():
     assert pka.decode_workspace_bytes(16, 32, 64, 512, 512) == 0  # one partition
     # 8 partitions: dense grid, partial rows + (max, sum) pairs
+    # (1 MiB of completion counters first)
     rows = 16 * 32 * 8
-    assert pka.decode_workspace_bytes(16, 32, 64, 1024, 128) == r256(rows * 64 * 4) + r256(rows * 8)
+    assert pka.decode_workspace_bytes(16, 32, 64, 1024, 128) == \
+        (1 << 20) + r256(rows * 64 * 4) + r256(rows * 8)
     # 16 partitions: a device-built work list follows (256-byte header, {b, j} items)
     rows = 16 * 32 * 16
     n = pka.decode_workspace_bytes(16, 32, 64, 1024, 64)
-    assert n == r256(rows * 64 * 4) + r256(rows * 8) + 256 + r256(16 * 16 * 8)
+    assert n == (1 << 20) + r256(rows * 64 * 4) + r256(rows * 8) + 256 + r256(16 * 16 * 8)
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -180,6 +180,77 @@ def test_skewed_work_list(dtype):
     assert np.all(got[0] == 0) and np.all(got[4] == 0)
 
 
+def test_workspace_reuse_across_shapes():
+    """One explicit workspace, zero-filled once, serves calls of different
+    shapes back to back (its completion counters stay at a fixed place and
+    every call leaves them zero)."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    cases = [case(20, "f16", [900, 33, 2000], 32, 8, 64, 16),
+             case(21, "bf16", [5000, 100], 16, 8, 128, 16),
+             case(22, "f16", [300] * 20, 8, 2, 64, 32)]
+    for rnd in range(2):
+        for i, wl in enumerate(cases):
+            d = W.device_inputs(wl, "cuda")
+            pka.kv_cache_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"],
+                               d["v_cache"])
+            out = pka.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"],
+                                             d["block_tables"], d["context_lens"],
+                                             float(wl.scale), wl.num_kv_heads, wl.block_size,
+                                             partition_size=64 if i != 1 else 256,
+                                             workspace=ws)
+            torch.cuda.synchronize()
+            check_close(out.double().cpu().numpy(), oracle_full(wl), wl.dtype,
+                        f"round {rnd} case {i}")
+    assert int(ws[: 1 << 20].count_nonzero()) == 0  # counters left at zero
+
+
+def test_graph_replay_matches_eager():
+    """Captured in a HIP graph, the multi-partition decode replays several
+    times (eager calls in between) and matches the eager result bit for bit."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+
+    wl = case(23, "bf16", [3000, 40, 1500, 777], 32, 8, 64, 16)
+    d = W.device_inputs(wl, "cuda")
+    pka.kv_cache_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), device="cuda")
+
+    def call(o):
+        pka.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                   d["context_lens"], float(wl.scale), wl.num_kv_heads,
+                                   wl.block_size, partition_size=128, out=o, workspace=ws,
+                                   max_context_len=wl.max_context_len)
+
+    eager = torch.empty_like(out)
+    call(eager)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    ref = eager.clone()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        call(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref)
+    check_close(ref.double().cpu().numpy(), oracle_full(wl), "bf16")
+
+
 def test_bad_partition_size_is_rejected():
     import paged_kv_attention_24_amd as pka
 
