@@ -45,16 +45,44 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="pools per step (default: 16 for workload 2, else enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a HIP graph")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="override the library's partition length (tokens)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one torch copy of this many MiB first (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(tag):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary profiles/<tag>.md, or None when the kernel source has changed
+    since the counters were taken (or no summary exists)."""
+    import hashlib
+
+    path = os.path.join(HERE, "profiles", f"{tag}.md")
+    src = os.path.join(HERE, "paged_kv_attention_24_amd", "csrc", "paged_decode.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+PROFILE_TAGS = {2: "paged_decode_llama3_1b_b16", 3: "paged_decode_mix_b64",
+                4: "paged_decode_qwen3_b128", 5: "paged_decode_skewed_b256"}
 
 
 def fill_pool(shape, dtype, seed, device):
@@ -136,6 +164,15 @@ def main():
         for r in range(R):
             decode(r)
 
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src_c = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        torch.cuda.synchronize()
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
@@ -196,7 +233,7 @@ def main():
                                           wl.scale, Hkv, bs, wl.dtype, threads=threads)
             n_done += 1
             el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or n_done >= 64:
+            if el >= args.cpu_seconds or n_done >= 512:
                 break
         cpu = {
             "value": round(kv_bytes * n_done / el / 1e9, 4),
@@ -237,12 +274,14 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (partition + merge kernels)",
+            "kernel": "partition_kernel (one launch per paged_attention_decode call)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(PROFILE_TAGS[cfg]),
+            "traffic_source": f"profiles/{PROFILE_TAGS[cfg]}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                              "copy-calibrated; null when the kernel changed since)",
             "us_per_launch": round(us_decode, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },

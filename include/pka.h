@@ -124,9 +124,13 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *
  * Long sequences are split into partitions of partition_size tokens that
  * are processed independently; each writes its running max, sum and
- * normalised partial output to the workspace, and a second kernel merges
- * them exactly (log-sum-exp).  The result does not depend on the partition
- * length beyond fp32 rounding.
+ * normalised partial output to the workspace, and the last partition of a
+ * (sequence, kv head) to finish merges them exactly (log-sum-exp) in the
+ * same launch.  The result does not depend on the partition length beyond
+ * fp32 rounding.  When the longest sequence spans more than 8 partitions,
+ * a one-workgroup planning kernel first lists the (sequence, partition)
+ * items on the device and a persistent grid processes them, so that short
+ * sequences in a skewed batch launch no empty workgroups.
  *
  *   out             device, [num_seqs][num_q_heads][head_dim], contiguous,
  *                   of out_dtype (PKA_F32, or the KV dtype: rounded to
@@ -135,13 +139,14 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                   of the KV dtype.
  *   k_cache,v_cache device pools (layout above), of kv_dtype.
  *   block_tables    device, int32 [num_seqs][max_blocks_per_seq].  Entries
- *                   at index >= ceil(L_b / block_size) are never read.  An
- *                   entry outside [0, num_blocks) is clamped into range (the
- *                   row's result is then meaningless, but no access leaves
- *                   the pools).
- *   context_lens    device, int32 [num_seqs].  Lengths are clamped to
- *                   [0, min(max_blocks_per_seq * block_size,
- *                   max_context_len)] on the device.
+ *                   at index >= ceil(L_b / block_size) may be read but are
+ *                   never used; any value there is harmless.  A used entry
+ *                   outside [0, num_blocks) is clamped into range (the row's
+ *                   result is then meaningless, but no access leaves the
+ *                   pools).
+ *   context_lens    device, int32 [num_seqs].  Lengths are clamped on the
+ *                   device to [0, min(max_blocks_per_seq * block_size,
+ *                   max_context_len rounded up to whole partitions)].
  *   scale           multiplier of the dot products (typically 1/sqrt(D)).
  *   max_context_len host hint: no sequence is longer.  <= 0 means
  *                   max_blocks_per_seq * block_size.  It sizes the launch
@@ -150,9 +155,15 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                   multiple of block_size.
  *   workspace       device scratch of workspace_bytes >=
  *                   pka_decode_workspace_bytes(...), 256-byte aligned; may
- *                   be NULL when that size is 0.  Its contents are
- *                   overwritten; calls that share one workspace on
- *                   different streams race.
+ *                   be NULL when that size is 0.  Its first 1 MiB holds
+ *                   completion counters (one int32 per (sequence, kv head);
+ *                   num_seqs * num_kv_heads <= 262144) that must be zero
+ *                   before the first call using this workspace: zero-fill a
+ *                   new workspace once.  Every call leaves the counters
+ *                   zero again, so a workspace can be reused by later calls
+ *                   of any shape on the same stream (or in a captured graph);
+ *                   calls that share one workspace on different streams
+ *                   race.  The rest is overwritten by each call.
  * Supported: kv_dtype in {F32, F16, BF16}; head_dim in {64, 128};
  * block_size in {16, 32}; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  */
