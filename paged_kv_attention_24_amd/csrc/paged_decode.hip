@@ -41,6 +41,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pka_internal.h"
 
 namespace pka {
@@ -151,6 +153,51 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// group_sum over N lanes applied to CNT independent values, one butterfly
+// stage at a time for all of them: consecutive DPP instructions never read
+// a register written by the instruction just before (no hazard stalls).
+template <int N, int CNT>
+__device__ __forceinline__ void group_sum_all(float (&x)[CNT])
+{
+    if constexpr (N >= 2) {
+#pragma unroll
+        for (int c = 0; c < CNT; ++c) x[c] += dpp<0xB1>(x[c]);
+    }
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int c = 0; c < CNT; ++c) x[c] += dpp<0x4E>(x[c]);
+    }
+    if constexpr (N >= 8) {
+#pragma unroll
+        for (int c = 0; c < CNT; ++c) x[c] += dpp<0x141>(x[c]);
+    }
+    if constexpr (N >= 16) {
+#pragma unroll
+        for (int c = 0; c < CNT; ++c) x[c] += dpp<0x140>(x[c]);
+    }
+    if constexpr (N >= 32) {
+#pragma unroll
+        for (int c = 0; c < CNT; ++c) x[c] += swz_xor16(x[c]);
+    }
+}
+
+// Sum over the lanes that share (lane % LPR), i.e. over a wave's token
+// groups (lane ^ LPR, lane ^ 2*LPR, ... up to lane ^ 32).
+__device__ __forceinline__ float xor32(float x)
+{
+    const int lane = __lane_id();
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2,
+                                                                  __builtin_bit_cast(int, x)));
+}
+template <int LPR>
+__device__ __forceinline__ float token_group_sum(float x)
+{
+    if constexpr (LPR <= 8) x += dpp<0x128>(x);  // row_ror:8 = lane ^ 8 within 16
+    if constexpr (LPR <= 16) x += swz_xor16(x);
+    x += xor32(x);
+    return x;
+}
+
 // Max over the whole wave, returned as a wave-uniform value.
 __device__ __forceinline__ float wave_max(float x)
 {
@@ -232,7 +279,7 @@ template <class T, int D, int BS, int G>
 __host__ __device__ constexpr size_t lds_bytes()
 {
     using S = Shape<T, D, BS, G>;
-    return (size_t)S::NW * S::TPL * G * (D + 1) * 4 + (size_t)S::NW * G * 4;
+    return (size_t)S::NW * G * (D + 2) * 4;
 }
 
 template <class T, int D, int BS, int G>
@@ -296,14 +343,24 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
     const int last_blk = t_end > 0 ? (t_end - 1) / BS - pb0 : 0;   // partition-relative
 
     // query rows of the group: 16 bytes per lane per head
+    // Softmax runs on raw dot products scaled by c = |scale| * log2(e) >= 0
+    // inside the exponent; a negative scale flips the sign of q instead (exact).
+    const float c = fabsf(p.scale_log2);
+    const uint32_t qflip = p.scale_log2 < 0.0f ? (S::ELT == 4 ? 0x80000000u : 0x80008000u) : 0u;
     uint4 qr[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
         qr[g] = *reinterpret_cast<const uint4 *>(
             p.q + (((int64_t)b * p.num_q_heads + h * G + g) * D + cl * VEC) * S::ELT);
+        qr[g].x ^= qflip;
+        qr[g].y ^= qflip;
+        qr[g].z ^= qflip;
+        qr[g].w ^= qflip;
+    }
 
     const int64_t head_off = (int64_t)h * S::TILE;
     const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
+    const uint32_t lane_off = lane * 16;
 
     // K and V of chunk k of this wave: NL wave loads each, issued without
     // conditions (so the compiler's wait counts stay exact).  Loads past the
@@ -317,10 +374,10 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             int rb = t0 / BS - pb0;
             rb = rb < last_blk ? rb : last_blk;
             const int blk = __builtin_amdgcn_readlane(ids, rb);
-            const int64_t off = blk * block_stride + head_off +
-                                (int64_t)(t0 % BS) * (D * S::ELT) + lane * 16;
-            kr[i] = *reinterpret_cast<const uint4 *>(p.k_cache + off);
-            vr[i] = *reinterpret_cast<const uint4 *>(p.v_cache + off);
+            // wave-uniform row address (scalar registers) + this lane's 16 B
+            const int64_t row = (int64_t)blk * block_stride + head_off + (t0 % BS) * (D * S::ELT);
+            kr[i] = *reinterpret_cast<const uint4 *>(p.k_cache + row + lane_off);
+            vr[i] = *reinterpret_cast<const uint4 *>(p.v_cache + row + lane_off);
         }
     };
 
@@ -335,31 +392,39 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             o[g][e] = 0.0f;
     }
 
-    auto process = [&](int k, const uint4 *kr, uint4 *vr) {
+    // One chunk: NL wave loads of K and V, each lane one token of each.
+    // FULL chunks lie entirely before t_end; the partial one masks with
+    // selects (never 0 * value, so stale or NaN slots cannot leak).
+    auto process = [&](auto full_tag, int k, const uint4 *kr, uint4 *vr) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int tc = t_begin + (w + k * NW) * CT;
-        const bool full = tc + CT <= t_end;
-        float s[NL][G];
+        float s[NL * G];
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                s[i * G + g] = dot16(T{}, qr[g], kr[i], 0.0f);
+        group_sum_all<LPR>(s);
+        bool valid[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const bool valid = full || tc + i * TPL + tg < t_end;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                s[i][g] = group_sum<LPR>(dot16(T{}, qr[g], kr[i], 0.0f)) * p.scale_log2;
-                if (!full)
-                    s[i][g] = valid ? s[i][g] : -INFINITY;
+            valid[i] = FULL || tc + i * TPL + tg < t_end;
+            if constexpr (!FULL) {
+                vr[i].x = valid[i] ? vr[i].x : 0u;
+                vr[i].y = valid[i] ? vr[i].y : 0u;
+                vr[i].z = valid[i] ? vr[i].z : 0u;
+                vr[i].w = valid[i] ? vr[i].w : 0u;
             }
-            if (!full && !valid)
-                vr[i] = make_uint4(0, 0, 0, 0);  // select: NaN bits never reach o
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float cm = s[0][g];
+            float cm = valid[0] ? s[g] : -INFINITY;
 #pragma unroll
             for (int i = 1; i < NL; ++i)
-                cm = fmaxf(cm, s[i][g]);
+                cm = fmaxf(cm, valid[i] ? s[i * G + g] : -INFINITY);
             const float m_new = fmaxf(m[g], cm);
-            const float mr = m_new == -INFINITY ? 0.0f : m_new;
-            const float corr = __builtin_amdgcn_exp2f(m[g] - mr);
+            const float nmc = -(m_new == -INFINITY ? 0.0f : m_new) * c;
+            const float corr = m[g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(m[g], c, nmc));
             l[g] *= corr;
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
@@ -367,11 +432,19 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             m[g] = m_new;
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
-                const float pw = __builtin_amdgcn_exp2f(s[i][g] - mr);
+                float pw = __builtin_amdgcn_exp2f(fmaf(s[i * G + g], c, nmc));
+                if constexpr (!FULL)
+                    pw = valid[i] ? pw : 0.0f;
                 l[g] += pw;
                 axpy16(T{}, pw, vr[i], o[g]);
             }
         }
+    };
+    auto process_any = [&](int k, const uint4 *kr, uint4 *vr) {
+        if (t_begin + (w + k * NW) * CT + CT <= t_end)
+            process(std::true_type{}, k, kr, vr);
+        else
+            process(std::false_type{}, k, kr, vr);
     };
 
     // Software pipeline: the loads of chunk k+1 are in flight while chunk k
@@ -382,51 +455,52 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
         int k = 0;
         for (; k + 2 < nk; k += 2) {
             load_chunk(k + 1, kb, vb);
-            process(k, ka, va);
+            process_any(k, ka, va);
             load_chunk(k + 2, ka, va);
-            process(k + 1, kb, vb);
+            process_any(k + 1, kb, vb);
         }
         if (k + 1 < nk) {
             load_chunk(k + 1, kb, vb);
-            process(k, ka, va);
-            process(k + 1, kb, vb);
+            process_any(k, ka, va);
+            process_any(k + 1, kb, vb);
         } else {
-            process(k, ka, va);
+            process_any(k, ka, va);
         }
     }
 
-    // Rescale every lane to the wave's maximum.
+    // Rescale every lane to the wave's maximum, then sum the token groups
+    // in registers (lanes that hold the same dims of different tokens).
     float mw[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         mw[g] = wave_max(m[g]);
-        const float f = __builtin_amdgcn_exp2f(m[g] - (mw[g] == -INFINITY ? 0.0f : mw[g]));
-        l[g] *= f;
+        const float f = m[g] == -INFINITY ? 0.0f
+                        : __builtin_amdgcn_exp2f((m[g] - mw[g]) * c);
+        l[g] = token_group_sum<LPR>(l[g] * f);
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            o[g][e] *= f;
+            o[g][e] = token_group_sum<LPR>(o[g][e] * f);
     }
 
-    // ---- merge token groups and waves (log-sum-exp with the wave maxima) --
-    float *red = smem;                                  // [NW][TPL][G][D]
-    float *lred = red + (size_t)NW * TPL * G * D;       // [NW][TPL][G]
-    float *mred = lred + (size_t)NW * TPL * G;          // [NW][G]
+    // ---- merge the waves in LDS (log-sum-exp with the wave maxima) ------
+    float *red = smem;                        // [NW][G][D]
+    float *lred = red + (size_t)NW * G * D;   // [NW][G]
+    float *mred = lred + (size_t)NW * G;      // [NW][G], raw dot units
+    if (tg == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float *dst = red + ((size_t)(w * TPL + tg) * G + g) * D + cl * VEC;
+        for (int g = 0; g < G; ++g) {
+            float *dst = red + ((size_t)w * G + g) * D + cl * VEC;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            dst[e] = o[g][e];
-    }
-    if (cl == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-            lred[(w * TPL + tg) * G + g] = l[g];
+            for (int e = 0; e < VEC; ++e)
+                dst[e] = o[g][e];
+        }
     }
     if (lane == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+            lred[w * G + g] = l[g];
             mred[w * G + g] = mw[g];
+        }
     }
     __syncthreads();
 
@@ -441,16 +515,11 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
             const float mv = mred[ww * G + g];
-            const float sc = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            float a = 0.0f, ls = 0.0f;
-#pragma unroll
-            for (int t = 0; t < TPL; ++t) {
-                a += red[((size_t)(ww * TPL + t) * G + g) * D + d];
-                ls += lred[(ww * TPL + t) * G + g];
-            }
-            acc = fmaf(a, sc, acc);
-            den = fmaf(ls, sc, den);
+            const float sc = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mv - M) * c);
+            acc = fmaf(red[((size_t)ww * G + g) * D + d], sc, acc);
+            den = fmaf(lred[ww * G + g], sc, den);
         }
+        M = M == -INFINITY ? M : M * c;  // log2 units for the partition merge
         const float res = den > 0.0f ? acc / den : 0.0f;
         const int hq = h * G + g;
         if (nparts_b == 1) {
