@@ -80,6 +80,10 @@ def _declare(h):
         P, P, P, P, ctypes.c_int, P, i32, P, i32, i32, i32, i32, i32, i32, f64, i32,
         P, i32, i32]
     h.oracle_paged_attention_decode.restype = ctypes.c_int
+    h.oracle_paged_attention_decode_append.argtypes = [
+        P, P, P, P, P, P, i64, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, i32, i32, f64,
+        P, i32, i32]
+    h.oracle_paged_attention_decode_append.restype = ctypes.c_int
     h.oracle_kv_cache_write.argtypes = [P, P, i64, i64, P, i32, P, P, i32, i32, i32, i32, i32]
     h.oracle_kv_cache_write.restype = ctypes.c_int
     return h
@@ -145,6 +149,41 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), DTYPE_CODE[dtype], _ptr(bt),
         bt.shape[1], _ptr(cl), B, Hq, Hkv, D, NB, bs, float(scale), int(partition_size),
         rp, nr, int(threads))
+    if rc != 0:
+        raise OracleError(f"oracle decode failed: {STATUS.get(rc, rc)}")
+    return out
+
+
+def paged_attention_decode_append(q, k_cache, v_cache, k_new, v_new, block_tables,
+                                  context_lens, scale, num_kv_heads, block_size, dtype, *,
+                                  rows=None, threads: int = 0, handle=None) -> np.ndarray:
+    """fp64 decode in which each sequence's last position L_b - 1 takes its
+    key/value from k_new[b], v_new[b] ([B, Hkv, D], any token stride) rather
+    than from the pool.  Same array conventions as paged_attention_decode."""
+    h = handle or lib()
+    for a, w in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_stored(a, dtype, w)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    item = k_new.itemsize
+    for a in (k_new, v_new):
+        want = np.float32 if dtype == "f32" else np.uint16
+        if a.dtype != want or a.shape != (B, Hkv, D) or a.strides[2] != item or \
+                a.strides[1] != D * item:
+            raise ValueError("k_new/v_new must be [B, Hkv, D] with contiguous heads")
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        out = np.empty((r.shape[0], D), dtype=np.float64)
+        rp, nr = _ptr(r), r.shape[0]
+    else:
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    rc = h.oracle_paged_attention_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        k_new.strides[0] // item, v_new.strides[0] // item, DTYPE_CODE[dtype], _ptr(bt),
+        bt.shape[1], _ptr(cl), B, Hq, Hkv, D, NB, bs, float(scale), rp, nr, int(threads))
     if rc != 0:
         raise OracleError(f"oracle decode failed: {STATUS.get(rc, rc)}")
     return out

@@ -102,6 +102,10 @@ void oracle_decode_array(const void *src, int dtype, int64_t n, double *dst)
 
 typedef struct {
     const void *q, *k_cache, *v_cache;
+    /* optional appended token per sequence (NULL: none): rows of
+     * [num_seqs][num_kv_heads][head_dim], token strides in elements */
+    const void *k_new, *v_new;
+    int64_t k_new_stride, v_new_stride;
     int dtype;
     const int32_t *block_tables;
     int32_t max_blocks_per_seq;
@@ -137,18 +141,30 @@ static int check_row(const decode_args *a, int b)
     return ORACLE_OK;
 }
 
+/* Element d of the key (or value) of logical token t of sequence b, kv
+ * head h: from the pool through the block table, except that with an
+ * appended token the last position L_b - 1 comes from k_new (v_new). */
+static double kv_elem(const decode_args *a, int is_value, int b, int h, int64_t t, int d)
+{
+    const void *app = is_value ? a->v_new : a->k_new;
+    if (app && t == (int64_t)a->context_lens[b] - 1) {
+        int64_t stride = is_value ? a->v_new_stride : a->k_new_stride;
+        return load_elem(app, a->dtype, (int64_t)b * stride + (int64_t)h * a->head_dim + d);
+    }
+    int64_t blk = block_of(a, b, t);
+    int off = (int)(t % a->block_size);
+    return load_elem(is_value ? a->v_cache : a->k_cache, a->dtype, pool_index(a, blk, h, off, d));
+}
+
 /* scale * (q . K_t) for the tokens [t0, t1) of sequence b, kv head h. */
 static void logits(const decode_args *a, int b, int hq, int h, int64_t t0, int64_t t1,
                    double *s)
 {
     int64_t qbase = ((int64_t)b * a->num_q_heads + hq) * a->head_dim;
     for (int64_t t = t0; t < t1; ++t) {
-        int64_t blk = block_of(a, b, t);
-        int off = (int)(t % a->block_size);
         double dot = 0.0;
         for (int d = 0; d < a->head_dim; ++d)
-            dot += load_elem(a->q, a->dtype, qbase + d) *
-                   load_elem(a->k_cache, a->dtype, pool_index(a, blk, h, off, d));
+            dot += load_elem(a->q, a->dtype, qbase + d) * kv_elem(a, 0, b, h, t, d);
         s[t - t0] = a->scale * dot;
     }
 }
@@ -170,12 +186,8 @@ static void softmax_v(const decode_args *a, int b, int h, int64_t t0, int64_t t1
     }
     for (int d = 0; d < a->head_dim; ++d) {
         double acc = 0.0;
-        for (int64_t i = 0; i < n; ++i) {
-            int64_t t = t0 + i;
-            int64_t blk = block_of(a, b, t);
-            int off = (int)(t % a->block_size);
-            acc += s[i] * load_elem(a->v_cache, a->dtype, pool_index(a, blk, h, off, d));
-        }
+        for (int64_t i = 0; i < n; ++i)
+            acc += s[i] * kv_elem(a, 1, b, h, t0 + i, d);
         o[d] = acc / l;
     }
     *m_out = m;
@@ -249,14 +261,14 @@ static int decode_row(const decode_args *a, int b, int hq, int32_t partition_siz
  * from partitions (a self-check of the split identity).  num_threads <= 0
  * leaves the OpenMP default.  Returns ORACLE_OK or the first error seen.
  */
-int oracle_paged_attention_decode(double *out, const void *q, const void *k_cache,
-                                  const void *v_cache, int dtype,
-                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                  const int32_t *context_lens, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t num_blocks, int32_t block_size, double scale,
-                                  int32_t partition_size, const int32_t *rows, int32_t n_rows,
-                                  int32_t num_threads)
+static int decode_all(double *out, const void *q, const void *k_cache, const void *v_cache,
+                      const void *k_new, const void *v_new, int64_t k_new_stride,
+                      int64_t v_new_stride, int dtype, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t num_blocks, int32_t block_size, double scale,
+                      int32_t partition_size, const int32_t *rows, int32_t n_rows,
+                      int32_t num_threads)
 {
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
         return ORACLE_BAD_ARGUMENT;
@@ -264,9 +276,9 @@ int oracle_paged_attention_decode(double *out, const void *q, const void *k_cach
         num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
         return ORACLE_BAD_ARGUMENT;
-    decode_args a = {q, k_cache, v_cache, dtype, block_tables, max_blocks_per_seq,
-                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                     num_blocks, block_size, scale};
+    decode_args a = {q, k_cache, v_cache, k_new, v_new, k_new_stride, v_new_stride,
+                     dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, scale};
     int64_t n = rows ? n_rows : (int64_t)num_seqs * num_q_heads;
     if (rows) {
         for (int64_t r = 0; r < n; ++r)
@@ -286,6 +298,48 @@ int oracle_paged_attention_decode(double *out, const void *q, const void *k_cach
         }
     }
     return status;
+}
+
+int oracle_paged_attention_decode(double *out, const void *q, const void *k_cache,
+                                  const void *v_cache, int dtype,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t num_blocks, int32_t block_size, double scale,
+                                  int32_t partition_size, const int32_t *rows, int32_t n_rows,
+                                  int32_t num_threads)
+{
+    return decode_all(out, q, k_cache, v_cache, NULL, NULL, 0, 0, dtype, block_tables,
+                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                      head_dim, num_blocks, block_size, scale, partition_size, rows, n_rows,
+                      num_threads);
+}
+
+/*
+ * Decode with one appended token per sequence: identical to the above
+ * except that, for every sequence b with L_b >= 1, the key and value of its
+ * last position L_b - 1 are k_new[b] and v_new[b] (rows [num_kv_heads]
+ * [head_dim], token strides in elements) instead of the pool's contents.
+ * When the new token has been stored at the slot of position L_b - 1, this
+ * is exactly the plain decode of the updated pool.
+ */
+int oracle_paged_attention_decode_append(double *out, const void *q, const void *k_cache,
+                                         const void *v_cache, const void *k_new,
+                                         const void *v_new, int64_t k_new_stride,
+                                         int64_t v_new_stride, int dtype,
+                                         const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t *context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t num_blocks,
+                                         int32_t block_size, double scale,
+                                         const int32_t *rows, int32_t n_rows, int32_t num_threads)
+{
+    if (!k_new || !v_new)
+        return ORACLE_BAD_ARGUMENT;
+    return decode_all(out, q, k_cache, v_cache, k_new, v_new, k_new_stride, v_new_stride,
+                      dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, scale, 0,
+                      rows, n_rows, num_threads);
 }
 
 /*

@@ -318,7 +318,27 @@ def pin_write(h):
         assert k2.tobytes() == k1.tobytes() and v2.tobytes() == v1.tobytes()
 
 
+def pin_append_equals_write_then_decode(h):
+    """Decoding with the appended token equals writing it to the slot of
+    position L-1 and decoding the updated pool, bit for bit; with a
+    different appended token the result moves (the new row is really used)."""
+    wl = small_case(19, dtype="bf16", lens=(5, 37, 16, 1, 33, 64), Hq=8, Hkv=2, bs=16)
+    fused = oracle.paged_attention_decode_append(
+        wl.q, wl.k_cache, wl.v_cache, wl.new_k, wl.new_v, wl.block_tables, wl.context_lens,
+        wl.scale, wl.num_kv_heads, wl.block_size, wl.dtype, handle=h)
+    two_step = run(h, wl)  # write (slot of position L-1), then decode
+    assert np.array_equal(fused, two_step)
+    # the pool still holds NaN at those slots, so a gather that ignored the
+    # appended row would have produced NaN
+    assert np.all(np.isfinite(fused))
+    other = oracle.paged_attention_decode_append(
+        wl.q, wl.k_cache, wl.v_cache, wl.new_v.copy(), wl.new_k.copy(), wl.block_tables,
+        wl.context_lens, wl.scale, wl.num_kv_heads, wl.block_size, wl.dtype, handle=h)
+    assert not np.array_equal(other, fused)
+
+
 PINS = {
+    "append_equals_write_then_decode": pin_append_equals_write_then_decode,
     "decoders_exhaustive": pin_decoders_exhaustive,
     "sdpa_contiguous": pin_sdpa_contiguous,
     "single_token": pin_single_token,

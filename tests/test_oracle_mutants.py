@@ -22,15 +22,15 @@ MUTANTS = {
     # block-table column taken from the offset
     "table_index": ("[(int64_t)b * a->max_blocks_per_seq + t / a->block_size]",
                     "[(int64_t)b * a->max_blocks_per_seq + t % a->max_blocks_per_seq]"),
-    # wrong in-block offset when reading K
-    "k_offset": ("        int off = (int)(t % a->block_size);\n        double dot",
-                 "        int off = (int)((t + 1) % a->block_size);\n        double dot"),
+    # wrong in-block offset in the gather
+    "kv_offset": ("    int off = (int)(t % a->block_size);\n    return load_elem(",
+                  "    int off = (int)((t + 1) % a->block_size);\n    return load_elem("),
     # head and offset swapped in the pool index
     "pool_index_order": ("((block * a->num_kv_heads + h) * a->block_size + off)",
                          "((block * a->block_size + off) * a->num_kv_heads + h)"),
     "scale_dropped": ("s[t - t0] = a->scale * dot;", "s[t - t0] = dot;"),
     "max_sign": ("s[i] = exp(s[i] - m);", "s[i] = exp(m - s[i]);"),
-    "values_from_k": ("acc += s[i] * load_elem(a->v_cache", "acc += s[i] * load_elem(a->k_cache"),
+    "values_from_k": ("is_value ? a->v_cache : a->k_cache", "is_value ? a->k_cache : a->k_cache"),
     "no_normalisation": ("o[d] = acc / l;", "o[d] = acc;"),
     "last_dim_dropped": ("for (int d = 0; d < a->head_dim; ++d)\n            dot +=",
                          "for (int d = 0; d < a->head_dim - 1; ++d)\n            dot +="),
@@ -44,6 +44,8 @@ MUTANTS = {
                      "int64_t blk = s / block_size, off = (s + 1) % block_size;"),
     "write_v_from_k": ("(const char *)v + ((int64_t)i * v_token_stride",
                        "(const char *)k + ((int64_t)i * k_token_stride"),
+    "append_position": ("if (app && t == (int64_t)a->context_lens[b] - 1)",
+                        "if (app && t == (int64_t)a->context_lens[b] - 2)"),
     "write_token_stride": ("(const char *)k + ((int64_t)i * k_token_stride + (int64_t)h * head_dim)",
                            "(const char *)k + ((int64_t)i * num_kv_heads * head_dim + (int64_t)h * head_dim)"),
 }
