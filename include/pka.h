@@ -177,6 +177,47 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
                                       int32_t partition_size, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/*
+ * pka_paged_attention_decode_append -- one decode step of a batch in a
+ * single launch: for every sequence b, store its new token's K/V rows
+ * (k_new[b], v_new[b]) at slot_mapping[b] and attend over its L_b tokens,
+ * the last of which (position L_b - 1) is that new token:
+ *
+ *   out[b][hq] = sum_{t < L_b} softmax_t(scale * q[b][hq] . K_t) V_t,
+ *   K_t, V_t from the pools for t < L_b - 1 and from k_new[b], v_new[b]
+ *   for t = L_b - 1.
+ *
+ * This is the batched write of the PhotonInfer README ("Technical details >
+ * Paged attention": one kernel for the K/V writes of many sequences) fused
+ * with the batched decode ("Key features > GPU-optimised kernels").  When
+ * slot_mapping[b] is the slot of position L_b - 1 of sequence b (the usual
+ * decode step), the pools and the output are bit-identical to
+ * pka_kv_cache_write followed by pka_paged_attention_decode.
+ *
+ *   q, out, pools, block_tables, context_lens, scale, max_context_len,
+ *   partition_size, workspace: as for pka_paged_attention_decode (the pools
+ *   are written, so they are not const here).
+ *   k_new, v_new    device, [num_seqs][num_kv_heads][head_dim] of kv_dtype,
+ *                   token strides k_new_token_stride / v_new_token_stride
+ *                   (elements, >= num_kv_heads * head_dim, rows 16-byte
+ *                   aligned), heads head_dim apart.
+ *   slot_mapping    device, int64 [num_seqs].  A negative slot, or one at or
+ *                   beyond num_blocks * block_size, stores nothing (the new
+ *                   token still takes part in the attention).  Sequences
+ *                   with L_b <= 0 store nothing and yield a zero row.  A slot
+ *                   that this call reads for another position of any
+ *                   sequence races with the store (unspecified result).
+ * Supported: as for pka_paged_attention_decode.
+ */
+pka_status pka_paged_attention_decode_append(
+    void *out, pka_dtype out_dtype, const void *q, const void *k_new, const void *v_new,
+    int64_t k_new_token_stride, int64_t v_new_token_stride, const int64_t *slot_mapping,
+    void *k_cache, void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_blocks, int32_t block_size, float scale, pka_dtype kv_dtype,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream);
+
 /* Static English name of a status code. */
 const char *pka_status_string(pka_status status);
 

@@ -24,7 +24,8 @@ import os
 from typing import Optional
 
 __all__ = [
-    "PkaError", "kv_cache_write", "paged_attention_decode", "decode_partition_size",
+    "PkaError", "kv_cache_write", "paged_attention_decode", "paged_attention_decode_append",
+    "decode_partition_size",
     "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
 ]
 
@@ -72,6 +73,10 @@ def load_library():
         P, ctypes.c_int, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
         ctypes.c_int, i32, i32, P, ctypes.c_size_t, P]
     lib.pka_paged_attention_decode.restype = ctypes.c_int
+    lib.pka_paged_attention_decode_append.argtypes = [
+        P, ctypes.c_int, P, P, P, i64, i64, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
+        ctypes.c_float, ctypes.c_int, i32, i32, P, ctypes.c_size_t, P]
+    lib.pka_paged_attention_decode_append.restype = ctypes.c_int
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_last_error.argtypes = []
@@ -160,20 +165,8 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
                                                          max_context_len, partition_size))
 
 
-def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                           num_kv_heads: int, block_size: int, *, out=None, out_dtype=None,
-                           partition_size: int = 0, max_context_len: int = 0,
-                           workspace=None):
-    """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache.
-
-    q [B, Hq, D] (the KV dtype); pools [NB, Hkv, bs, D]; block_tables int32
-    [B, MB]; context_lens int32 [B] (device).  Returns out [B, Hq, D], fp32
-    unless ``out_dtype`` (or ``out``) says the KV dtype.  ``max_context_len``
-    is an optional host hint (no device sync); ``partition_size`` 0 lets the
-    library choose.  ``workspace`` (uint8 device tensor, zero-filled before
-    its first use; each call leaves it reusable) defaults to a cached one per
-    device.
-    """
+def _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, block_size,
+                  out, out_dtype, partition_size, max_context_len, workspace):
     import torch
 
     _require_gpu(q, k_cache, v_cache, block_tables, context_lens)
@@ -204,28 +197,90 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     else:
         if tuple(out.shape) != (B, Hq, D) or not out.is_contiguous() or out.device != q.device:
             raise ValueError("out must be a contiguous [B, Hq, D] tensor on q's device")
-    if B == 0:
-        return out
-    lib = load_library()
     hint = max_context_len if max_context_len > 0 else MB * bs
     hint = min(hint, MB * bs)
-    P = partition_size if partition_size > 0 else decode_partition_size(B, Hkv, bs, hint)
-    need = decode_workspace_bytes(B, Hq, D, hint, P)
-    if need > 0:
-        if workspace is None:
-            workspace = _cached_workspace(q.device, need)
-        elif workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
-                             f"bytes, {need} needed")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    else:
-        ws_ptr, ws_bytes = None, 0
+    P = 0
+    ws_ptr, ws_bytes = None, 0
+    if B > 0:
+        P = partition_size if partition_size > 0 else decode_partition_size(B, Hkv, bs, hint)
+        need = decode_workspace_bytes(B, Hq, D, hint, P)
+        if need > 0:
+            if workspace is None:
+                workspace = _cached_workspace(q.device, need)
+            elif workspace.numel() * workspace.element_size() < need:
+                raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                                 f"bytes, {need} needed")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return dict(q=q, block_tables=block_tables, context_lens=context_lens, out=out, B=B, Hq=Hq,
+                Hkv=Hkv, D=D, NB=NB, bs=bs, MB=MB, hint=hint, P=P, ws_ptr=ws_ptr,
+                ws_bytes=ws_bytes)
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           num_kv_heads: int, block_size: int, *, out=None, out_dtype=None,
+                           partition_size: int = 0, max_context_len: int = 0,
+                           workspace=None):
+    """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache.
+
+    q [B, Hq, D] (the KV dtype); pools [NB, Hkv, bs, D]; block_tables int32
+    [B, MB]; context_lens int32 [B] (device).  Returns out [B, Hq, D], fp32
+    unless ``out_dtype`` (or ``out``) says the KV dtype.  ``max_context_len``
+    is an optional host hint (no device sync); ``partition_size`` 0 lets the
+    library choose.  ``workspace`` (uint8 device tensor, zero-filled before
+    its first use; each call leaves it reusable) defaults to a cached one per
+    device.
+    """
+    a = _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                      block_size, out, out_dtype, partition_size, max_context_len, workspace)
+    if a["B"] == 0:
+        return a["out"]
+    lib = load_library()
     _check(lib.pka_paged_attention_decode(
-        out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
-        v_cache.data_ptr(), block_tables.data_ptr(), MB, context_lens.data_ptr(), B, Hq, Hkv, D,
-        NB, bs, float(scale), _dtype_code(k_cache.dtype), hint, P, ws_ptr, ws_bytes,
+        a["out"].data_ptr(), _dtype_code(a["out"].dtype), a["q"].data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), a["block_tables"].data_ptr(), a["MB"], a["context_lens"].data_ptr(),
+        a["B"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], float(scale),
+        _dtype_code(k_cache.dtype), a["hint"], a["P"], a["ws_ptr"], a["ws_bytes"],
         _stream_ptr(q.device)))
-    return out
+    return a["out"]
+
+
+def paged_attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                                  context_lens, scale: float, num_kv_heads: int,
+                                  block_size: int, *, out=None, out_dtype=None,
+                                  partition_size: int = 0, max_context_len: int = 0,
+                                  workspace=None):
+    """One fused decode step: store each sequence's new token (k_new[b],
+    v_new[b], [B, Hkv, D]) at slot_mapping[b] (int64 [B]) and attend over
+    its L_b tokens, the last of which is that new token.  Equal, bit for bit,
+    to kv_cache_write followed by paged_attention_decode when slot_mapping[b]
+    is the slot of position L_b - 1.  Mutates the pools; returns out."""
+    import torch
+
+    a = _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                      block_size, out, out_dtype, partition_size, max_context_len, workspace)
+    B, Hkv, D = a["B"], a["Hkv"], a["D"]
+    _require_gpu(k_new, v_new, slot_mapping)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 3 or tuple(t.shape) != (B, Hkv, D):
+            raise ValueError(f"{name} must be [{B}, {Hkv}, {D}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} must have contiguous heads (strides [*, {D}, 1])")
+        if t.dtype != k_cache.dtype:
+            raise TypeError(f"{name} must have the pools' dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [B]")
+    slot_mapping = slot_mapping.contiguous()
+    if B == 0:
+        return a["out"]
+    lib = load_library()
+    _check(lib.pka_paged_attention_decode_append(
+        a["out"].data_ptr(), _dtype_code(a["out"].dtype), a["q"].data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), k_new.stride(0), v_new.stride(0), slot_mapping.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), a["block_tables"].data_ptr(), a["MB"],
+        a["context_lens"].data_ptr(), B, a["Hq"], Hkv, D, a["NB"], a["bs"], float(scale),
+        _dtype_code(k_cache.dtype), a["hint"], a["P"], a["ws_ptr"], a["ws_bytes"],
+        _stream_ptr(q.device)))
+    return a["out"]
 
 
 _WORKSPACES = {}
@@ -271,3 +326,9 @@ class PagedKVCache:
     def decode(self, q, block_tables, context_lens, scale: float, **kw):
         return paged_attention_decode(q, self.k_cache, self.v_cache, block_tables, context_lens,
                                       scale, self.num_kv_heads, self.block_size, **kw)
+
+    def decode_append(self, q, k_new, v_new, slot_mapping, block_tables, context_lens,
+                      scale: float, **kw):
+        return paged_attention_decode_append(q, k_new, v_new, slot_mapping, self.k_cache,
+                                             self.v_cache, block_tables, context_lens, scale,
+                                             self.num_kv_heads, self.block_size, **kw)

@@ -154,15 +154,18 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
         .total;
 }
 
-pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void *q,
-                                      const void *k_cache, const void *v_cache,
-                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                      const int32_t *context_lens, int32_t num_seqs,
-                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t num_blocks, int32_t block_size, float scale,
-                                      pka_dtype kv_dtype, int32_t max_context_len,
-                                      int32_t partition_size, void *workspace,
-                                      size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                              float scale, pka_dtype kv_dtype, int32_t max_context_len,
+                              int32_t partition_size, void *workspace, size_t workspace_bytes,
+                              void *stream, const void *k_new, const void *v_new,
+                              int64_t k_new_token_stride, int64_t v_new_token_stride,
+                              const int64_t *slot_mapping)
 {
     if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype))
         return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype");
@@ -198,6 +201,20 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
         return fail(PKA_ERR_INVALID_ARGUMENT, "null pointer argument");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKA_ERR_INVALID_ARGUMENT, "out, q and the caches must be 16-byte aligned");
+    if (k_new || v_new || slot_mapping) {
+        if (!k_new || !v_new || !slot_mapping)
+            return fail(PKA_ERR_INVALID_ARGUMENT, "null k_new, v_new or slot_mapping");
+        const int elt = pka::dtype_bytes(to_internal(kv_dtype));
+        const int64_t row = (int64_t)num_kv_heads * head_dim;
+        if (k_new_token_stride < row || v_new_token_stride < row)
+            return fail(PKA_ERR_INVALID_ARGUMENT,
+                        "new-token strides (%lld, %lld) must be >= num_kv_heads * head_dim = %lld",
+                        (long long)k_new_token_stride, (long long)v_new_token_stride,
+                        (long long)row);
+        if (!aligned16(k_new) || !aligned16(v_new) || (k_new_token_stride * elt) % 16 ||
+            (v_new_token_stride * elt) % 16)
+            return fail(PKA_ERR_INVALID_ARGUMENT, "k_new/v_new rows must be 16-byte aligned");
+    }
     const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
     int64_t lmax = max_context_len > 0 ? max_context_len : table_cap;
     if (lmax > table_cap)
@@ -245,6 +262,11 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
     a.max_context_len = (int32_t)lmax;
     a.partition_size = partition_size;
     a.num_partitions = (int32_t)parts;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_new_token_stride = k_new_token_stride;
+    a.v_new_token_stride = v_new_token_stride;
+    a.slot_mapping = slot_mapping;
     if (need > 0) {
         const pka::WorkspaceLayout w =
             pka::decode_workspace_layout(num_seqs, num_q_heads, head_dim, parts);
@@ -261,6 +283,43 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
     if (e != hipSuccess)
         return fail(PKA_ERR_HIP, "paged_attention_decode launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+
+extern "C" {
+
+pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void *q,
+                                      const void *k_cache, const void *v_cache,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t num_blocks, int32_t block_size, float scale,
+                                      pka_dtype kv_dtype, int32_t max_context_len,
+                                      int32_t partition_size, void *workspace,
+                                      size_t workspace_bytes, void *stream)
+{
+    return decode_impl(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                       block_size, scale, kv_dtype, max_context_len, partition_size, workspace,
+                       workspace_bytes, stream, nullptr, nullptr, 0, 0, nullptr);
+}
+
+pka_status pka_paged_attention_decode_append(
+    void *out, pka_dtype out_dtype, const void *q, const void *k_new, const void *v_new,
+    int64_t k_new_token_stride, int64_t v_new_token_stride, const int64_t *slot_mapping,
+    void *k_cache, void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_blocks, int32_t block_size, float scale, pka_dtype kv_dtype,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream)
+{
+    if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null k_new, v_new or slot_mapping");
+    return decode_impl(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                       block_size, scale, kv_dtype, max_context_len, partition_size, workspace,
+                       workspace_bytes, stream, k_new, v_new, k_new_token_stride,
+                       v_new_token_stride, slot_mapping);
 }
 
 }  // extern "C"

@@ -259,6 +259,12 @@ struct PartitionParams {
     const int2 *items;    // work list {b, j} (null: dense grid over (j, h, b))
     int32_t *wl_header;   // [0] next dynamic item, [1] number of {b, j} items
     int32_t *counters;    // per (b, kv head): partitions done; zero between calls
+    // appended token per sequence (k_new null: plain decode)
+    const char *k_new, *v_new;
+    int64_t k_new_stride, v_new_stride;  // bytes between sequences
+    const int64_t *slots;
+    char *k_store, *v_store;             // the pools, written at slots[b]
+    int64_t num_slots;
 };
 
 template <class T, int D, int BS, int G>
@@ -341,6 +347,32 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
     const int nchunks = (t_end - t_begin + CT - 1) / CT;
     const int nk = nchunks > w ? (nchunks - w + NW - 1) / NW : 0;  // chunks of this wave
     const int last_blk = t_end > 0 ? (t_end - 1) / BS - pb0 : 0;   // partition-relative
+
+    // Appended token: the item holding position L-1 stores the new K/V row
+    // at slots[b] and uses it from registers for that position, so no other
+    // workgroup ever has to see the store.
+    const bool app = p.k_new != nullptr && L > 0 && t_end == L;
+    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+    int k_last = -1, w_last = -1, i_last = 0, tg_last = 0;
+    if (app) {
+        const int rel = L - 1 - t_begin;
+        const int c_last = rel / CT;
+        w_last = c_last % NW;
+        k_last = c_last / NW;
+        i_last = (rel % CT) / TPL;
+        tg_last = rel % TPL;
+        const int64_t hoff = (int64_t)h * D * S::ELT + cl * 16;
+        knew = *reinterpret_cast<const uint4 *>(p.k_new + b * p.k_new_stride + hoff);
+        vnew = *reinterpret_cast<const uint4 *>(p.v_new + b * p.v_new_stride + hoff);
+        const int64_t slot = p.slots[b];
+        if (w == 0 && tg == 0 && slot >= 0 && slot < p.num_slots) {
+            const int64_t blk = slot / BS;
+            const int64_t dst = (blk * p.num_kv_heads + h) * S::TILE + (slot - blk * BS) * (D * S::ELT) +
+                                cl * 16;
+            *reinterpret_cast<uint4 *>(p.k_store + dst) = knew;
+            *reinterpret_cast<uint4 *>(p.v_store + dst) = vnew;
+        }
+    }
 
     // query rows of the group: 16 bytes per lane per head
     // Softmax runs on raw dot products scaled by c = |scale| * log2(e) >= 0
@@ -440,7 +472,23 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             }
         }
     };
-    auto process_any = [&](int k, const uint4 *kr, uint4 *vr) {
+    auto process_any = [&](int k, uint4 *kr, uint4 *vr) {
+        if (app && k == k_last && w == w_last) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                if (i == i_last) {
+                    const bool mine = tg == tg_last;
+                    kr[i].x = mine ? knew.x : kr[i].x;
+                    kr[i].y = mine ? knew.y : kr[i].y;
+                    kr[i].z = mine ? knew.z : kr[i].z;
+                    kr[i].w = mine ? knew.w : kr[i].w;
+                    vr[i].x = mine ? vnew.x : vr[i].x;
+                    vr[i].y = mine ? vnew.y : vr[i].y;
+                    vr[i].z = mine ? vnew.z : vr[i].z;
+                    vr[i].w = mine ? vnew.w : vr[i].w;
+                }
+            }
+        }
         if (t_begin + (w + k * NW) * CT + CT <= t_end)
             process(std::true_type{}, k, kr, vr);
         else
@@ -680,6 +728,14 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
     p.items = a.items;
     p.wl_header = a.wl_header;
     p.counters = a.counters;
+    p.k_new = static_cast<const char *>(a.k_new);
+    p.v_new = static_cast<const char *>(a.v_new);
+    p.k_new_stride = a.k_new_token_stride * dtype_bytes(a.kv_dtype);
+    p.v_new_stride = a.v_new_token_stride * dtype_bytes(a.kv_dtype);
+    p.slots = a.slot_mapping;
+    p.k_store = static_cast<char *>(const_cast<void *>(a.k_cache));
+    p.v_store = static_cast<char *>(const_cast<void *>(a.v_cache));
+    p.num_slots = (int64_t)a.num_blocks * a.block_size;
 
     const size_t lds = lds_bytes<T, D, BS, G>() + 16;
     hipError_t e;

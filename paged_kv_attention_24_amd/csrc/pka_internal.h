@@ -44,6 +44,10 @@ struct DecodeArgs {
     int2 *items;              // work list {b, j}, [B * num_partitions]; null: dense grid
     int32_t *wl_header;       // [2]: dynamic-item counter, item count (work-list mode)
     int32_t *counters;        // [B][Hkv] completion counters; zero before and after a call
+    // optional appended token per sequence (k_new null: plain decode)
+    const void *k_new, *v_new;
+    int64_t k_new_token_stride, v_new_token_stride;  // elements
+    const int64_t *slot_mapping;
 };
 
 // The workspace of a multi-partition decode starts with this many bytes of

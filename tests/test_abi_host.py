@@ -133,3 +133,27 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         pka.paged_attention_decode(torch.zeros(1, 4, 64), kc, kc, torch.zeros(1, 1, dtype=torch.int32),
                                    torch.ones(1, dtype=torch.int32), 0.125, 2, 16)
+
+
+def append(**over):
+    a = dict(out=FAKE, odt=0, q=FAKE, kn=FAKE, vn=FAKE, ks=512, vs=512, sl=FAKE, kc=FAKE,
+             vc=FAKE, bt=FAKE, MB=64, cl=FAKE, B=16, Hq=32, Hkv=8, D=64, NB=1000, bs=16,
+             scale=0.125, kdt=1, maxl=1024, P=0, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    lib = pka.load_library()
+    st = lib.pka_paged_attention_decode_append(
+        a["out"], a["odt"], a["q"], a["kn"], a["vn"], a["ks"], a["vs"], a["sl"], a["kc"],
+        a["vc"], a["bt"], a["MB"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"],
+        a["scale"], a["kdt"], a["maxl"], a["P"], a["ws"], a["wsb"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kn=None), 1), (dict(vn=None), 1), (dict(sl=None), 1), (dict(ks=511), 1),
+    (dict(vs=8), 1), (dict(kn=FAKE + 4), 1), (dict(ks=516), 1), (dict(D=96), 2),
+    (dict(kdt=9), 1), (dict(Hq=12), 1), (dict(P=24), 1), (dict(ws=None), 3),
+])
+def test_append_rejects(over, status):
+    st, msg = append(**over)
+    assert st == status, (over, st, msg)
+    assert msg
