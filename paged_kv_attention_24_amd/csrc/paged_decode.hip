@@ -50,7 +50,14 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kLoadsPerChunk = 4;
+#ifndef PKA_LOADS_PER_CHUNK
+#define PKA_LOADS_PER_CHUNK 4
+#endif
+#ifndef PKA_PREFETCH_DEPTH
+#define PKA_PREFETCH_DEPTH 1
+#endif
+constexpr int kLoadsPerChunk = PKA_LOADS_PER_CHUNK;  // 1 KiB wave loads per chunk per tensor
+constexpr int kPrefetchDepth = PKA_PREFETCH_DEPTH;   // chunks in flight ahead of the one processed
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -495,24 +502,27 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             process(std::false_type{}, k, kr, vr);
     };
 
-    // Software pipeline: the loads of chunk k+1 are in flight while chunk k
-    // is processed; the steady-state loop issues its loads unconditionally.
+    // Software pipeline: a ring of kPrefetchDepth + 1 chunk buffers; the
+    // loads of chunks k+1 .. k+kPrefetchDepth are in flight while chunk k is
+    // processed.  Every load is issued unconditionally (past the wave's last
+    // chunk the index is clamped to it, a cache hit), so the compiler's wait
+    // counts stay exact.
     if (nk > 0) {
-        uint4 ka[NL], va[NL], kb[NL], vb[NL];
-        load_chunk(0, ka, va);
-        int k = 0;
-        for (; k + 2 < nk; k += 2) {
-            load_chunk(k + 1, kb, vb);
-            process_any(k, ka, va);
-            load_chunk(k + 2, ka, va);
-            process_any(k + 1, kb, vb);
-        }
-        if (k + 1 < nk) {
-            load_chunk(k + 1, kb, vb);
-            process_any(k, ka, va);
-            process_any(k + 1, kb, vb);
-        } else {
-            process_any(k, ka, va);
+        constexpr int NBUF = kPrefetchDepth + 1;
+        uint4 kbuf[NBUF][NL], vbuf[NBUF][NL];
+#pragma unroll
+        for (int d = 0; d < kPrefetchDepth; ++d)
+            load_chunk(d < nk ? d : nk - 1, kbuf[d], vbuf[d]);
+        for (int k0 = 0; k0 < nk; k0 += NBUF) {
+#pragma unroll
+            for (int r = 0; r < NBUF; ++r) {
+                const int k = k0 + r;
+                if (k >= nk)
+                    break;
+                const int kn = k + kPrefetchDepth < nk ? k + kPrefetchDepth : nk - 1;
+                load_chunk(kn, kbuf[(r + kPrefetchDepth) % NBUF], vbuf[(r + kPrefetchDepth) % NBUF]);
+                process_any(k, kbuf[r], vbuf[r]);
+            }
         }
     }
 
