@@ -74,6 +74,13 @@ struct TBF16 {
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+// c ? a : b per component (a ternary on the struct type would select
+// addresses and keep register arrays in memory)
+__device__ __forceinline__ uint4 select4(bool c, const uint4 &a, const uint4 &b)
+{
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 // acc + (16 bytes of q) . (16 bytes of k), fp32 accumulation.
 __device__ __forceinline__ float dot16(TF32, const uint4 &q, const uint4 &k, float acc)
 {
@@ -132,6 +139,56 @@ __device__ __forceinline__ void axpy16(TBF16, float p, const uint4 &v, float *o)
     axpy_b2(p, v.y, o + 2);
     axpy_b2(p, v.z, o + 4);
     axpy_b2(p, v.w, o + 6);
+}
+
+// ---- matrix-core pieces (fp16 / bf16 KV) --------------------------------
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// S^T tile += K rows (16 tokens x 32 dims) * q^T (32 dims x 16 heads).
+// Lane l supplies K[token l%16][dims 8(l/16)..+7] and q[head l%16][same dims];
+// it receives S^T[token 4(l/16)+i][head l%16], i = 0..3.
+__device__ __forceinline__ float4_t mma_qk(TF16, const uint4 &k, const uint4 &q, float4_t acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k),
+                                                  __builtin_bit_cast(half8_t, q), acc, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mma_qk(TBF16, const uint4 &k, const uint4 &q, float4_t acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k),
+                                                   __builtin_bit_cast(bf16x8_t, q), acc, 0, 0, 0);
+}
+// O^T tile += V^T (16 dims x 16 tokens) * P^T (16 tokens x 16 heads).
+// Lane l supplies V[tokens 4(l/16)..+3][dim l%16] and P[same tokens][head l%16];
+// it accumulates O^T[dim 4(l/16)+i][head l%16].
+__device__ __forceinline__ float4_t mma_pv(TF16, const uint2 &v, const uint2 &pr, float4_t acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, v),
+                                                 __builtin_bit_cast(half4_t, pr), acc, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mma_pv(TBF16, const uint2 &v, const uint2 &pr, float4_t acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v),
+                                                     __builtin_bit_cast(short4_t, pr), acc, 0, 0, 0);
+}
+
+// 16 bytes per lane straight from global memory into LDS at base + 16*lane.
+__device__ __forceinline__ void load_to_lds(const char *g, char *lds_base)
+{
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds_base), 16, 0, 0);
+}
+
+// Transposing LDS read: within each group of 16 lanes, the four 16-bit
+// values read by lanes 4r..4r+3 become element r of the lanes, one column
+// per lane (lane i receives value i%4 of lane 4r + i/4).
+__device__ __forceinline__ uint2 lds_read_tr16(const char *p)
+{
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(p)));
 }
 
 template <int CTRL>
@@ -248,9 +305,11 @@ __device__ __forceinline__ float coherent_load(const float *p)
 {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every store of this
-// wave has been acknowledged.
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every vector memory
+// access of this wave has completed (loads landed, stores acknowledged).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left free
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
 
 struct PartitionParams {
     void *out;
@@ -274,7 +333,7 @@ struct PartitionParams {
     int64_t num_slots;
 };
 
-template <class T, int D, int BS, int G>
+template <class T, int D, int BS, int G, int W>
 struct Shape {
     static constexpr int ELT = T::kBytes;
     static constexpr int VEC = 16 / ELT;           // elements per lane load
@@ -283,23 +342,65 @@ struct Shape {
     static constexpr int NL = kLoadsPerChunk;      // loads per chunk per tensor
     static constexpr int CT = NL * TPL;            // tokens per chunk
     static constexpr int TILE = BS * D * ELT;      // bytes of one (block, head) tile
-    static constexpr int NW = (G * D * TPL * 4 * 4 > 48 * 1024) ? 2 : 4;  // waves per workgroup
+    // half-precision KV runs QK^T and PV on the matrix cores, with K and V
+    // staged through LDS; fp32 KV stays on the vector ALUs
+    static constexpr bool MFMA = !std::is_same<T, TF32>::value;
+    static constexpr int NW = W;                   // waves per workgroup
+    static constexpr int STAGE = MFMA ? 2 * 2 * NL * 1024 : 0;  // LDS bytes per wave: 2 chunks of K and V
     static_assert(LPR >= 1 && LPR <= 32 && TPL * LPR == kWave, "row must fit a wave");
     static_assert(BS % TPL == 0, "a wave load must stay inside one block");
 };
 
-template <class T, int D, int BS, int G>
+// LDS of a workgroup.  The dynamic area holds, on the vector-ALU path,
+// [NW][G][D] wave rows, then [NW][G] sums and [NW][G] maxima; on the matrix
+// path only the sums and maxima.  Two ints (work-list slot, merge flag)
+// follow it.  The matrix path has a static staging buffer, two chunks of K
+// and V per wave; once a wave has finished streaming, its rows for the merge
+// reuse the start of its part.
+struct Lds {
+    float *smem;
+    char *sb[1];
+};
+template <class T, int D, int BS, int G, int W>
 __host__ __device__ constexpr size_t lds_bytes()
 {
-    using S = Shape<T, D, BS, G>;
-    return (size_t)S::NW * G * (D + 2) * 4;
+    using S = Shape<T, D, BS, G, W>;
+    return S::MFMA ? (size_t)S::NW * G * 2 * 4 : (size_t)S::NW * G * (D + 2) * 4;
+}
+template <class T, int D, int BS, int G, int W>
+__device__ __forceinline__ float *wave_rows(const Lds &lds, int ww)
+{
+    using S = Shape<T, D, BS, G, W>;
+    return S::MFMA ? reinterpret_cast<float *>(lds.sb[0] + (size_t)ww * S::STAGE)
+                   : lds.smem + (size_t)ww * G * D;
+}
+template <class T, int D, int BS, int G, int W>
+__device__ __forceinline__ float *wave_sums(const Lds &lds)
+{
+    using S = Shape<T, D, BS, G, W>;
+    return S::MFMA ? lds.smem : lds.smem + (size_t)S::NW * G * D;
 }
 
-template <class T, int D, int BS, int G>
+template <class T, int D, int BS, int G, int W>
 __global__ void partition_kernel(PartitionParams p);
 
+// Compute units of the current device (cached per device ordinal).
+inline int device_compute_units()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        cached[dev] = cus > 0 ? cus : 256;
+    }
+    return cached[dev];
+}
+
 // Workgroups of partition_kernel<...> that fit the device at once.
-template <class T, int D, int BS, int G>
+template <class T, int D, int BS, int G, int W>
 int resident_workgroups()
 {
     static int cached[64];  // per device ordinal; 0 = not yet queried
@@ -310,21 +411,245 @@ int resident_workgroups()
         int cus = 0, per_cu = 0;
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, partition_kernel<T, D, BS, G>, Shape<T, D, BS, G>::NW * kWave,
-            lds_bytes<T, D, BS, G>() + 16);
+            &per_cu, partition_kernel<T, D, BS, G, W>, Shape<T, D, BS, G, W>::NW * kWave,
+            lds_bytes<T, D, BS, G, W>() + 16);  // static staging buffers are counted by the runtime
         cached[dev] = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
     }
     return cached[dev];
 }
 
+// One wave's share of a work item on the matrix cores (fp16 / bf16 KV).
+// The wave's chunks of K and V go straight from HBM into its LDS staging
+// area (two chunk buffers: chunk k+1 is in flight while chunk k is
+// computed).  Per 16-token tile:
+//   S^T (16 tokens x 16 heads) = K_tile . q^T     D/32 MFMAs 16x16x32
+//   online softmax on S^T, in the registers the MFMA wrote
+//   O^T (16 dims x 16 heads) += V_tile^T . P^T      D/16 MFMAs 16x16x16
+// Lane l holds S^T[token 4(l/16)+i][head l%16], which is exactly the P^T
+// operand of the second product; V_tile^T comes from the transposing LDS
+// load.  Heads l%16 >= G are padding (zero q, results discarded).  P enters
+// the product as fp16 for fp16 KV, and as a bf16 hi + lo pair (two MFMAs, 16
+// significant bits) for bf16 KV.  The softmax reference maximum of a head
+// only moves when a logit exceeds it by more than 8 (log2 units); the sum
+// and O always use the same reference, so the lazy update is exact.  Ends by
+// writing the wave's rows, sums and maxima for the merge.
+template <class T, int D, int BS, int G, int W, class LoadNew, class StoreNew>
+__device__ __forceinline__ void wave_mfma(const PartitionParams &p, int b, int h, int t_begin,
+                                          int t_end, int nk, int last_blk, int pb0, int ids,
+                                          int64_t head_off, int64_t block_stride, float c,
+                                          uint32_t qflip, bool app, int k_last, int w_last,
+                                          int row_app, const LoadNew &load_new,
+                                          const StoreNew &store_new, const Lds &lds, float *lred,
+                                          float *mred)
+{
+    using S = Shape<T, D, BS, G, W>;
+    constexpr int NW = S::NW, LPR = S::LPR, TPL = S::TPL, NL = S::NL, CT = S::CT;
+    constexpr int R = D * S::ELT;     // bytes per token row
+    constexpr int TPC = CT / 16;      // 16-token tiles per chunk
+    constexpr int KS = D / 32;        // 32-dim steps of the QK product
+    constexpr int MT = D / 16;        // 16-dim tiles of the output
+    constexpr int CHUNK = NL * 1024;  // bytes of one tensor's chunk
+    constexpr float kSlack = 8.0f;    // log2 units a logit may exceed the reference max by
+    static_assert(CT % 16 == 0 && TPC >= 1, "a chunk holds whole 16-token tiles");
+    static_assert(G <= 16 && (size_t)G * D * 4 <= (size_t)CHUNK, "merge rows fit the staging area");
+
+    const int lane = threadIdx.x % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int tg = lane / LPR, cl = lane % LPR;
+    const int n = lane % 16, quad = lane / 16;
+    const bool head_ok = n < G;
+    char *stage = lds.sb[0] + (size_t)w * S::STAGE;  // this wave's [2 buffers][K, V][CHUNK]
+
+    // XOR swizzles of a staged row's 16-byte units, so that the operand reads
+    // below hit distinct LDS banks: physical unit = logical unit ^ sw(row).
+    auto swk = [](int r) { return (D == 64 ? r >> 1 : r) & (LPR - 1); };
+    auto swv = [](int r) { return ((D == 64 ? r >> 1 : r) & (LPR / 2 - 1)) << 1; };
+
+    // this lane's operand offsets inside a staged chunk
+    uint32_t kofs[TPC][KS], vofs[TPC][MT];
+#pragma unroll
+    for (int t = 0; t < TPC; ++t) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const int r = 16 * t + n, u = quad + 4 * st;
+            kofs[t][st] = r * R + 16 * (u ^ swk(r));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = 16 * t + lane / 4, u = 2 * mt + (lane % 4) / 2;
+            vofs[t][mt] = r * R + 16 * (u ^ swv(r)) + 8 * (lane % 2);
+        }
+    }
+
+    // chunk k of this wave -> buffer kd: NL 1 KiB loads of K and of V, each
+    // covering TPL whole rows of one block; lane l fills physical unit l%LPR
+    // of row l/LPR, i.e. reads that row's logical unit (l%LPR) ^ sw(row)
+    auto stage_chunk = [&](int k, char *kd) {
+        const int tc = t_begin + (w + k * NW) * CT;
+        char *vd = kd + CHUNK;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int t0 = tc + i * TPL;
+            int rb = t0 / BS - pb0;
+            rb = rb < last_blk ? rb : last_blk;
+            const int blk = __builtin_amdgcn_readlane(ids, rb);
+            const int64_t row = (int64_t)blk * block_stride + head_off + (t0 % BS) * R;
+            const int rr = i * TPL + tg;
+            load_to_lds(p.k_cache + row + tg * R + 16 * (cl ^ swk(rr)), kd + i * 1024);
+            load_to_lds(p.v_cache + row + tg * R + 16 * (cl ^ swv(rr)), vd + i * 1024);
+        }
+    };
+
+    float4_t O[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        O[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float mref = -INFINITY, lsum = 0.0f;
+
+    // The first chunk's loads go out before anything else is requested.
+    if (nk > 0)
+        stage_chunk(0, stage);
+    // q^T operand: head n, dims 8*quad + 32*st (zero for padding heads)
+    uint4 qop[KS];
+    {
+        const int nn = head_ok ? n : G - 1;
+        const char *qrow =
+            p.q + (((int64_t)b * p.num_q_heads + h * G + nn) * D + 8 * quad) * S::ELT;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * st * S::ELT);
+            v.x ^= qflip;
+            v.y ^= qflip;
+            v.z ^= qflip;
+            v.w ^= qflip;
+            qop[st] = select4(head_ok, v, make_uint4(0, 0, 0, 0));
+        }
+    }
+    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+    if (app)
+        load_new(knew, vnew);
+
+    for (int k = 0; k < nk; ++k) {
+        char *kd = stage + (k & 1) * (2 * CHUNK);
+        char *vd = kd + CHUNK;
+        const int tc = t_begin + (w + k * NW) * CT;
+        wait_vmem();  // chunk k is in LDS; nothing newer has been issued yet
+        const bool full = tc + CT <= t_end;
+        if (!full) {
+            // rows past the end: zero V (stale or NaN slots must not reach the sum)
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                if (tc + i * TPL + tg >= t_end)
+                    *reinterpret_cast<uint4 *>(vd + i * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+        }
+        if (app && k == k_last && w == w_last && lane < LPR) {
+            // position L-1 takes the new K/V, not the pool
+            *reinterpret_cast<uint4 *>(kd + row_app * R + 16 * (lane ^ swk(row_app))) = knew;
+            *reinterpret_cast<uint4 *>(vd + row_app * R + 16 * (lane ^ swv(row_app))) = vnew;
+        }
+        uint4 kop[TPC][KS];
+        uint2 vop[TPC][MT];
+#pragma unroll
+        for (int t = 0; t < TPC; ++t) {
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                kop[t][st] = *reinterpret_cast<const uint4 *>(kd + kofs[t][st]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                vop[t][mt] = lds_read_tr16(vd + vofs[t][mt]);
+        }
+        // next chunk into the other buffer (read in the previous iteration)
+        if (k + 1 < nk)
+            stage_chunk(k + 1, stage + ((k + 1) & 1) * (2 * CHUNK));
+
+#pragma unroll
+        for (int t = 0; t < TPC; ++t) {
+            float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                sacc = mma_qk(T{}, kop[t][st], qop[st], sacc);
+            const int tok0 = tc + 16 * t + 4 * quad;
+            bool ok[4];
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ok[i] = full || tok0 + i < t_end;
+                sv[i] = ok[i] ? sacc[i] : -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            if (__builtin_amdgcn_ballot_w64(head_ok && mx * c > mref * c + kSlack)) {
+                // new reference: the head's maximum over its four lanes
+                float mh = fmaxf(mx, swz_xor16(mx));
+                mh = fmaxf(mh, xor32(mh));
+                const float mnew = fmaxf(mref, mh);
+                const float corr =
+                    mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mref - mnew) * c);
+                lsum *= corr;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    O[mt] *= corr;
+                mref = mnew;
+            }
+            const float nmc = mref == -INFINITY ? 0.0f : -mref * c;
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pr[i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(sv[i], c, nmc)) : 0.0f;
+            if constexpr (std::is_same<T, TF16>::value) {
+                const half2_t h01 = {(_Float16)pr[0], (_Float16)pr[1]};
+                const half2_t h23 = {(_Float16)pr[2], (_Float16)pr[3]};
+                const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                            __builtin_bit_cast(uint32_t, h23));
+                lsum += ((float)h01.x + (float)h01.y) + ((float)h23.x + (float)h23.y);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    O[mt] = mma_pv(T{}, vop[t][mt], ph, O[mt]);
+            } else {
+                const bf162_t h01 = {(__bf16)pr[0], (__bf16)pr[1]};
+                const bf162_t h23 = {(__bf16)pr[2], (__bf16)pr[3]};
+                const bf162_t l01 = {(__bf16)(pr[0] - (float)h01.x), (__bf16)(pr[1] - (float)h01.y)};
+                const bf162_t l23 = {(__bf16)(pr[2] - (float)h23.x), (__bf16)(pr[3] - (float)h23.y)};
+                const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                            __builtin_bit_cast(uint32_t, h23));
+                const uint2 pl = make_uint2(__builtin_bit_cast(uint32_t, l01),
+                                            __builtin_bit_cast(uint32_t, l23));
+                lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    O[mt] = mma_pv(T{}, vop[t][mt], ph, O[mt]);
+                    O[mt] = mma_pv(T{}, vop[t][mt], pl, O[mt]);
+                }
+            }
+        }
+    }
+    if (app)
+        store_new(knew, vnew);
+
+    // The head's sum over its four lanes; its rows into this wave's (now
+    // idle) staging area: lane l holds dims 16*mt + 4*quad + i of head n.
+    float lh = lsum + swz_xor16(lsum);
+    lh += xor32(lh);
+    float *rows = wave_rows<T, D, BS, G, W>(lds, w);
+    if (head_ok) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<float4_t *>(rows + n * D + 16 * mt + 4 * quad) = O[mt];
+    }
+    if (lane < G) {
+        lred[w * G + lane] = lh;
+        mred[w * G + lane] = mref;
+    }
+}
+
 // One work item: the tokens [j*P, min((j+1)*P, L_b)) of kv head h of
 // sequence b, for all G query heads of the group.  Called by every thread
 // of the workgroup with the same (b, h, j).
-template <class T, int D, int BS, int G>
+template <class T, int D, int BS, int G, int W>
 __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h, int j,
-                                          float *smem)
+                                          const Lds &lds)
 {
-    using S = Shape<T, D, BS, G>;
+    float *smem = lds.smem;
+    using S = Shape<T, D, BS, G, W>;
     constexpr int NW = S::NW, LPR = S::LPR, TPL = S::TPL, NL = S::NL, CT = S::CT, VEC = S::VEC;
 
     const int lane = threadIdx.x % kWave;
@@ -359,33 +684,50 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
     // at slots[b] and uses it from registers for that position, so no other
     // workgroup ever has to see the store.
     const bool app = p.k_new != nullptr && L > 0 && t_end == L;
-    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
     int k_last = -1, w_last = -1, i_last = 0, tg_last = 0;
+    const int rel_app = L - 1 - t_begin;
     if (app) {
-        const int rel = L - 1 - t_begin;
-        const int c_last = rel / CT;
+        const int c_last = rel_app / CT;
         w_last = c_last % NW;
         k_last = c_last / NW;
-        i_last = (rel % CT) / TPL;
-        tg_last = rel % TPL;
+        i_last = (rel_app % CT) / TPL;
+        tg_last = rel_app % TPL;
+    }
+    // this lane's 16 bytes of the appended K/V row, and their store at slots[b]
+    // by the first wave (the pool copy is for later steps; this item uses
+    // the registers)
+    auto load_new = [&](uint4 &kn, uint4 &vn) {
         const int64_t hoff = (int64_t)h * D * S::ELT + cl * 16;
-        knew = *reinterpret_cast<const uint4 *>(p.k_new + b * p.k_new_stride + hoff);
-        vnew = *reinterpret_cast<const uint4 *>(p.v_new + b * p.v_new_stride + hoff);
+        kn = *reinterpret_cast<const uint4 *>(p.k_new + b * p.k_new_stride + hoff);
+        vn = *reinterpret_cast<const uint4 *>(p.v_new + b * p.v_new_stride + hoff);
+    };
+    auto store_new = [&](const uint4 &kn, const uint4 &vn) {
         const int64_t slot = p.slots[b];
         if (w == 0 && tg == 0 && slot >= 0 && slot < p.num_slots) {
             const int64_t blk = slot / BS;
             const int64_t dst = (blk * p.num_kv_heads + h) * S::TILE + (slot - blk * BS) * (D * S::ELT) +
                                 cl * 16;
-            *reinterpret_cast<uint4 *>(p.k_store + dst) = knew;
-            *reinterpret_cast<uint4 *>(p.v_store + dst) = vnew;
+            *reinterpret_cast<uint4 *>(p.k_store + dst) = kn;
+            *reinterpret_cast<uint4 *>(p.v_store + dst) = vn;
         }
-    }
+    };
 
-    // query rows of the group: 16 bytes per lane per head
     // Softmax runs on raw dot products scaled by c = |scale| * log2(e) >= 0
     // inside the exponent; a negative scale flips the sign of q instead (exact).
     const float c = fabsf(p.scale_log2);
     const uint32_t qflip = p.scale_log2 < 0.0f ? (S::ELT == 4 ? 0x80000000u : 0x80008000u) : 0u;
+    const int64_t head_off = (int64_t)h * S::TILE;
+    const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
+    float *lred = wave_sums<T, D, BS, G, W>(lds);   // [NW][G] softmax sums
+    float *mred = lred + (size_t)NW * G;         // [NW][G] maxima, raw dot units
+
+    if constexpr (!S::MFMA) {
+    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+    if (app) {
+        load_new(knew, vnew);
+        store_new(knew, vnew);
+    }
+    // query rows of the group: 16 bytes per lane per head
     uint4 qr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -397,8 +739,6 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
         qr[g].w ^= qflip;
     }
 
-    const int64_t head_off = (int64_t)h * S::TILE;
-    const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
     const uint32_t lane_off = lane * 16;
 
     // K and V of chunk k of this wave: NL wave loads each, issued without
@@ -540,14 +880,11 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             o[g][e] = token_group_sum<LPR>(o[g][e] * f);
     }
 
-    // ---- merge the waves in LDS (log-sum-exp with the wave maxima) ------
-    float *red = smem;                        // [NW][G][D]
-    float *lred = red + (size_t)NW * G * D;   // [NW][G]
-    float *mred = lred + (size_t)NW * G;      // [NW][G], raw dot units
+    // this wave's rows for the merge in LDS
     if (tg == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float *dst = red + ((size_t)w * G + g) * D + cl * VEC;
+            float *dst = wave_rows<T, D, BS, G, W>(lds, w) + (size_t)g * D + cl * VEC;
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 dst[e] = o[g][e];
@@ -560,7 +897,14 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
             mred[w * G + g] = mw[g];
         }
     }
+    } else {
+        wave_mfma<T, D, BS, G, W>(p, b, h, t_begin, t_end, nk, last_blk, pb0, ids, head_off,
+                               block_stride, c, qflip, app, k_last, w_last, rel_app % CT,
+                               load_new, store_new, lds, lred, mred);
+    }
     __syncthreads();
+
+    // ---- merge the waves in LDS (log-sum-exp with the wave maxima) ------
 
     const int nparts_b = L == 0 ? 1 : (L + P - 1) / P;
     for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
@@ -574,7 +918,7 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
         for (int ww = 0; ww < NW; ++ww) {
             const float mv = mred[ww * G + g];
             const float sc = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mv - M) * c);
-            acc = fmaf(red[((size_t)ww * G + g) * D + d], sc, acc);
+            acc = fmaf(wave_rows<T, D, BS, G, W>(lds, ww)[(size_t)g * D + d], sc, acc);
             den = fmaf(lred[ww * G + g], sc, den);
         }
         M = M == -INFINITY ? M : M * c;  // log2 units for the partition merge
@@ -603,9 +947,9 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
     // coherent stores; waiting for their acknowledgement before the
     // workgroup barrier orders them before the counter increment, and the
     // merging workgroup reads them back with coherent loads.
-    int *flag = reinterpret_cast<int *>(smem + lds_bytes<T, D, BS, G>() / 4) + 1;
+    int *flag = reinterpret_cast<int *>(smem + lds_bytes<T, D, BS, G, W>() / 4) + 1;
     int32_t *counter = p.counters + (int64_t)b * p.num_kv_heads + h;
-    wait_stores();
+    wait_vmem();
     __syncthreads();
     if (threadIdx.x == 0)
         *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -632,18 +976,21 @@ __device__ __forceinline__ void work_item(const PartitionParams &p, int b, int h
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class T, int D, int BS, int G>
-__global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_kernel(PartitionParams p)
+template <class T, int D, int BS, int G, int W>
+__global__ __launch_bounds__((Shape<T, D, BS, G, W>::NW * kWave)) void partition_kernel(PartitionParams p)
 {
+    using S = Shape<T, D, BS, G, W>;
     extern __shared__ float smem[];
+    __shared__ __attribute__((aligned(1024))) char sb0[S::MFMA ? S::STAGE * S::NW : 16];
+    const Lds lds{smem, {sb0}};
     if (p.items == nullptr) {
-        work_item<T, D, BS, G>(p, blockIdx.z, blockIdx.y, blockIdx.x, smem);
+        work_item<T, D, BS, G, W>(p, blockIdx.z, blockIdx.y, blockIdx.x, lds);
         return;
     }
     // Work-list mode (skewed batches): a persistent grid.  Workgroup g starts
     // with item g and then takes the next unclaimed item from the counter the
     // plan kernel initialised to the grid size.
-    int *slot = reinterpret_cast<int *>(smem + lds_bytes<T, D, BS, G>() / 4);
+    int *slot = reinterpret_cast<int *>(smem + lds_bytes<T, D, BS, G, W>() / 4);
     const int hkv = p.num_kv_heads;
     const int total = p.wl_header[1] * hkv;
     int u = blockIdx.x;
@@ -653,7 +1000,7 @@ __global__ __launch_bounds__((Shape<T, D, BS, G>::NW * kWave)) void partition_ke
             next = atomicAdd(&p.wl_header[0], 1);  // consumed after the item
         const int sidx = u / hkv;
         const int2 it = p.items[sidx];
-        work_item<T, D, BS, G>(p, it.x, u - sidx * hkv, it.y, smem);
+        work_item<T, D, BS, G, W>(p, it.x, u - sidx * hkv, it.y, lds);
         if (threadIdx.x == 0)
             *slot = next;
         __syncthreads();
@@ -710,10 +1057,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *context_lens,
     }
 }
 
-template <class T, int D, int BS, int G>
-hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
+template <class T, int D, int BS, int G, int W>
+hipError_t launch_waves(const DecodeArgs &a, hipStream_t stream)
 {
-    using S = Shape<T, D, BS, G>;
+    using S = Shape<T, D, BS, G, W>;
     PartitionParams p;
     p.out = a.out;
     p.out_kind = (int)a.out_dtype;
@@ -747,25 +1094,44 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream)
     p.v_store = static_cast<char *>(const_cast<void *>(a.v_cache));
     p.num_slots = (int64_t)a.num_blocks * a.block_size;
 
-    const size_t lds = lds_bytes<T, D, BS, G>() + 16;
+    const size_t lds = lds_bytes<T, D, BS, G, W>() + 16;
     hipError_t e;
     if (a.items) {
         const int64_t dense = (int64_t)a.num_partitions * a.num_kv_heads * a.num_seqs;
-        const int64_t res = resident_workgroups<T, D, BS, G>();
+        const int64_t res = resident_workgroups<T, D, BS, G, W>();
         const int grid = (int)(dense < res ? dense : res);
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
                            a.num_seqs, a.partition_size, p.len_cap, a.items, a.wl_header, grid);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), dim3(grid), dim3(S::NW * kWave), lds,
+        hipLaunchKernelGGL((partition_kernel<T, D, BS, G, W>), dim3(grid), dim3(S::NW * kWave), lds,
                            stream, p);
     } else {
         const dim3 grid((unsigned)a.num_partitions, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-        hipLaunchKernelGGL((partition_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), lds, stream,
+        hipLaunchKernelGGL((partition_kernel<T, D, BS, G, W>), grid, dim3(S::NW * kWave), lds, stream,
                            p);
     }
     return hipGetLastError();
+}
+
+// Waves per workgroup.  fp32 KV (vector ALUs): 4, or 2 where the register
+// state of a wave is large.  Half KV (matrix cores): 8 when the grid of work
+// items is no larger than the number of compute units (a short batch is
+// latency-bound, so each item gets more waves), else 4 (more items resident
+// per compute unit).
+template <class T, int D, int BS, int G>
+hipError_t launch_typed(const DecodeArgs &a, hipStream_t s)
+{
+    if constexpr (std::is_same<T, TF32>::value) {
+        constexpr int TPL = kWave / (D * 4 / 16);
+        return launch_waves<T, D, BS, G, (G * D * TPL * 4 * 4 > 48 * 1024) ? 2 : 4>(a, s);
+    } else {
+        const int64_t items = (int64_t)a.num_partitions * a.num_kv_heads * a.num_seqs;
+        if (a.items == nullptr && items <= device_compute_units())
+            return launch_waves<T, D, BS, G, 8>(a, s);
+        return launch_waves<T, D, BS, G, 4>(a, s);
+    }
 }
 
 template <class T, int D, int BS>
