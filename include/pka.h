@@ -156,8 +156,9 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   workspace       device scratch of workspace_bytes >=
  *                   pka_decode_workspace_bytes(...), 256-byte aligned; may
  *                   be NULL when that size is 0.  Its first 1 MiB holds
- *                   completion counters (one int32 per (sequence, kv head);
- *                   num_seqs * num_kv_heads <= 262144) that must be zero
+ *                   completion and scheduling counters (one int32 per
+ *                   (sequence, kv head); num_seqs * num_kv_heads <= 262128)
+ *                   that must be zero
  *                   before the first call using this workspace: zero-fill a
  *                   new workspace once.  Every call leaves the counters
  *                   zero again, so a workspace can be reused by later calls

@@ -228,11 +228,11 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
         return fail(PKA_ERR_UNSUPPORTED, "too many partitions");
     const size_t need = pka_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
                                                    (int32_t)lmax, partition_size);
-    if (need > 0 && (int64_t)num_seqs * num_kv_heads * 4 > pka::kCounterBytes)
+    if (need > 0 && (int64_t)num_seqs * num_kv_heads > pka::kMaxCompletionCounters)
         return fail(PKA_ERR_UNSUPPORTED,
                     "num_seqs * num_kv_heads = %lld exceeds the %lld completion counters of a "
                     "multi-partition workspace",
-                    (long long)num_seqs * num_kv_heads, (long long)(pka::kCounterBytes / 4));
+                    (long long)num_seqs * num_kv_heads, (long long)pka::kMaxCompletionCounters);
     if (need > 0) {
         if (!workspace)
             return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);

@@ -55,11 +55,23 @@ struct DecodeArgs {
 // zero before the first call that uses the workspace; every call leaves
 // them zero.  A fixed size keeps them in place whatever the shapes.
 constexpr int64_t kCounterBytes = 1 << 20;
+// The persistent grid's scheduler keeps two counters (next work unit,
+// finished workgroups) in the last 64 bytes of that region, so
+// num_seqs * num_kv_heads completion counters fit in kCounterBytes - 64.
+constexpr int64_t kSchedBytes = 64;
+constexpr int64_t kMaxCompletionCounters = (kCounterBytes - kSchedBytes) / 4;
+// Work lists of at most this many sequences are planned inside the decode
+// kernel (a prefix of partition counts in LDS); longer batches get a
+// separate planning launch that writes the list to the workspace.
+constexpr int kPlanInKernelSeqs = 2048;
 
 // Above this many partitions per sequence the decode builds a work list on
 // the device instead of launching a dense (partition, head, sequence) grid
 // whose workgroups past a short sequence's end would exit empty.
-constexpr int kDenseMaxPartitions = 8;
+#ifndef PKA_DENSE_MAX_PARTITIONS
+#define PKA_DENSE_MAX_PARTITIONS 8
+#endif
+constexpr int kDenseMaxPartitions = PKA_DENSE_MAX_PARTITIONS;
 
 // Byte offsets of the decode workspace's two regions (256-aligned starts)
 // and its total size; zero when one partition covers every sequence.
