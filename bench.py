@@ -84,6 +84,8 @@ def measured_traffic(tag):
     return int(fields["traffic_bytes_per_launch"])
 
 
+DENSE_MAX_PARTITIONS = 8  # the library's switch to its persistent work-list grid
+
 PROFILE_TAGS = {2: "paged_decode_llama3_1b_b16", 3: "paged_decode_mix_b64",
                 4: "paged_decode_qwen3_b128", 5: "paged_decode_skewed_b256"}
 
@@ -226,7 +228,12 @@ def main():
     nblk = int(np.sum((wl.context_lens.astype(np.int64) + bs - 1) // bs))
     new_rows = B * Hkv * D * wl.elt_bytes * 2
     alg_bytes = kv_bytes + B * Hq * D * (wl.elt_bytes + 4) + nblk * 4 + B * 4 + 2 * new_rows + 8 * B
-    us_launch = us_per_layer  # each layer of the step is exactly one launch
+    # A layer is one decode launch, or (more than DENSE_MAX_PARTITIONS
+    # partitions per sequence: persistent grid) the decode launch plus a
+    # small launch that merges partitions; the per-layer time covers both.
+    nparts = -(-wl.max_context_len // P)
+    launches = 1 if nparts <= DENSE_MAX_PARTITIONS else 2
+    us_launch = us_per_layer
     achieved = alg_bytes / (us_launch * 1e-6) / 1e9
 
     cpu = None
@@ -284,7 +291,11 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "partition_kernel (one launch per layer: new-token store + decode)",
+            "kernel": ("partition_kernel (one launch per layer: new-token store + decode)"
+                       if launches == 1 else
+                       "partition_kernel + merge_kernel (per layer: new-token store + decode, "
+                       "then the partition merge)"),
+            "launches_per_layer": launches,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
