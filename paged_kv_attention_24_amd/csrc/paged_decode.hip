@@ -66,6 +66,10 @@ constexpr int kMfmaChunkKiB = PKA_MFMA_CHUNK_KIB;  // KiB of K (and of V) per ch
 #define PKA_SPLIT_MERGE 1
 #endif
 constexpr int kSplitMerge = PKA_SPLIT_MERGE;  // persistent grid: merge partitions in a second launch
+#ifndef PKA_PERSISTENT_WAVES
+#define PKA_PERSISTENT_WAVES 4
+#endif
+constexpr int kPersistentWaves = PKA_PERSISTENT_WAVES;  // waves per workgroup of the persistent grid
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -183,11 +187,18 @@ __device__ __forceinline__ float4_t mma_pv(TBF16, const uint2 &v, const uint2 &p
                                                      __builtin_bit_cast(short4_t, pr), acc, 0, 0, 0);
 }
 
-// 16 bytes per lane straight from global memory into LDS at base + 16*lane.
-__device__ __forceinline__ void load_to_lds(const char *g, char *lds_base)
+// 16 bytes per lane straight from global memory into LDS at byte address
+// lds_base + 16*lane (lds_base is wave-uniform: it goes to M0).
+__device__ __forceinline__ void load_to_lds(const char *g, uint32_t lds_base)
 {
     typedef __attribute__((address_space(3))) void lds_void;
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds_base), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(uintptr_t)lds_base, 16, 0, 0);
+}
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    typedef __attribute__((address_space(3))) const char lds_char;
+    return (uint32_t)(uintptr_t)(lds_char *)p;
 }
 
 // Transposing LDS read: within each group of 16 lanes, the four 16-bit
@@ -488,6 +499,19 @@ __device__ __forceinline__ ItemGeom item_geom(const PartitionParams &p, int j, i
     g.k_last = g.app ? rel / S::CT / S::NW : -1;
     g.w_last = g.app ? rel / S::CT % S::NW : -1;
     g.row_app = g.app ? rel % S::CT : 0;
+    // every field is the same in all lanes: keep them in scalar registers
+    auto u = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    g.t_begin = u(g.t_begin);
+    g.t_end = u(g.t_end);
+    g.pb0 = u(g.pb0);
+    g.last_blk = u(g.last_blk);
+    g.nk = u(g.nk);
+    g.nparts = u(g.nparts);
+    g.empty = u(g.empty);
+    g.app = u(g.app);
+    g.k_last = u(g.k_last);
+    g.w_last = u(g.w_last);
+    g.row_app = u(g.row_app);
     return g;
 }
 
@@ -732,6 +756,7 @@ __device__ __forceinline__ void mfma_items(const PartitionParams &p, const Lds &
     const int n = lane % 16, quad = lane / 16;
     const bool head_ok = n < G;
     char *stage = lds.sb[0] + (size_t)w * S::STAGE;  // this wave's [2 buffers][K, V][CHUNK]
+    const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(lds_address(stage));
     float *lred = wave_sums<T, D, BS, G, W>(lds);     // [NW][G] softmax sums
     float *mred = lred + (size_t)NW * G;             // [NW][G] maxima, raw dot units
     // Softmax runs on raw dot products scaled by c = |scale| * log2(e) >= 0
@@ -764,11 +789,12 @@ __device__ __forceinline__ void mfma_items(const PartitionParams &p, const Lds &
     // chunk k of an item -> buffer kd: NL 1 KiB loads of K and of V, each
     // covering TPL whole rows of one block; lane l fills physical unit l%LPR
     // of row l/LPR, i.e. reads that row's logical unit (l%LPR) ^ sw(row)
-    auto stage_chunk = [&](int h, const ItemGeom &g, int ids, int k, char *kd)
+    auto stage_chunk = [&](int h, const ItemGeom &g, int ids, int k, int buf)
                            __attribute__((always_inline)) {
-        const int tc = g.t_begin + (w + k * NW) * CT;
+        const int tc = __builtin_amdgcn_readfirstlane(g.t_begin + (w + k * NW) * CT);
         const int64_t head_off = (int64_t)h * S::TILE;
-        char *vd = kd + CHUNK;
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(stage_lds + buf * (2 * CHUNK));
+        const uint32_t vd = kd + CHUNK;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int t0 = tc + i * TPL;
@@ -790,7 +816,7 @@ __device__ __forceinline__ void mfma_items(const PartitionParams &p, const Lds &
                      uint4 &vnew, int buf) __attribute__((always_inline)) {
         int issued = KS + (g.app ? 2 : 0);
         if (g.nk > 0) {
-            stage_chunk(h, g, ids, 0, stage + buf * (2 * CHUNK));
+            stage_chunk(h, g, ids, 0, buf);
             issued += 2 * NL;
         }
         const int nn = head_ok ? n : G - 1;
@@ -866,7 +892,7 @@ __device__ __forceinline__ void mfma_items(const PartitionParams &p, const Lds &
             }
             // next chunk into the other buffer (read in the previous iteration)
             if (k + 1 < g.nk)
-                stage_chunk(h, g, ids, k + 1, stage + ((par + k + 1) & 1) * (2 * CHUNK));
+                stage_chunk(h, g, ids, k + 1, (par + k + 1) & 1);
             else
                 last((par + k + 1) & 1);
 
@@ -1060,7 +1086,7 @@ __device__ __forceinline__ void mfma_items(const PartitionParams &p, const Lds &
             ids = idsn;
             L = Ln;
             g = gn;
-            par = parn;
+            par = __builtin_amdgcn_readfirstlane(parn);
 #pragma unroll
             for (int st = 0; st < KS; ++st)
                 qop[st] = qopn[st];
@@ -1522,6 +1548,8 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t s)
         const int64_t items = (int64_t)a.num_partitions * a.num_kv_heads * a.num_seqs;
         if (a.items == nullptr && items <= device_compute_units())
             return launch_waves<T, D, BS, G, 8>(a, s);
+        if (a.items != nullptr)
+            return launch_waves<T, D, BS, G, kPersistentWaves>(a, s);
         return launch_waves<T, D, BS, G, 4>(a, s);
     }
 }
