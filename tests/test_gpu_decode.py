@@ -259,3 +259,23 @@ def test_bad_partition_size_is_rejected():
         gpu_decode(wl, partition_size=24)
     with pytest.raises(pka.PkaError):
         gpu_decode(wl, partition_size=4096)
+
+
+@pytest.mark.parametrize("dtype,B", [("f16", 2048), ("bf16", 2049), ("f32", 2049)])
+def test_large_batch_work_list(dtype, B):
+    """Batches at and past the size the kernel plans in its own LDS: beyond
+    it the work list is planned by a separate launch into the workspace.
+    Several partitions per sequence, empty sequences mixed in; rows of the
+    longest sequence and of the last sequences are always compared."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 700, size=B)
+    lens[::97] = 0
+    lens[B - 1] = 1300
+    wl = case(31, dtype, [int(x) for x in lens], 8, 2, 64, 16)
+    got = gpu_decode(wl, partition_size=128)
+    assert np.all(np.isfinite(got))
+    assert np.all(got[lens == 0] == 0)
+    must = [(B - 1, h) for h in range(8)] + [(B - 2, h) for h in range(8)] + [(0, 3), (2047, 5)]
+    rows = sample_rows(wl, 160, seed=B, must=must)
+    ref = oracle.decode_workload(wl, rows=rows)
+    check_close(got[rows[:, 0], rows[:, 1]], ref, dtype, f"B={B}")
