@@ -16,6 +16,10 @@ Paged attention" and "Key features > GPU-optimised kernels"):
       batched one-token attention over the block-wise cache.
 
 Pools are [num_blocks, num_kv_heads, block_size, head_dim].
+
+PKA_LIBRARY, if set, names another library file of this directory to load
+instead of libpka.so (libpka_vector_alu.so: the vector-ALU build that the
+matrix-core path is measured against).
 """
 from __future__ import annotations
 
@@ -30,7 +34,10 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpka.so")
+_LIB_NAME = os.environ.get("PKA_LIBRARY", "libpka.so")
+if os.path.basename(_LIB_NAME) != _LIB_NAME or not _LIB_NAME.startswith("libpka"):
+    raise ImportError(f"PKA_LIBRARY={_LIB_NAME!r}: expected a libpka*.so file name of the package")
+_LIB_PATH = os.path.join(_HERE, _LIB_NAME)
 
 PKA_OK = 0
 _DTYPE_CODES = None  # filled lazily (needs torch)

@@ -1,6 +1,11 @@
 """Build libpka.so (HIP kernels for gfx950 + the C ABI) in the package dir.
 
-    python -m paged_kv_attention_24_amd._build
+    python -m paged_kv_attention_24_amd._build [-v] [--variant vector_alu]
+
+``--variant vector_alu`` builds libpka_vector_alu.so instead: the same
+library with fp16/bf16 KV on the vector ALUs rather than the matrix cores,
+the build the matrix-core path is measured against (load it by setting
+PKA_LIBRARY=libpka_vector_alu.so before importing the package).
 
 Every HIP translation unit is compiled with packed FP32 instructions
 disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host
@@ -23,6 +28,7 @@ LIB_PATH = os.path.join(PKG, "libpka.so")
 ARCH = "gfx950"
 SOURCES = ["paged_decode.hip", "kv_cache_write.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+VARIANTS = {"vector_alu": ["-DPKA_MATRIX_CORES=0"]}
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,12 +40,17 @@ def _compile_cmd(src: str, obj: str, extra=()):
     return [HIPCC, *lang, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), variant: str | None = None) -> str:
+    build_dir, lib_path = BUILD_DIR, LIB_PATH
+    if variant is not None:
+        extra_flags = [*extra_flags, *VARIANTS[variant]]
+        build_dir = os.path.join(BUILD_DIR, variant)
+        lib_path = os.path.join(PKG, f"libpka_{variant}.so")
+    os.makedirs(build_dir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = _compile_cmd(src, obj, extra_flags)
         if verbose:
@@ -57,13 +68,13 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def clean():
@@ -71,4 +82,5 @@ def clean():
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    var = sys.argv[sys.argv.index("--variant") + 1] if "--variant" in sys.argv else None
+    print(build(verbose="-v" in sys.argv, variant=var))

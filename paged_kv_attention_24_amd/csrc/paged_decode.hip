@@ -70,6 +70,12 @@ constexpr int kSplitMerge = PKA_SPLIT_MERGE;  // persistent grid: merge partitio
 #define PKA_PERSISTENT_WAVES 4
 #endif
 constexpr int kPersistentWaves = PKA_PERSISTENT_WAVES;  // waves per workgroup of the persistent grid
+#ifndef PKA_MATRIX_CORES
+#define PKA_MATRIX_CORES 1
+#endif
+// fp16/bf16 KV on the matrix cores (1) or, like fp32 KV, on the vector ALUs
+// (0: the build that the matrix path is measured against)
+constexpr bool kMatrixCores = PKA_MATRIX_CORES != 0;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -381,15 +387,15 @@ struct Shape {
     static constexpr int VEC = 16 / ELT;           // elements per lane load
     static constexpr int LPR = D / VEC;            // lanes per token row
     static constexpr int TPL = kWave / LPR;        // tokens per wave load
+    // half-precision KV runs QK^T and PV on the matrix cores, with K and V
+    // staged through LDS; fp32 KV stays on the vector ALUs
+    static constexpr bool MFMA = kMatrixCores && !std::is_same<T, TF32>::value;
     // loads per chunk per tensor: kLoadsPerChunk on the vector-ALU path;
     // kMfmaChunkKiB on the matrix path, but at least one 16-token tile
-    static constexpr int NL = std::is_same<T, TF32>::value ? kLoadsPerChunk
+    static constexpr int NL = !MFMA ? kLoadsPerChunk
                               : (kMfmaChunkKiB > 16 * D * ELT / 1024 ? kMfmaChunkKiB : 16 * D * ELT / 1024);
     static constexpr int CT = NL * TPL;            // tokens per chunk
     static constexpr int TILE = BS * D * ELT;      // bytes of one (block, head) tile
-    // half-precision KV runs QK^T and PV on the matrix cores, with K and V
-    // staged through LDS; fp32 KV stays on the vector ALUs
-    static constexpr bool MFMA = !std::is_same<T, TF32>::value;
     static constexpr int NW = W;                   // waves per workgroup
     static constexpr int STAGE = MFMA ? 2 * 2 * NL * 1024 : 0;  // LDS bytes per wave: 2 chunks of K and V
     static_assert(LPR >= 1 && LPR <= 32 && TPL * LPR == kWave, "row must fit a wave");
@@ -1533,16 +1539,16 @@ hipError_t launch_waves(const DecodeArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Waves per workgroup.  fp32 KV (vector ALUs): 4, or 2 where the register
-// state of a wave is large.  Half KV (matrix cores): 8 when the grid of work
+// Waves per workgroup.  fp32 KV (and half KV in a vector-ALU build): 4, or 2
+// where the register state of a wave is large.  Half KV (matrix cores): 8 when the grid of work
 // items is no larger than the number of compute units (a short batch is
 // latency-bound, so each item gets more waves), else 4 (more items resident
 // per compute unit).
 template <class T, int D, int BS, int G>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s)
 {
-    if constexpr (std::is_same<T, TF32>::value) {
-        constexpr int TPL = kWave / (D * 4 / 16);
+    if constexpr (std::is_same<T, TF32>::value || !kMatrixCores) {
+        constexpr int TPL = kWave / (D * T::kBytes / 16);
         return launch_waves<T, D, BS, G, (G * D * TPL * 4 * 4 > 48 * 1024) ? 2 : 4>(a, s);
     } else {
         const int64_t items = (int64_t)a.num_partitions * a.num_kv_heads * a.num_seqs;
