@@ -14,28 +14,38 @@
 //    [j*P, min((j+1)*P, L_b)) of one kv head.  All G = Hq/Hkv query heads of
 //    the group are served by the same K/V reads, so every KV byte is read
 //    from HBM exactly once.
-//  * One workgroup of NW wave64s per work item.  The partition is cut into
-//    chunks of CT tokens (4 coalesced 1 KiB loads per chunk per tensor);
-//    chunks are dealt round-robin to the waves.
+//  * A workgroup of NW wave64s works on an item; the partition is cut into
+//    chunks that are dealt round-robin to the waves, and the waves' (max,
+//    sum, O) are merged in LDS with log-sum-exp once per item.
 //  * Lane layout of a load: a (block, kv head) tile is a contiguous
 //    [block_size][head_dim] run, so one wave load of 64 lanes x 16 bytes
 //    covers TPL = 64 / LPR whole token rows, LPR = head_dim*elt/16 lanes per
-//    row.  Lane l holds 16 bytes (VEC elements) of token l / LPR.
-//  * Pass 1 streams K: partial dot products with v_dot2_f32_{f16,bf16} (or
-//    fp32 FMA), a DPP butterfly over the LPR lanes of a row, the scale and
-//    log2(e) folded in; logits go to LDS, a running max stays in registers.
-//  * Pass 2 streams V: p = exp2(s - m_wave) and o += p * V with
-//    v_fma_mix-style mixed-precision FMAs into fp32 accumulators.  Because
-//    each wave knows its maximum before pass 2, nothing is ever rescaled in
-//    the loop.
-//  * Merge: per-lane partial sums (token groups x waves) are combined in LDS
-//    with each wave's maximum (log-sum-exp), once per work item.
-//  * Partitions: with more than one partition per sequence each work item
-//    writes (max, sum, normalised row) to the workspace and counts itself
-//    done; the last one of its (sequence, kv head) merges all of them into
-//    the output (log-sum-exp) and resets the counter.  One launch per call.
-//  * Every K/V load is issued one chunk ahead of its use (register double
-//    buffering), so each wave keeps up to 8 KiB in flight.
+//    row.  Lane l moves 16 bytes (VEC elements) of token l / LPR.
+//  * fp16 / bf16 KV run on the matrix cores (mfma_items): each wave copies
+//    its chunks of K and V straight from HBM into LDS (global_load_lds,
+//    XOR-swizzled rows), one chunk ahead of the one computed.  Per 16-token
+//    tile, 16x16x32 MFMAs give the scores of all G heads (K tile times q^T),
+//    the online softmax runs in the registers the MFMA wrote, and 16x16x16
+//    MFMAs accumulate O^T += V^T P^T, V^T coming from the transposing LDS
+//    read.
+//  * fp32 KV runs on the vector ALUs (work_item): fp32 FMAs and a DPP
+//    butterfly over the LPR lanes of a row give the scores, a single-pass
+//    online softmax rescales once per chunk, and o += p V accumulates in
+//    fp32; the K and V loads of chunk k+1 are in flight while chunk k is
+//    processed.  (A build with PKA_MATRIX_CORES=0 runs half KV this way too,
+//    with v_dot2_f32_{f16,bf16} products; it exists to measure against.)
+//  * Grids.  With at most kDenseMaxPartitions partitions per sequence, one
+//    workgroup per item (a dense grid); when a sequence has several
+//    partitions each item writes (max, sum, normalised row) to the workspace
+//    and the last one of its (sequence, kv head) to finish, found with a
+//    counter, merges them into the output.  With more, a persistent grid of
+//    as many workgroups as fit the GPU claims (item, kv head) units from a
+//    counter, over a work list planned in each workgroup's LDS (matrix path,
+//    up to kPlanInKernelSeqs sequences) or by a one-workgroup plan_kernel;
+//    on the matrix path merge_kernel then combines the partitions.
+//  * Fused append: for pka_paged_attention_decode_append the item that holds
+//    position L_b - 1 stores the sequence's new K/V row in its slot and uses
+//    it from registers for that position.
 //  * Tokens >= L (the tail of the last block) are excluded by selects, never
 //    by multiplying with 0, so stale or NaN slot contents cannot leak.
 
