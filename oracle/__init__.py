@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged decode attention and the KV-cache write.
+"""fp64 CPU oracle for paged decode attention, its multi-token causal form,
+and the KV-cache write.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package.  The product path
@@ -84,6 +85,9 @@ def _declare(h):
         P, P, P, P, P, P, i64, i64, ctypes.c_int, P, i32, P, i32, i32, i32, i32, i32, i32, f64,
         P, i32, i32]
     h.oracle_paged_attention_decode_append.restype = ctypes.c_int
+    h.oracle_paged_attention_prefill.argtypes = [
+        P, P, P, P, ctypes.c_int, P, i32, P, P, i32, i32, i32, i32, i32, i32, f64, P, i32, i32]
+    h.oracle_paged_attention_prefill.restype = ctypes.c_int
     h.oracle_kv_cache_write.argtypes = [P, P, i64, i64, P, i32, P, P, i32, i32, i32, i32, i32]
     h.oracle_kv_cache_write.restype = ctypes.c_int
     return h
@@ -187,6 +191,55 @@ def paged_attention_decode_append(q, k_cache, v_cache, k_new, v_new, block_table
     if rc != 0:
         raise OracleError(f"oracle decode failed: {STATUS.get(rc, rc)}")
     return out
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                            scale, num_kv_heads, block_size, dtype, *, rows=None,
+                            threads: int = 0, handle=None) -> np.ndarray:
+    """fp64 multi-token causal paged attention.
+
+    q [N, Hq, D] holds the query rows of all sequences, sequence b owning
+    rows [query_start[b], query_start[b+1]); with T_b rows and L_b =
+    context_lens[b], its row i sits at position L_b - T_b + i and attends to
+    the tokens at positions 0 .. L_b - T_b + i.  ``rows`` (optional [n, 2]
+    pairs (r, hq)) restricts the computation; the result is then [n, D],
+    else [N, Hq, D].
+    """
+    h = handle or lib()
+    for a, w in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_stored(a, dtype, w)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    N, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    B = cl.shape[0]
+    if v_cache.shape != k_cache.shape or D2 != D or Hkv != num_kv_heads or bs != block_size:
+        raise ValueError("cache shape does not match the arguments")
+    if bt.ndim != 2 or bt.shape[0] != B or qs.shape != (B + 1,) or int(qs[-1]) != N:
+        raise ValueError("block_tables / query_start do not match q and context_lens")
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        out = np.empty((r.shape[0], D), dtype=np.float64)
+        rp, nr = _ptr(r), r.shape[0]
+    else:
+        out = np.empty((N, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    rc = h.oracle_paged_attention_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), DTYPE_CODE[dtype], _ptr(bt),
+        bt.shape[1], _ptr(cl), _ptr(qs), B, Hq, Hkv, D, NB, bs, float(scale), rp, nr,
+        int(threads))
+    if rc != 0:
+        raise OracleError(f"oracle prefill failed: {STATUS.get(rc, rc)}")
+    return out
+
+
+def prefill_workload(wl, *, rows=None, threads=0, handle=None):
+    """Oracle multi-token attention of a workloads.PrefillWorkload."""
+    return paged_attention_prefill(
+        wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start,
+        wl.scale, wl.num_kv_heads, wl.block_size, wl.dtype, rows=rows, threads=threads,
+        handle=handle)
 
 
 def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, dtype, handle=None) -> None:

@@ -1,6 +1,6 @@
 /*
- * oracle.c -- plain fp64 CPU oracle for batched paged-attention decode and
- * the multi-sequence KV-cache write.
+ * oracle.c -- plain fp64 CPU oracle for batched paged-attention decode, its
+ * multi-token causal form, and the multi-sequence KV-cache write.
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  It shares no code, header
@@ -340,6 +340,108 @@ int oracle_paged_attention_decode_append(double *out, const void *q, const void 
                       dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                       num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, scale, 0,
                       rows, n_rows, num_threads);
+}
+
+/*
+ * Multi-token causal paged attention: several new query tokens of a
+ * sequence attend over its cache, each one up to its own position.  This is
+ * the prefill of a chunk of a prompt, or the check of drafted tokens
+ * (PhotonInfer README, Korean translation: "Continuous batching scheduler",
+ * where a request advances token by token through num_computed_tokens, and
+ * the speculative-decoding item of its "Roadmap"; JackerLab "vllm" tag page,
+ * "Speculative Decoding": a large model checks several proposed tokens at
+ * once).
+ *
+ * Sequence b owns the query rows [query_start[b], query_start[b+1]).  With
+ * T = query_start[b+1] - query_start[b] and L = context_lens[b] (the tokens
+ * in the cache, the T new ones included; their K and V are already in the
+ * pools), query row r = query_start[b] + i sits at position p = L - T + i:
+ *
+ *     out[r, hq] = sum_{t <= p} softmax_t(scale * q[r, hq] . K_t) V_t.
+ *
+ * q and out are [num_query_tokens][num_q_heads][head_dim].  Every row is the
+ * definition evaluated directly in double precision: the logits of the
+ * p + 1 tokens, their maximum, the exponentials and their sum, the weighted
+ * sum of V.
+ */
+static int prefill_row(const decode_args *a, const int32_t *query_start, int64_t r, int b,
+                       int hq, double *out_row)
+{
+    int kvh = hq / (a->num_q_heads / a->num_kv_heads); /* contiguous grouping */
+    int64_t T = (int64_t)query_start[b + 1] - query_start[b];
+    int64_t i = r - query_start[b];
+    int64_t p = (int64_t)a->context_lens[b] - T + i; /* this query's position */
+    if (p < 0)
+        return ORACLE_BAD_ARGUMENT; /* more new tokens than cached ones */
+    int rc = check_row(a, b);
+    if (rc != ORACLE_OK)
+        return rc;
+    int64_t n = p + 1;
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!s)
+        return ORACLE_NO_MEMORY;
+    int64_t qbase = (r * a->num_q_heads + hq) * (int64_t)a->head_dim;
+    for (int64_t t = 0; t < n; ++t) {
+        double acc = 0.0;
+        for (int e = 0; e < a->head_dim; ++e)
+            acc += load_elem(a->q, a->dtype, qbase + e) * kv_elem(a, 0, b, kvh, t, e);
+        s[t] = a->scale * acc;
+    }
+    double m, l;
+    softmax_v(a, b, kvh, 0, n, s, out_row, &m, &l);
+    free(s);
+    return ORACLE_OK;
+}
+
+/*
+ * Every (query row, q head) of a multi-token call, or only the pairs listed
+ * in `rows` (n_rows pairs r, hq; out is then [n_rows, head_dim]).
+ * query_start has num_seqs + 1 non-decreasing entries starting at 0; its
+ * last entry is the number of query rows.
+ */
+int oracle_paged_attention_prefill(double *out, const void *q, const void *k_cache,
+                                   const void *v_cache, int dtype, const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   const int32_t *query_start, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_blocks, int32_t block_size, double scale,
+                                   const int32_t *rows, int32_t n_rows, int32_t num_threads)
+{
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16 || num_seqs < 0 || num_kv_heads <= 0 ||
+        num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || query_start[0] != 0)
+        return ORACLE_BAD_ARGUMENT;
+    for (int b = 0; b < num_seqs; ++b)
+        if (query_start[b + 1] < query_start[b])
+            return ORACLE_BAD_ARGUMENT;
+    int64_t num_rows = query_start[num_seqs];
+    decode_args a = {q, k_cache, v_cache, NULL, NULL, 0, 0, dtype, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, num_blocks, block_size, scale};
+    int64_t n = rows ? n_rows : num_rows * num_q_heads;
+    if (rows) {
+        for (int64_t k = 0; k < n; ++k)
+            if (rows[2 * k] < 0 || rows[2 * k] >= num_rows || rows[2 * k + 1] < 0 ||
+                rows[2 * k + 1] >= num_q_heads)
+                return ORACLE_BAD_ARGUMENT;
+    }
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : omp_get_max_threads())
+    for (int64_t k = 0; k < n; ++k) {
+        int64_t r = rows ? rows[2 * k] : k / num_q_heads;
+        int hq = rows ? rows[2 * k + 1] : (int)(k % num_q_heads);
+        int b = 0; /* the sequence whose query rows contain r */
+        while (query_start[b + 1] <= r)
+            ++b;
+        int rc = prefill_row(&a, query_start, r, b, hq, out + k * head_dim);
+        if (rc != ORACLE_OK) {
+#pragma omp critical
+            status = status == ORACLE_OK ? rc : status;
+        }
+    }
+    return status;
 }
 
 /*

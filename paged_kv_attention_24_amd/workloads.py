@@ -285,6 +285,87 @@ def make_config(cfg: int, *, seed: Optional[int] = None, poison: bool = True,
 
 
 # ---------------------------------------------------------------------------
+# Multi-token (causal) inputs: chunked prefill and the check of drafted tokens
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload(Workload):
+    """Inputs of a multi-token call: sequence b brings T_b new query tokens
+    (rows query_start[b] .. query_start[b+1] - 1 of q, [N, Hq, D]) whose K/V
+    are already in the pools; context_lens[b] counts the cached tokens, the
+    new ones included, so row i of sequence b sits at position
+    context_lens[b] - T_b + i."""
+
+    query_start: Optional[np.ndarray] = None  # int32 [B + 1]
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(np.diff(self.query_start).max()) if self.num_seqs else 0
+
+
+def make_prefill_case(seed: int, *, dtype: str, prefix_lens: Sequence[int],
+                      query_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                      head_dim: int, block_size: int, poison: bool = True,
+                      rng: Optional[np.random.Generator] = None, name: str = "prefill",
+                      **kw) -> PrefillWorkload:
+    """Sequences with prefix_lens[b] cached tokens and query_lens[b] new ones
+    (L_b = prefix + new).  Draw order: the pool permutation, the K pool, the
+    V pool and the decode q as make_case, then the query rows."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    new = np.asarray(query_lens, dtype=np.int64)
+    if pre.shape != new.shape or (pre < 0).any() or (new < 0).any():
+        raise ValueError("prefix_lens and query_lens: equal length, non-negative")
+    base = make_case(seed, dtype=dtype, context_lens=pre + new, num_q_heads=num_q_heads,
+                     num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                     write=False, poison=poison, rng=rng, name=name, **kw)
+    qs = np.zeros(len(new) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(new)
+    q = _round_to_dtype(
+        rng.standard_normal((int(qs[-1]), num_q_heads, head_dim), dtype=np.float32), dtype)
+    fields = {k: getattr(base, k) for k in base.__dataclass_fields__}
+    fields["q"] = q
+    return PrefillWorkload(**fields, query_start=qs)
+
+
+PREFILL_NAMES = {
+    1: "tiny multi-token: 3 seqs, cached {0,5,40} + new {7,1,20}, 8q/2kv, D=64, bs=16, fp16",
+    2: "chunked prefill, Llama-3.2-1B layer: 8 seqs x 256 new tokens after U[0,3072] cached, "
+       "32q/8kv, D=64, bs=16, fp16",
+    3: "drafted-token check, Qwen3-style layer: 64 seqs x 5 new tokens after U[2048,8192] "
+       "cached, 16q/8kv, D=128, bs=16, bf16",
+}
+
+
+def make_prefill_config(n: int, *, seed: Optional[int] = None,
+                        poison: bool = True) -> PrefillWorkload:
+    """Named multi-token workload n (1..3); seed defaults to 100 + n.  Step 1
+    of the draw order is the cached lengths (the new-token counts are fixed)."""
+    seed = 100 + n if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if n == 1:
+        pre, new = [0, 5, 40], [7, 1, 20]
+        shape = dict(dtype="f16", num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16)
+    elif n == 2:
+        pre, new = rng.integers(0, 3072 + 1, size=8), [256] * 8
+        shape = dict(dtype="f16", num_q_heads=32, num_kv_heads=8, head_dim=64, block_size=16)
+    elif n == 3:
+        pre, new = rng.integers(2048, 8192 + 1, size=64), [5] * 64
+        shape = dict(dtype="bf16", num_q_heads=16, num_kv_heads=8, head_dim=128,
+                     block_size=16)
+    else:
+        raise ValueError(f"no multi-token workload {n}")
+    wl = make_prefill_case(seed, prefix_lens=pre, query_lens=new, poison=poison, rng=rng,
+                           name=f"prefill{n}", **shape)
+    wl.meta["description"] = PREFILL_NAMES[n]
+    return wl
+
+
+# ---------------------------------------------------------------------------
 # Device transfer (data movement only)
 # ---------------------------------------------------------------------------
 

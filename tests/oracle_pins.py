@@ -10,7 +10,9 @@ the oracle disagrees with:
   * invariants (physical block relabelling, a common shift of all keys,
     convexity, batch permutation, partition independence),
   * an exhaustive check of the half-precision decoders against torch,
-  * the bitwise semantics of the cache write.
+  * the bitwise semantics of the cache write,
+  * for the multi-token causal form: fp64 SDPA with an explicit causal mask,
+    the one-token case against decode, causality bounds and closed forms.
 
 The method's statement these follow: PhotonInfer README (Korean
 translation), "Technical details > Paged attention" (block-wise cache,
@@ -337,6 +339,108 @@ def pin_append_equals_write_then_decode(h):
     assert not np.array_equal(other, fused)
 
 
+# ---------------------------------------------------------------------------
+# multi-token causal attention (chunked prefill, drafted-token check)
+# ---------------------------------------------------------------------------
+
+def prefill_case(seed, dtype="f16", pre=(0, 5, 40), new=(7, 1, 20), Hq=8, Hkv=2, D=64, bs=16,
+                 **kw):
+    return W.make_prefill_case(seed, dtype=dtype, prefix_lens=pre, query_lens=new,
+                               num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                               **kw)
+
+
+def run_prefill(h, wl, **kw):
+    return oracle.prefill_workload(wl, handle=h, **kw)
+
+
+def sdpa_causal_reference(wl):
+    """torch fp64 SDPA per sequence with an explicit boolean mask: new token
+    i of a sequence with T new and L cached tokens may see key t iff
+    t <= L - T + i."""
+    out = np.zeros((wl.num_query_tokens, wl.num_q_heads, wl.head_dim))
+    for b in range(wl.num_seqs):
+        r0, r1 = int(wl.query_start[b]), int(wl.query_start[b + 1])
+        T, L = r1 - r0, int(wl.context_lens[b])
+        if T == 0:
+            continue
+        K = torch.from_numpy(f64(gather(wl, wl.k_cache, b), wl.dtype)).permute(1, 0, 2)[None]
+        V = torch.from_numpy(f64(gather(wl, wl.v_cache, b), wl.dtype)).permute(1, 0, 2)[None]
+        Q = torch.from_numpy(f64(wl.q[r0:r1], wl.dtype)).permute(1, 0, 2)[None]
+        mask = torch.arange(L)[None, :] <= (L - T + torch.arange(T))[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            Q.contiguous(), K.contiguous(), V.contiguous(), attn_mask=mask,
+            scale=float(wl.scale), enable_gqa=True)
+        out[r0:r1] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def pin_prefill_sdpa_causal(h):
+    """P-m: multi-token result == torch fp64 SDPA with the causal mask
+    (aligned to the end of the cache) on the contiguous gathered K/V, over
+    dtypes, group sizes, head dims, block sizes, empty and full prefixes."""
+    cases = [
+        dict(dtype="f32", pre=(0, 5, 40), new=(7, 1, 20), Hq=4, Hkv=2, D=64, bs=16),
+        dict(dtype="f16", pre=(0, 31, 3), new=(33, 2, 0), Hq=8, Hkv=8, D=64, bs=16),
+        dict(dtype="bf16", pre=(17, 0), new=(16, 48), Hq=8, Hkv=4, D=128, bs=32),
+        dict(dtype="f16", pre=(64, 1, 9), new=(5, 5, 5), Hq=32, Hkv=4, D=64, bs=16),
+    ]
+    for i, c in enumerate(cases):
+        wl = prefill_case(200 + i, **c)
+        got = run_prefill(h, wl)
+        err = np.max(np.abs(got - sdpa_causal_reference(wl)))
+        assert err <= 1e-12, (c, err)
+
+
+def pin_prefill_one_token_is_decode(h):
+    """P-n: with one new token per sequence the multi-token call is the
+    decode of that token over its whole cache."""
+    wl = prefill_case(210, dtype="bf16", pre=(4, 0, 37, 15), new=(1, 1, 1, 1), Hq=8, Hkv=2)
+    got = run_prefill(h, wl)
+    dec = oracle.paged_attention_decode(
+        wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.scale,
+        wl.num_kv_heads, wl.block_size, wl.dtype, handle=h)
+    assert np.max(np.abs(got - dec)) <= 1e-14
+
+
+def pin_prefill_causality(h):
+    """P-o: a query at position p is unchanged, bit for bit, when every key
+    and value after p is replaced, and it moves when the token at p itself
+    is replaced (the bound is inclusive)."""
+    wl = prefill_case(211, dtype="f32", pre=(3, 20), new=(6, 9), Hq=4, Hkv=2)
+    base = run_prefill(h, wl)
+    b, i = 1, 4  # query row of sequence 1 at position 20 + 4
+    r = int(wl.query_start[b]) + i
+    p = int(wl.context_lens[b]) - (int(wl.query_start[b + 1]) - int(wl.query_start[b])) + i
+    later = prefill_case(211, dtype="f32", pre=(3, 20), new=(6, 9), Hq=4, Hkv=2)
+    rng = np.random.default_rng(5)
+    for t in range(p + 1, int(wl.context_lens[b])):
+        blk, off = later.block_tables[b, t // 16], t % 16
+        later.k_cache[blk, :, off, :] = rng.standard_normal((2, 64)).astype(np.float32)
+        later.v_cache[blk, :, off, :] = rng.standard_normal((2, 64)).astype(np.float32)
+    assert np.array_equal(run_prefill(h, later)[r], base[r])
+    same = prefill_case(211, dtype="f32", pre=(3, 20), new=(6, 9), Hq=4, Hkv=2)
+    blk, off = same.block_tables[b, p // 16], p % 16
+    same.v_cache[blk, :, off, :] += 1.0
+    assert not np.array_equal(run_prefill(h, same)[r], base[r])
+
+
+def pin_prefill_fresh_sequence(h):
+    """P-p: a sequence with nothing cached: its first new token sees only
+    itself (out == V_0 exactly); with all keys equal, token i gets the mean
+    of V_0 .. V_i."""
+    wl = prefill_case(212, dtype="f16", pre=(0,), new=(21,), Hq=4, Hkv=2)
+    k0 = wl.k_cache[wl.block_tables[0, 0], :, 0, :].copy()
+    for t in range(21):
+        wl.k_cache[wl.block_tables[0, t // 16], :, t % 16, :] = k0
+    got = run_prefill(h, wl)
+    V = f64(gather(wl, wl.v_cache, 0), wl.dtype)  # [21, Hkv, D]
+    for hq in range(4):
+        assert np.array_equal(got[0, hq], V[0, hq // 2])
+        for i in range(21):
+            assert np.max(np.abs(got[i, hq] - V[: i + 1, hq // 2].mean(axis=0))) <= 1e-12
+
+
 PINS = {
     "append_equals_write_then_decode": pin_append_equals_write_then_decode,
     "decoders_exhaustive": pin_decoders_exhaustive,
@@ -352,4 +456,8 @@ PINS = {
     "batch_permutation": pin_batch_permutation,
     "zero_length": pin_zero_length,
     "write": pin_write,
+    "prefill_sdpa_causal": pin_prefill_sdpa_causal,
+    "prefill_one_token_is_decode": pin_prefill_one_token_is_decode,
+    "prefill_causality": pin_prefill_causality,
+    "prefill_fresh_sequence": pin_prefill_fresh_sequence,
 }

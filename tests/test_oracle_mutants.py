@@ -48,6 +48,20 @@ MUTANTS = {
                         "if (app && t == (int64_t)a->context_lens[b] - 2)"),
     "write_token_stride": ("(const char *)k + ((int64_t)i * k_token_stride + (int64_t)h * head_dim)",
                            "(const char *)k + ((int64_t)i * num_kv_heads * head_dim + (int64_t)h * head_dim)"),
+    # multi-token: the query's own position excluded from its keys
+    "prefill_diagonal": ("    int64_t n = p + 1;\n", "    int64_t n = p;\n"),
+    # multi-token: causal mask aligned to the start instead of the end of the cache
+    "prefill_alignment": ("int64_t p = (int64_t)a->context_lens[b] - T + i;",
+                          "int64_t p = i;"),
+    # multi-token: the query row taken from the sequence index
+    "prefill_query_row": ("int64_t qbase = (r * a->num_q_heads + hq)",
+                          "int64_t qbase = ((int64_t)b * a->num_q_heads + hq)"),
+    # multi-token: query heads interleaved over kv heads
+    "prefill_gqa": ("int kvh = hq / (a->num_q_heads / a->num_kv_heads);",
+                    "int kvh = hq % a->num_kv_heads;"),
+    # multi-token: a row on a sequence boundary given to the previous sequence
+    "prefill_sequence_search": ("while (query_start[b + 1] <= r)",
+                                "while (query_start[b + 1] < r)"),
 }
 
 

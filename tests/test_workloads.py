@@ -72,3 +72,18 @@ def test_half_rounding_is_nearest_even():
     assert list(f16) == [0x3C00, 0x3C02, 0x3C04]
     bf = W._round_to_dtype(np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8], np.float32), "bf16")
     assert list(bf) == [0x3F80, 0x3F82]
+
+
+def test_prefill_workloads_shapes_and_determinism():
+    a, b = W.make_prefill_config(1), W.make_prefill_config(1)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k_cache, b.k_cache)
+    assert a.query_start.tolist() == [0, 7, 8, 28]
+    assert a.context_lens.tolist() == [7, 6, 60]
+    assert a.q.shape == (28, 8, 64) and a.max_query_len == 20
+    w2 = W.make_prefill_config(2, poison=False)
+    assert w2.num_query_tokens == 2048 and (np.diff(w2.query_start) == 256).all()
+    assert (w2.context_lens >= 256).all() and (w2.context_lens <= 3072 + 256).all()
+    # every position of every sequence is backed by a block of the pool
+    for s in range(w2.num_seqs):
+        nblk = -(-int(w2.context_lens[s]) // w2.block_size)
+        assert (w2.block_tables[s, :nblk] >= 0).all()
