@@ -2,15 +2,18 @@
  * pka.h -- C ABI of the paged KV attention library for AMD Instinct MI355X
  * (gfx950).
  *
- * Two operations, both described in the PhotonInfer README (Korean
- * translation):
+ * Operations described in the PhotonInfer README (Korean translation):
  *   - "Technical details > Paged attention": the KV cache is managed in
  *     fixed-size blocks without fragmentation, each sequence keeps its own
  *     cache offsets, and one kernel performs the K/V writes of many
  *     sequences at once  ->  pka_kv_cache_write.
  *   - "Key features > GPU-optimised kernels": batched paged attention over
  *     that block-wise cache, with a numerically stable softmax
- *     ->  pka_paged_attention_decode.
+ *     ->  pka_paged_attention_decode (and, fused with the write of one new
+ *     token per sequence, pka_paged_attention_decode_append).
+ *   - Its multi-token form, for prompts admitted chunk by chunk and for
+ *     drafted tokens ("Continuous batching scheduler", "Roadmap")
+ *     ->  pka_paged_attention_prefill.
  *
  * Conventions (same README, "Modern C++20 architecture": explicit error
  * results instead of exceptions, zero-copy borrowed buffers):
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 1
+#define PKA_ABI_VERSION 2
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -218,6 +221,53 @@ pka_status pka_paged_attention_decode_append(
     int32_t head_dim, int32_t num_blocks, int32_t block_size, float scale, pka_dtype kv_dtype,
     int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
     void *stream);
+
+/*
+ * pka_paged_attention_prefill -- multi-token causal attention over the
+ * block-wise cache: the prefill of a chunk of a prompt, or the check of
+ * several drafted tokens, for a batch of sequences in one launch.  The
+ * PhotonInfer README (Korean translation) schedules requests token by token
+ * ("Continuous batching scheduler": num_computed_tokens) and lists
+ * speculative decoding on its "Roadmap"; the JackerLab "vllm" tag page
+ * ("Speculative Decoding") describes a large model checking several proposed
+ * tokens at once.  Sequence b brings T_b = query_start[b+1] - query_start[b]
+ * new tokens whose K/V are already in the pools (pka_kv_cache_write with
+ * T_b tokens); L_b = context_lens[b] counts the cached tokens including
+ * them, so new token i sits at position p = L_b - T_b + i and
+ *
+ *   out[query_start[b] + i][hq] =
+ *       sum_{t <= p} softmax_t(scale * q[query_start[b] + i][hq] . K_t) V_t.
+ *
+ *   out             device, [num_query_tokens][num_q_heads][head_dim] of
+ *                   out_dtype (F32, or the KV dtype, rounded to nearest
+ *                   even), 16-byte aligned.  Rows of new tokens with p < 0
+ *                   (T_b > L_b: a caller error) are zero.
+ *   q               device, [num_query_tokens][num_q_heads][head_dim] of
+ *                   kv_dtype, 16-byte aligned.
+ *   k_cache, v_cache, block_tables, max_blocks_per_seq, num_blocks,
+ *   block_size, scale: as for pka_paged_attention_decode.
+ *   context_lens    device, int32 [num_seqs]; values are clamped to
+ *                   [0, max_blocks_per_seq * block_size].
+ *   query_start     device, int32 [num_seqs + 1], non-decreasing from 0 to
+ *                   num_query_tokens.  A sequence whose two entries are out
+ *                   of order or out of [0, num_query_tokens] is skipped
+ *                   (its rows are left unwritten).
+ *   max_query_len   host hint: an upper bound of T_b (sizes the grid); <= 0
+ *                   means num_query_tokens.  New tokens past it are not
+ *                   computed.
+ * Supported: kv_dtype in {F16, BF16} (matrix cores; F32 returns
+ * PKA_ERR_UNSUPPORTED); head_dim in {64, 128}; block_size in {16, 32};
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}.  No workspace.
+ */
+pka_status pka_paged_attention_prefill(void *out, pka_dtype out_dtype, const void *q,
+                                       const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, const int32_t *query_start,
+                                       int32_t num_seqs, int32_t num_query_tokens,
+                                       int32_t max_query_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                       int32_t block_size, float scale, pka_dtype kv_dtype,
+                                       void *stream);
 
 /* Static English name of a status code. */
 const char *pka_status_string(pka_status status);

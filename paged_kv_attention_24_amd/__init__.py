@@ -14,6 +14,10 @@ Paged attention" and "Key features > GPU-optimised kernels"):
   paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens,
                          scale, num_kv_heads, block_size)
       batched one-token attention over the block-wise cache.
+  paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens,
+                          query_start, scale, num_kv_heads, block_size)
+      its multi-token causal form (chunked prefill, drafted-token check;
+      "Continuous batching scheduler" and "Roadmap" of the same README).
 
 Pools are [num_blocks, num_kv_heads, block_size, head_dim].
 
@@ -29,6 +33,7 @@ from typing import Optional
 
 __all__ = [
     "PkaError", "kv_cache_write", "paged_attention_decode", "paged_attention_decode_append",
+    "paged_attention_prefill",
     "decode_partition_size",
     "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
 ]
@@ -84,6 +89,10 @@ def load_library():
         P, ctypes.c_int, P, P, P, i64, i64, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
         ctypes.c_float, ctypes.c_int, i32, i32, P, ctypes.c_size_t, P]
     lib.pka_paged_attention_decode_append.restype = ctypes.c_int
+    lib.pka_paged_attention_prefill.argtypes = [
+        P, ctypes.c_int, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
+        ctypes.c_float, ctypes.c_int, P]
+    lib.pka_paged_attention_prefill.restype = ctypes.c_int
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_last_error.argtypes = []
@@ -288,6 +297,59 @@ def paged_attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cach
         _dtype_code(k_cache.dtype), a["hint"], a["P"], a["ws_ptr"], a["ws_bytes"],
         _stream_ptr(q.device)))
     return a["out"]
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                            scale: float, num_kv_heads: int, block_size: int, *, out=None,
+                            out_dtype=None, max_query_len: int = 0):
+    """Multi-token causal attention: q [N, Hq, D] holds the new tokens of all
+    sequences, sequence b owning rows query_start[b] .. query_start[b+1] - 1
+    (int32 [B + 1]); their K/V are already in the pools and context_lens[b]
+    counts them, so new token i of sequence b sits at position
+    context_lens[b] - T_b + i and attends to positions 0 .. that one.
+    max_query_len, an upper bound of T_b, sizes the grid (0: N).  Returns
+    out [N, Hq, D]."""
+    import torch
+
+    _require_gpu(q, k_cache, v_cache, block_tables, context_lens, query_start)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    NB, Hkv, bs, D = k_cache.shape
+    if Hkv != num_kv_heads or bs != block_size:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match num_kv_heads="
+                         f"{num_kv_heads}, block_size={block_size}")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError(f"q must be [N, Hq, {D}]")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    q = q.contiguous()
+    N, Hq, _ = q.shape
+    B = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    if context_lens.dtype != torch.int32 or B < 0:
+        raise ValueError("context_lens must be int32 [B]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks_per_seq]")
+    if query_start.dtype != torch.int32 or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("query_start must be int32 [B + 1]")
+    block_tables = block_tables.contiguous()
+    context_lens = context_lens.contiguous()
+    query_start = query_start.contiguous()
+    if out is None:
+        odt = torch.float32 if out_dtype is None else out_dtype
+        out = torch.empty((N, Hq, D), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (N, Hq, D) or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous [N, Hq, D] tensor on q's device")
+    if B == 0 or N == 0:
+        return out
+    lib = load_library()
+    _check(lib.pka_paged_attention_prefill(
+        out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), query_start.data_ptr(), B, N, int(max_query_len), Hq, Hkv, D,
+        NB, bs, float(scale), _dtype_code(k_cache.dtype), _stream_ptr(q.device)))
+    return out
 
 
 _WORKSPACES = {}

@@ -322,4 +322,71 @@ pka_status pka_paged_attention_decode_append(
                        v_new_token_stride, slot_mapping);
 }
 
+pka_status pka_paged_attention_prefill(void *out, pka_dtype out_dtype, const void *q,
+                                       const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, const int32_t *query_start,
+                                       int32_t num_seqs, int32_t num_query_tokens,
+                                       int32_t max_query_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                       int32_t block_size, float scale, pka_dtype kv_dtype,
+                                       void *stream)
+{
+    if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (out_dtype != PKA_F32 && out_dtype != kv_dtype)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "out dtype must be F32 or the KV dtype");
+    if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "num_seqs, num_query_tokens >= 0 and positive num_q_heads, num_kv_heads, "
+                    "num_blocks, max_blocks_per_seq required");
+    if (num_q_heads % num_kv_heads)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_q_heads %d not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    const int group = num_q_heads / num_kv_heads;
+    if (!pka::prefill_supported(to_internal(kv_dtype), head_dim, block_size, group))
+        return fail(PKA_ERR_UNSUPPORTED,
+                    "multi-token attention needs F16/BF16 KV, head_dim in {64,128}, block_size "
+                    "in {16,32}, group in {1,2,4,8} (got dtype %d, %d, %d, %d)",
+                    (int)kv_dtype, head_dim, block_size, group);
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return fail(PKA_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535");
+    if (!(scale == scale))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (num_seqs == 0 || num_query_tokens == 0)
+        return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "out, q and the caches must be 16-byte aligned");
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        return fail(PKA_ERR_UNSUPPORTED, "context length beyond int32");
+    pka::PrefillArgs a{};
+    a.out = out;
+    a.out_dtype = to_internal(out_dtype);
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.query_start = query_start;
+    a.num_seqs = num_seqs;
+    a.num_query_tokens = num_query_tokens;
+    a.max_query_len =
+        max_query_len > 0 && max_query_len < num_query_tokens ? max_query_len : num_query_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.scale = scale;
+    a.kv_dtype = to_internal(kv_dtype);
+    hipError_t e = pka::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "paged_attention_prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -1,0 +1,393 @@
+// Multi-token causal paged attention for gfx950 (CDNA4): the chunked
+// prefill of a prompt, or the check of drafted tokens.
+//
+// What is computed (PhotonInfer README, Korean translation: "Continuous
+// batching scheduler", where a request advances token by token through
+// num_computed_tokens, and the speculative-decoding item of its "Roadmap";
+// JackerLab "vllm" tag page, "Speculative Decoding": a large model checks
+// several proposed tokens at once).  Sequence b brings T_b new query tokens,
+// rows query_start[b] .. query_start[b+1] - 1 of q, whose K/V are already in
+// the block-wise cache; with L_b = context_lens[b] (those new tokens
+// included), new token i sits at position p = L_b - T_b + i and
+//     out[row, hq, :] = sum_{t <= p} softmax_t(scale * q[row, hq, :] . K_t) V_t.
+//
+// Design.  A workgroup of four wave64s takes one (query block, kv head,
+// sequence).  Its 64 columns are (new token, query head) pairs: G heads of
+// 64 / G consecutive new tokens, 16 columns per wave.  It streams the
+// sequence's K and V from position 0 to the block's last position in chunks
+// (4 KiB of K and of V), which the waves copy by DMA (global_load_lds) into
+// two LDS buffers shared by the workgroup, one chunk ahead.  Per 16-token tile
+// each wave computes
+//   S^T (16 tokens x 16 columns) = K_tile . Q^T        D/32 MFMAs 16x16x32
+//   the online softmax on S^T, with the causal bound t <= p applied per
+//   element by selects,
+//   O^T (16 dims x 16 columns) += V_tile^T . P^T        D/16 MFMAs 16x16x16,
+// the layout of the decode kernel with columns in place of heads.  Every K/V
+// byte a workgroup reads serves 64 columns.  A wave whose columns all end
+// before a chunk skips its arithmetic but keeps staging its share.
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "cdna4.h"
+#include "pka_internal.h"
+
+namespace pka {
+namespace {
+
+struct PrefillParams {
+    void *out;
+    int out_kind;  // 0 f32, 1 f16, 2 bf16
+    const char *q, *k_cache, *v_cache;
+    const int32_t *block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+    const int32_t *query_start;
+    int32_t num_query_tokens, num_q_heads, num_kv_heads, num_blocks;
+    int32_t len_cap;  // max_blocks_per_seq * block_size
+    float scale_log2;  // scale * log2(e)
+};
+
+template <class T, int D, int BS, int G>
+struct PShape {
+    static constexpr int ELT = T::kBytes;
+    static constexpr int LPR = D * ELT / 16;  // lanes per token row
+    static constexpr int TPL = kWave / LPR;   // token rows per 1 KiB wave load
+    static constexpr int NW = 4;              // waves per workgroup
+    static constexpr int NL = NW;             // 1 KiB loads per tensor per chunk: one per wave
+    static constexpr int CT = NL * TPL;       // tokens per chunk
+    static constexpr int TPC = CT / 16;       // 16-token tiles per chunk
+    static constexpr int KS = D / 32;         // 32-dim steps of QK^T
+    static constexpr int MT = D / 16;         // 16-dim tiles of O
+    static constexpr int R = D * ELT;         // bytes per token row
+    static constexpr int CHUNK = NL * 1024;   // bytes of one tensor's chunk
+    static constexpr int TILE = BS * D * ELT; // bytes of one (block, head) tile
+    static constexpr int QB = NW * 16 / G;    // new tokens per workgroup
+    static_assert(TPC >= 1 && CT % 16 == 0, "a chunk holds whole 16-token tiles");
+    static_assert(BS % TPL == 0, "a wave load stays inside one block");
+};
+
+template <class T, int D, int BS, int G>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
+{
+    using S = PShape<T, D, BS, G>;
+    constexpr int LPR = S::LPR, TPL = S::TPL, TPC = S::TPC, KS = S::KS, MT = S::MT, CT = S::CT;
+    constexpr int R = S::R, CHUNK = S::CHUNK;
+    constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the reference max by
+    __shared__ __attribute__((aligned(1024))) char stage[2 * 2 * CHUNK];  // [buffer][K, V]
+
+    const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * S::QB;
+    const int lane = threadIdx.x % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n = lane % 16, quad = lane / 16;
+    const int tg = lane / LPR, cl = lane % LPR;
+
+    // the sequence's new tokens (malformed offsets: nothing to do)
+    const int r0 = __builtin_amdgcn_readfirstlane(p.query_start[b]);
+    const int r1 = __builtin_amdgcn_readfirstlane(p.query_start[b + 1]);
+    if (r0 < 0 || r1 < r0 || r1 > p.num_query_tokens)
+        return;
+    const int nq = r1 - r0;  // new tokens of the sequence
+    if (q0 >= nq)
+        return;
+    int L = __builtin_amdgcn_readfirstlane(p.context_lens[b]);
+    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+    const int base = L - nq;  // position of new token 0
+
+    // this lane's column: new token qi, query head h*G + g, position pos
+    const int col = 16 * w + n;
+    const int qi = q0 + col / G, g = col % G;
+    const bool col_ok = qi < nq && base + qi >= 0;
+    const int pos = base + qi;
+    // last position of the workgroup and of this wave (wave-uniform)
+    const int qlast = (q0 + S::QB < nq ? q0 + S::QB : nq) - 1;
+    const int n_tok = base + qlast + 1;  // tokens the workgroup streams
+    const int wq1 = q0 + (16 * w + 15) / G;
+    const int wave_last = base + (wq1 < nq ? wq1 : nq - 1);
+    const bool wave_any = q0 + (16 * w) / G < nq;
+
+    const int64_t orow = ((int64_t)(r0 + qi) * p.num_q_heads + h * G + g) * D;
+    if (n_tok <= 0) {
+        // no token precedes any of these queries (more new tokens than cached
+        // ones): zero rows
+        if (qi < nq)
+            for (int d = 4 * quad; d < D; d += 16)
+                for (int i = 0; i < 4; ++i)
+                    store_out(p.out, orow + d + i, 0.0f, p.out_kind);
+        return;
+    }
+    const int nch = (n_tok + CT - 1) / CT;
+    const int last_blk = (n_tok - 1) / BS;
+
+    // Softmax on raw dot products scaled by c = |scale| * log2(e) inside the
+    // exponent; a negative scale flips the sign of q instead (exact).
+    const float c = fabsf(p.scale_log2);
+    const uint32_t qflip = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
+
+    // Q^T operand: column n, dims 32 st + 8 quad .. + 7
+    uint4 qop[KS];
+    {
+        // columns without a query read row 0 (in bounds) and are zeroed
+        const char *qrow = p.q + ((col_ok ? orow : 0) + 8 * quad) * S::ELT;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * st * S::ELT);
+            v.x ^= qflip;
+            v.y ^= qflip;
+            v.z ^= qflip;
+            v.w ^= qflip;
+            qop[st] = select4(col_ok, v, make_uint4(0, 0, 0, 0));
+        }
+    }
+
+    // XOR swizzles of a staged row's 16-byte units (physical = logical ^ sw)
+    auto swk = [](int r) { return (D == 64 ? r >> 1 : r) & (LPR - 1); };
+    auto swv = [](int r) { return ((D == 64 ? r >> 1 : r) & (LPR / 2 - 1)) << 1; };
+    uint32_t kofs[TPC][KS], vofs[TPC][MT];
+#pragma unroll
+    for (int t = 0; t < TPC; ++t) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const int r = 16 * t + n, u = quad + 4 * st;
+            kofs[t][st] = r * R + 16 * (u ^ swk(r));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = 16 * t + lane / 4, u = 2 * mt + (lane % 4) / 2;
+            vofs[t][mt] = r * R + 16 * (u ^ swv(r)) + 8 * (lane % 2);
+        }
+    }
+
+    // Block ids: a window of 64 consecutive entries of the block table, one
+    // per lane, read again when a chunk leaves it (ids clamped to the pool).
+    const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+    int win0 = -2 * kWave, ids = 0;  // no window loaded yet
+    auto block_id = [&](int bi) __attribute__((always_inline)) {
+        if (bi < win0 || bi >= win0 + kWave) {  // wave-uniform
+            win0 = bi;
+            const int e = win0 + lane < p.max_blocks_per_seq ? win0 + lane : p.max_blocks_per_seq - 1;
+            const int id = bt[e];
+            ids = id < 0 ? 0 : (id > p.num_blocks - 1 ? p.num_blocks - 1 : id);
+        }
+        return __builtin_amdgcn_readlane(ids, bi - win0);
+    };
+
+    // This wave's share of chunk k: token rows [k CT + w TPL, + TPL) of K
+    // and of V into buffer buf (lane l fills physical unit l % LPR of its row).
+    const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(lds_address(stage));
+    const int64_t head_off = (int64_t)h * S::TILE;
+    const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
+    auto stage_share = [&](int k, int buf) __attribute__((always_inline)) {
+        const int t0 = k * CT + w * TPL;
+        int bi = t0 / BS;
+        bi = bi < last_blk ? bi : last_blk;  // rows past the end re-read the last block
+        const int blk = block_id(bi);
+        const int64_t row = (int64_t)blk * block_stride + head_off + (t0 % BS) * R;
+        const int rr = w * TPL + tg;
+        const uint32_t kd = stage_lds + buf * (2 * CHUNK) + w * 1024;
+        load_to_lds(p.k_cache + row + tg * R + 16 * (cl ^ swk(rr)), kd);
+        load_to_lds(p.v_cache + row + tg * R + 16 * (cl ^ swv(rr)), kd + CHUNK);
+    };
+
+    float4_t O[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        O[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float mref = -INFINITY, lsum = 0.0f;
+
+    stage_share(0, 0);
+    for (int k = 0; k < nch; ++k) {
+        const int buf = k & 1;
+        char *kd = stage + buf * (2 * CHUNK);
+        char *vd = kd + CHUNK;
+        const int tc = k * CT;
+        wait_vmem();  // this wave's share of chunk k is in LDS
+        {
+            // rows at or past L hold stale or NaN slots: zero their V (K is
+            // masked by selects)
+            const int t = tc + w * TPL + tg;
+            if (tc + CT > L && t >= L)
+                *reinterpret_cast<uint4 *>(vd + w * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();  // every share landed; chunk k - 1's buffer is free
+        const bool work = wave_any && tc <= wave_last;
+        uint4 kop[TPC][KS];
+        uint2 vop[TPC][MT];
+        if (work) {
+#pragma unroll
+            for (int t = 0; t < TPC; ++t) {
+#pragma unroll
+                for (int st = 0; st < KS; ++st)
+                    kop[t][st] = *reinterpret_cast<const uint4 *>(kd + kofs[t][st]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    vop[t][mt] = lds_read_tr16(vd + vofs[t][mt]);
+            }
+        }
+        if (k + 1 < nch)
+            stage_share(k + 1, buf ^ 1);
+        if (!work)
+            continue;
+#pragma unroll
+        for (int t = 0; t < TPC; ++t) {
+            float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                sacc = mma_qk(T{}, kop[t][st], qop[st], sacc);
+            const int tok0 = tc + 16 * t + 4 * quad;
+            bool ok[4];
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ok[i] = col_ok && tok0 + i <= pos;
+                sv[i] = ok[i] ? sacc[i] : -INFINITY;
+            }
+            const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            if (__builtin_amdgcn_ballot_w64(mx * c > mref * c + kSlack)) {
+                // new reference: the column's maximum over its four lanes
+                float mh = fmaxf(mx, swz_xor16(mx));
+                mh = fmaxf(mh, xor32(mh));
+                const float mnew = fmaxf(mref, mh);
+                const float corr =
+                    mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mref - mnew) * c);
+                lsum *= corr;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    O[mt] *= corr;
+                mref = mnew;
+            }
+            const float nmc = mref == -INFINITY ? 0.0f : -mref * c;
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pr[i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(sv[i], c, nmc)) : 0.0f;
+            if constexpr (std::is_same<T, TF16>::value) {
+                const half2_t h01 = {(_Float16)pr[0], (_Float16)pr[1]};
+                const half2_t h23 = {(_Float16)pr[2], (_Float16)pr[3]};
+                const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                            __builtin_bit_cast(uint32_t, h23));
+                lsum += ((float)h01.x + (float)h01.y) + ((float)h23.x + (float)h23.y);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    O[mt] = mma_pv(T{}, vop[t][mt], ph, O[mt]);
+            } else {
+                // P as a bf16 hi + lo pair: 16 significant bits
+                const bf162_t h01 = {(__bf16)pr[0], (__bf16)pr[1]};
+                const bf162_t h23 = {(__bf16)pr[2], (__bf16)pr[3]};
+                const bf162_t l01 = {(__bf16)(pr[0] - (float)h01.x), (__bf16)(pr[1] - (float)h01.y)};
+                const bf162_t l23 = {(__bf16)(pr[2] - (float)h23.x), (__bf16)(pr[3] - (float)h23.y)};
+                const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                            __builtin_bit_cast(uint32_t, h23));
+                const uint2 pl = make_uint2(__builtin_bit_cast(uint32_t, l01),
+                                            __builtin_bit_cast(uint32_t, l23));
+                lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    O[mt] = mma_pv(T{}, vop[t][mt], ph, O[mt]);
+                    O[mt] = mma_pv(T{}, vop[t][mt], pl, O[mt]);
+                }
+            }
+        }
+    }
+
+    // the column's sum over its four lanes, then the normalised row: lane
+    // holds dims 16 mt + 4 quad + i of its column
+    float lh = lsum + swz_xor16(lsum);
+    lh += xor32(lh);
+    if (qi < nq) {
+        const float inv = col_ok && lh > 0.0f ? 1.0f / lh : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int64_t o = orow + 16 * mt + 4 * quad;
+            if (p.out_kind == 0) {
+                *reinterpret_cast<float4_t *>(static_cast<float *>(p.out) + o) = O[mt] * inv;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    store_out(p.out, o + i, O[mt][i] * inv, p.out_kind);
+            }
+        }
+    }
+}
+
+template <class T, int D, int BS, int G>
+hipError_t launch_prefill_typed(const PrefillArgs &a, hipStream_t stream)
+{
+    using S = PShape<T, D, BS, G>;
+    PrefillParams p;
+    p.out = a.out;
+    p.out_kind = (int)a.out_dtype;
+    p.q = static_cast<const char *>(a.q);
+    p.k_cache = static_cast<const char *>(a.k_cache);
+    p.v_cache = static_cast<const char *>(a.v_cache);
+    p.block_tables = a.block_tables;
+    p.max_blocks_per_seq = a.max_blocks_per_seq;
+    p.context_lens = a.context_lens;
+    p.query_start = a.query_start;
+    p.num_query_tokens = a.num_query_tokens;
+    p.num_q_heads = a.num_q_heads;
+    p.num_kv_heads = a.num_kv_heads;
+    p.num_blocks = a.num_blocks;
+    const int64_t cap = (int64_t)a.max_blocks_per_seq * BS;
+    p.len_cap = (int32_t)(cap > INT32_MAX ? INT32_MAX : cap);
+    p.scale_log2 = a.scale * kLog2e;
+    const dim3 grid((unsigned)((a.max_query_len + S::QB - 1) / S::QB), (unsigned)a.num_kv_heads,
+                    (unsigned)a.num_seqs);
+    hipLaunchKernelGGL((prefill_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <class T, int D, int BS>
+hipError_t prefill_group(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_prefill_typed<T, D, BS, 1>(a, s);
+    case 2: return launch_prefill_typed<T, D, BS, 2>(a, s);
+    case 4: return launch_prefill_typed<T, D, BS, 4>(a, s);
+    case 8: return launch_prefill_typed<T, D, BS, 8>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T, int D>
+hipError_t prefill_block(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.block_size) {
+    case 16: return prefill_group<T, D, 16>(a, s);
+    case 32: return prefill_group<T, D, 32>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t prefill_dim(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.head_dim) {
+    case 64: return prefill_block<T, 64>(a, s);
+    case 128: return prefill_block<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool prefill_supported(DType kv, int head_dim, int block_size, int group)
+{
+    return kv != DType::F32 && (head_dim == 64 || head_dim == 128) &&
+           (block_size == 16 || block_size == 32) &&
+           (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream)
+{
+    if (a.num_seqs == 0 || a.num_query_tokens == 0 || a.max_query_len == 0)
+        return hipSuccess;
+    switch (a.kv_dtype) {
+    case DType::F16: return prefill_dim<TF16>(a, stream);
+    case DType::BF16: return prefill_dim<TBF16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pka

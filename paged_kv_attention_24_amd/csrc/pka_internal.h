@@ -90,4 +90,23 @@ constexpr int kMaxPartition = 1024;
 
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 
+// Multi-token causal paged attention (chunked prefill, drafted-token check).
+struct PrefillArgs {
+    void *out;
+    DType out_dtype;
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+    const int32_t *query_start;  // [num_seqs + 1], device
+    int32_t num_seqs, num_query_tokens, max_query_len;
+    int32_t num_q_heads, num_kv_heads, head_dim;
+    int32_t num_blocks, block_size;
+    float scale;
+    DType kv_dtype;
+};
+
+bool prefill_supported(DType kv, int head_dim, int block_size, int group);
+hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
+
 }  // namespace pka

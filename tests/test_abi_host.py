@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strings():
     lib = pka.load_library()
-    assert lib.pka_abi_version() == 1
+    assert lib.pka_abi_version() == 2
     assert lib.pka_status_string(0) == b"ok"
     assert lib.pka_status_string(3) == b"workspace too small"
     assert lib.pka_status_string(99) == b"unknown status"
@@ -157,3 +157,33 @@ def test_append_rejects(over, status):
     st, msg = append(**over)
     assert st == status, (over, st, msg)
     assert msg
+
+
+def prefill(**over):
+    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=64, cl=FAKE, qs=FAKE, B=8,
+             N=2048, maxq=256, Hq=32, Hkv=8, D=64, NB=1000, bs=16, scale=0.125, kdt=1)
+    a.update(over)
+    lib = pka.load_library()
+    st = lib.pka_paged_attention_prefill(a["out"], a["odt"], a["q"], a["kc"], a["vc"], a["bt"],
+                                         a["MB"], a["cl"], a["qs"], a["B"], a["N"], a["maxq"],
+                                         a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], a["scale"],
+                                         a["kdt"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kdt=0), 2), (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1),
+    (dict(NB=0), 1), (dict(MB=0), 1), (dict(B=-1), 1), (dict(N=-1), 1), (dict(D=96), 2),
+    (dict(bs=8), 2), (dict(Hq=128), 2), (dict(scale=float("nan")), 1), (dict(q=None), 1),
+    (dict(qs=None), 1), (dict(cl=None), 1), (dict(out=FAKE + 4), 1), (dict(kc=FAKE + 8), 1),
+    (dict(B=70000), 2),
+])
+def test_prefill_rejects(over, status):
+    st, msg = prefill(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+def test_prefill_empty_is_ok_without_launch():
+    assert prefill(B=0, out=None, q=None)[0] == 0
+    assert prefill(N=0, out=None, q=None)[0] == 0
