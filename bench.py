@@ -43,8 +43,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--path", default="decode", choices=["decode", "prefill"],
+                    help="decode step (the headline) or multi-token causal attention")
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
-                    help="workload (2 = Llama-3.2-1B batch 16, the headline)")
+                    help="workload (decode: 2 = Llama-3.2-1B batch 16, the headline; "
+                         "prefill: 2 = chunked prefill, 3 = drafted-token check)")
     ap.add_argument("--layers", type=int, default=0,
                     help="pools per step (default: 16 for workload 2, else enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -63,14 +66,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic(tag):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary profiles/<tag>.md, or None when the kernel source has changed
-    since the counters were taken (or no summary exists)."""
+# the sources that define each kernel (hashed to tell whether a committed
+# counter summary still describes it)
+KERNEL_SOURCES = {"decode": ("paged_decode.hip", "cdna4.h"),
+                  "prefill": ("paged_prefill.hip", "cdna4.h")}
+
+
+def kernel_source_sha(path_kind):
     import hashlib
 
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[path_kind]:
+        h.update(open(os.path.join(HERE, "paged_kv_attention_24_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(tag, path_kind="decode"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<tag>.md, or None when the kernel's sources have changed since
+    the counters were taken (or no summary exists)."""
     path = os.path.join(HERE, "profiles", f"{tag}.md")
-    src = os.path.join(HERE, "paged_kv_attention_24_amd", "csrc", "paged_decode.hip")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -78,7 +93,7 @@ def measured_traffic(tag):
         if ":" in line:
             k, _, v = line.partition(":")
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = kernel_source_sha(path_kind)
     if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -116,6 +131,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pka.load_library()
+    if args.path == "prefill":
+        return run_prefill(args, dev)
 
     cfg = args.config
     host_pools = cfg in (2, 3)
@@ -300,12 +317,183 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(PROFILE_TAGS[cfg]),
+            "traffic": measured_traffic(PROFILE_TAGS[cfg], "decode"),
             "traffic_source": f"profiles/{PROFILE_TAGS[cfg]}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                               "copy-calibrated; null when the kernel changed since)",
             "us_per_launch": round(us_launch, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+PREFILL_TAGS = {2: "paged_prefill_chunked_b8", 3: "paged_prefill_drafted_b64"}
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix throughput, vendor specification
+
+
+def timed_calls(fn, n, warmup, use_graph):
+    """ms per call of fn: HIP-graph replay (or eager calls) bracketed by
+    events on the current stream, after warmup calls."""
+    import torch
+
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        run = g.replay
+    else:
+        run = fn
+    for _ in range(max(1, warmup)):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def run_prefill(args, dev):
+    """Multi-token causal attention: workload 2 (chunked prefill, matrix-core
+    bound) or 3 (drafted-token check, HBM bound), over enough layer pools to
+    exceed 1 GB, one launch per layer."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+    from paged_kv_attention_24_amd import workloads as W
+
+    n = args.config if args.config in (2, 3) else 2
+    wl = W.make_prefill_config(n, poison=False, pools=False)
+    tdt = W.torch_dtype(wl.dtype)
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    pool_bytes = 2 * wl.num_blocks * Hkv * bs * D * wl.elt_bytes
+    R = args.layers if args.layers > 0 else max(1, int(np.ceil(1.0e9 / pool_bytes)))
+    log(f"multi-token workload {n}: {wl.meta['description']}; pools per step {R} "
+        f"({R * pool_bytes / 1e6:.0f} MB)")
+    shape = (wl.num_blocks, Hkv, bs, D)
+    kcs = [fill_pool(shape, tdt, 2000 + 2 * r, dev) for r in range(R)]
+    vcs = [fill_pool(shape, tdt, 2001 + 2 * r, dev) for r in range(R)]
+    q = W.as_torch(wl.q, wl.dtype, dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    qs = torch.from_numpy(wl.query_start).to(dev)
+    N = wl.num_query_tokens
+    outs = [torch.empty((N, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def step():
+        for r in range(R):
+            pka.paged_attention_prefill(q, kcs[r], vcs[r], bt, cl, qs, float(wl.scale), Hkv, bs,
+                                        out=outs[r], max_query_len=wl.max_query_len)
+
+    if args.calibration_copy_mib > 0:
+        src_c = torch.ones(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+    step()
+    torch.cuda.synchronize()
+    ms = timed_calls(step, args.steps, args.warmup, not args.eager)
+    us_layer = ms * 1e3 / R
+
+    # per (new token, query head): 2 D flops for each score and 2 D for each
+    # weighted value, over the pos + 1 visible tokens
+    T = np.diff(wl.query_start).astype(np.int64)
+    L = wl.context_lens.astype(np.int64)
+    visible = sum(int(np.sum(L[b] - T[b] + np.arange(T[b]) + 1)) for b in range(B))
+    flops = 4.0 * D * Hq * visible
+    kv_bytes = int(L.sum()) * 2 * Hkv * D * wl.elt_bytes
+    nblk = int(np.sum((L + bs - 1) // bs))
+    alg_bytes = kv_bytes + N * Hq * D * (wl.elt_bytes + 4) + nblk * 4 + B * 4 + (B + 1) * 4
+    tflops = flops / (us_layer * 1e-6) / 1e12
+    gbps = alg_bytes / (us_layer * 1e-6) / 1e9
+    mfma_bound = flops / alg_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        metric = "multi-token paged attention TFLOP/s (chunked prefill)"
+        value, unit = tflops, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4)}
+    else:
+        metric = "multi-token paged attention effective GB/s (drafted-token check)"
+        value, unit = gbps, "GB/s"
+        roof = {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    roof.update({
+        "traffic": measured_traffic(PREFILL_TAGS[n], "prefill"),
+        "traffic_source": f"profiles/{PREFILL_TAGS[n]}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                          "copy-calibrated; null when the kernel changed since)",
+        "kernel": "prefill_kernel (one launch per layer)",
+        "us_per_launch": round(us_layer, 3),
+        "algorithmic_bytes_per_launch": int(alg_bytes),
+        "flops_per_launch": int(flops),
+    })
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+        kc_h = W.to_numpy_bits(kcs[0], wl.dtype)  # the first layer pool, on the host
+        vc_h = W.to_numpy_bits(vcs[0], wl.dtype)
+        rng = np.random.default_rng(0)
+        rows = np.stack([rng.integers(0, N, 256), rng.integers(0, Hq, 256)], 1).astype(np.int32)
+        row_b = np.searchsorted(wl.query_start, rows[:, 0], side="right") - 1
+        pos = L[row_b] - T[row_b] + (rows[:, 0] - wl.query_start[row_b])
+        s_flops = 4.0 * D * float(np.sum(pos + 1))
+        s_bytes = float(np.sum(pos + 1)) * 2 * D * wl.elt_bytes
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention_prefill(wl.q, kc_h, vc_h, wl.block_tables, wl.context_lens,
+                                           wl.query_start, wl.scale, Hkv, bs, wl.dtype,
+                                           rows=rows, threads=threads)
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n_done >= 512:
+                break
+        cpu_value = (s_flops * n_done / el / 1e12) if mfma_bound else (s_bytes * n_done / el / 1e9)
+        cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": threads, "kind": "oracle",
+               "sample": f"256 random (new token, query head) rows of the workload, repeated "
+                         f"{n_done}x in {el:.1f} s; fp64 C oracle, OpenMP"}
+
+    line = {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) KV/q, shuffled block pool)",
+        "config": {
+            "workload": wl.meta["description"],
+            "global_batch": B,
+            "new_tokens": N,
+            "layers_per_step": R,
+            "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+            "kv_dtype": wl.dtype, "accumulate": "f32", "out_dtype": "f32",
+            "sum_context_tokens": int(L.sum()),
+            "timing": "hip-graph replay" if not args.eager else "eager",
+            "parallelism": "single GPU",
+        },
+        "us_per_layer": round(us_layer, 3),
+        "tflops": round(tflops, 3),
+        "effective_gbps": round(gbps, 2),
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

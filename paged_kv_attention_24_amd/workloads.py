@@ -341,8 +341,8 @@ PREFILL_NAMES = {
 }
 
 
-def make_prefill_config(n: int, *, seed: Optional[int] = None,
-                        poison: bool = True) -> PrefillWorkload:
+def make_prefill_config(n: int, *, seed: Optional[int] = None, poison: bool = True,
+                        pools: bool = True) -> PrefillWorkload:
     """Named multi-token workload n (1..3); seed defaults to 100 + n.  Step 1
     of the draw order is the cached lengths (the new-token counts are fixed)."""
     seed = 100 + n if seed is None else seed
@@ -360,7 +360,7 @@ def make_prefill_config(n: int, *, seed: Optional[int] = None,
     else:
         raise ValueError(f"no multi-token workload {n}")
     wl = make_prefill_case(seed, prefix_lens=pre, query_lens=new, poison=poison, rng=rng,
-                           name=f"prefill{n}", **shape)
+                           name=f"prefill{n}", pools=pools, **shape)
     wl.meta["description"] = PREFILL_NAMES[n]
     return wl
 
