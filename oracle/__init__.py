@@ -89,6 +89,12 @@ def _declare(h):
         P, P, P, P, ctypes.c_int, P, i32, P, P, i32, i32, i32, i32, i32, i32, f64, P, i32, i32]
     h.oracle_paged_attention_prefill.restype = ctypes.c_int
     h.oracle_kv_cache_write.argtypes = [P, P, i64, i64, P, i32, P, P, i32, i32, i32, i32, i32]
+    h.oracle_copy_blocks.argtypes = [P, P, P, i32, i32, i64]
+    h.oracle_copy_blocks.restype = ctypes.c_int
+    h.oracle_gather_blocks.argtypes = [P, P, P, P, i32, i32, i64]
+    h.oracle_gather_blocks.restype = ctypes.c_int
+    h.oracle_scatter_blocks.argtypes = [P, P, P, P, i32, i32, i64]
+    h.oracle_scatter_blocks.restype = ctypes.c_int
     h.oracle_kv_cache_write.restype = ctypes.c_int
     return h
 
@@ -279,3 +285,56 @@ def decode_workload(wl, *, rows=None, partition_size=0, threads=0, after_write=T
         wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, wl.num_kv_heads,
         wl.block_size, wl.dtype, rows=rows, partition_size=partition_size,
         threads=threads, handle=handle)
+
+
+# ---------------------------------------------------------------------------
+# block movement (preemption, GPU <-> CPU paging): bit copies of whole blocks
+# ---------------------------------------------------------------------------
+
+def _pools(k_cache, v_cache):
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("K and V pools must match")
+    if not (k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]):
+        raise ValueError("pools must be C-contiguous")
+    nb = k_cache.shape[0]
+    return nb, k_cache.nbytes // nb
+
+
+def copy_blocks(k_cache, v_cache, pairs, handle=None) -> None:
+    """In place: for each (src, dst) row of pairs (int64 [n, 2]) block dst of
+    both pools becomes a copy of block src, all sources read first."""
+    h = handle or lib()
+    nb, bb = _pools(k_cache, v_cache)
+    pr = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    rc = h.oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pr), pr.shape[0], nb, bb)
+    if rc != 0:
+        raise OracleError(f"oracle copy_blocks failed: {STATUS.get(rc, rc)}")
+
+
+def gather_blocks(k_cache, v_cache, ids, handle=None) -> np.ndarray:
+    """[n, 2, block_bytes] uint8: K then V bytes of blocks ids (int64 [n]);
+    rows of invalid ids are zero."""
+    h = handle or lib()
+    nb, bb = _pools(k_cache, v_cache)
+    ix = np.ascontiguousarray(ids, dtype=np.int64)
+    out = np.zeros((ix.shape[0], 2, bb), dtype=np.uint8)
+    rc = h.oracle_gather_blocks(_ptr(out), _ptr(k_cache), _ptr(v_cache), _ptr(ix), ix.shape[0],
+                                nb, bb)
+    if rc != 0:
+        raise OracleError(f"oracle gather_blocks failed: {STATUS.get(rc, rc)}")
+    return out
+
+
+def scatter_blocks(k_cache, v_cache, packed, ids, handle=None) -> None:
+    """In place: blocks ids (int64 [n]) of the pools take packed [n, 2,
+    block_bytes] (K then V)."""
+    h = handle or lib()
+    nb, bb = _pools(k_cache, v_cache)
+    ix = np.ascontiguousarray(ids, dtype=np.int64)
+    pk = np.ascontiguousarray(packed, dtype=np.uint8)
+    if pk.shape != (ix.shape[0], 2, bb):
+        raise ValueError("packed must be [n, 2, block_bytes]")
+    rc = h.oracle_scatter_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pk), _ptr(ix), ix.shape[0],
+                                 nb, bb)
+    if rc != 0:
+        raise OracleError(f"oracle scatter_blocks failed: {STATUS.get(rc, rc)}")

@@ -483,3 +483,79 @@ int oracle_kv_cache_write(const void *k, const void *v, int64_t k_token_stride,
     }
     return ORACLE_OK;
 }
+
+/*
+ * Block movement for preemption and paging (PhotonInfer README, Korean
+ * translation, "Continuous batching scheduler": requests can be PREEMPTED;
+ * JackerLab "vllm" tag page, PagedAttention: KV pages move between GPU and
+ * CPU memory).  A block is the contiguous run of block_bytes bytes that one
+ * physical block holds in a pool ([num_blocks][num_kv_heads][block_size]
+ * [head_dim], so block_bytes = num_kv_heads * block_size * head_dim * elt).
+ * All three are bit copies; an id outside [0, num_blocks) skips its entry.
+ */
+
+/* For each pair i: block pairs[2i+1] of both pools becomes a copy of block
+ * pairs[2i] (read before anything is written: sources and destinations
+ * are taken from a snapshot of the pools). */
+int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int32_t num_pairs,
+                       int32_t num_blocks, int64_t block_bytes)
+{
+    if (num_pairs < 0 || num_blocks <= 0 || block_bytes <= 0)
+        return ORACLE_BAD_ARGUMENT;
+    if (num_pairs == 0)
+        return ORACLE_OK;
+    size_t pool = (size_t)num_blocks * (size_t)block_bytes;
+    char *ks = (char *)malloc(pool), *vs = (char *)malloc(pool);
+    if (!ks || !vs) {
+        free(ks);
+        free(vs);
+        return ORACLE_NO_MEMORY;
+    }
+    memcpy(ks, k_cache, pool);
+    memcpy(vs, v_cache, pool);
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks)
+            continue;
+        memcpy((char *)k_cache + dst * block_bytes, ks + src * block_bytes, (size_t)block_bytes);
+        memcpy((char *)v_cache + dst * block_bytes, vs + src * block_bytes, (size_t)block_bytes);
+    }
+    free(ks);
+    free(vs);
+    return ORACLE_OK;
+}
+
+/* packed[i] = (K block ids[i], V block ids[i]): [n][2][block_bytes]; an
+ * entry with an invalid id is left as it was. */
+int oracle_gather_blocks(void *packed, const void *k_cache, const void *v_cache,
+                         const int64_t *ids, int32_t n, int32_t num_blocks, int64_t block_bytes)
+{
+    if (n < 0 || num_blocks <= 0 || block_bytes <= 0)
+        return ORACLE_BAD_ARGUMENT;
+    for (int32_t i = 0; i < n; ++i) {
+        int64_t id = ids[i];
+        if (id < 0 || id >= num_blocks)
+            continue;
+        char *row = (char *)packed + (int64_t)i * 2 * block_bytes;
+        memcpy(row, (const char *)k_cache + id * block_bytes, (size_t)block_bytes);
+        memcpy(row + block_bytes, (const char *)v_cache + id * block_bytes, (size_t)block_bytes);
+    }
+    return ORACLE_OK;
+}
+
+/* The inverse: block ids[i] of the K and V pools take packed[i]. */
+int oracle_scatter_blocks(void *k_cache, void *v_cache, const void *packed, const int64_t *ids,
+                          int32_t n, int32_t num_blocks, int64_t block_bytes)
+{
+    if (n < 0 || num_blocks <= 0 || block_bytes <= 0)
+        return ORACLE_BAD_ARGUMENT;
+    for (int32_t i = 0; i < n; ++i) {
+        int64_t id = ids[i];
+        if (id < 0 || id >= num_blocks)
+            continue;
+        const char *row = (const char *)packed + (int64_t)i * 2 * block_bytes;
+        memcpy((char *)k_cache + id * block_bytes, row, (size_t)block_bytes);
+        memcpy((char *)v_cache + id * block_bytes, row + block_bytes, (size_t)block_bytes);
+    }
+    return ORACLE_OK;
+}

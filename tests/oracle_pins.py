@@ -441,6 +441,73 @@ def pin_prefill_fresh_sequence(h):
             assert np.max(np.abs(got[i, hq] - V[: i + 1, hq // 2].mean(axis=0))) <= 1e-12
 
 
+# ---------------------------------------------------------------------------
+# block movement (preemption, paging)
+# ---------------------------------------------------------------------------
+
+def _pool_pair(seed, nb=12, hkv=2, bs=16, d=64, dtype=np.uint16):
+    rng = np.random.default_rng(seed)
+    k = rng.integers(0, 1 << 16, size=(nb, hkv, bs, d)).astype(dtype)
+    v = rng.integers(0, 1 << 16, size=(nb, hkv, bs, d)).astype(dtype)
+    return k, v
+
+
+def pin_copy_blocks(h):
+    """P-q: block copies equal numpy's indexed assignment from a snapshot
+    (a chain src -> dst -> dst2 copies the original), invalid ids are
+    skipped and every other block keeps its bytes."""
+    k, v = _pool_pair(40)
+    pairs = np.array([[1, 4], [4, 7], [0, 2], [9, -1], [30, 3], [5, 5]], dtype=np.int64)
+    k0, v0 = k.copy(), v.copy()
+    oracle.copy_blocks(k, v, pairs, handle=h)
+    ek, ev = k0.copy(), v0.copy()
+    ok = (pairs >= 0).all(1) & (pairs < k.shape[0]).all(1)
+    ek[pairs[ok, 1]] = k0[pairs[ok, 0]]
+    ev[pairs[ok, 1]] = v0[pairs[ok, 0]]
+    assert k.tobytes() == ek.tobytes() and v.tobytes() == ev.tobytes()
+    assert not np.array_equal(k[7], k0[1])  # the chain copied the snapshot of block 4
+    assert np.array_equal(k[7], k0[4])
+
+
+def pin_gather_scatter(h):
+    """P-r: gathered rows are the blocks' bytes (K then V, numpy view);
+    scattering them into a zero pool at the same ids restores exactly those
+    blocks and leaves the rest zero."""
+    k, v = _pool_pair(41, dtype=np.float32)
+    ids = np.array([3, 0, 11, 3, 50], dtype=np.int64)
+    packed = oracle.gather_blocks(k, v, ids, handle=h)
+    bb = k[0].nbytes
+    for i, b in enumerate(ids):
+        if b < k.shape[0]:
+            assert packed[i, 0].tobytes() == k[b].tobytes()
+            assert packed[i, 1].tobytes() == v[b].tobytes()
+        else:
+            assert not packed[i].any()
+    zk, zv = np.zeros_like(k), np.zeros_like(v)
+    oracle.scatter_blocks(zk, zv, packed[:3], ids[:3], handle=h)
+    for b in range(k.shape[0]):
+        if b in (3, 0, 11):
+            assert zk[b].tobytes() == k[b].tobytes() and zv[b].tobytes() == v[b].tobytes()
+        else:
+            assert not zk[b].any() and not zv[b].any()
+    assert packed.shape == (5, 2, bb)
+
+
+def pin_moved_blocks_decode_unchanged(h):
+    """P-s: moving a sequence's blocks elsewhere (gather, scatter into free
+    blocks, table rewritten) leaves its decode bit for bit unchanged: a
+    block is exactly the pool's [Hkv][bs][D] slab."""
+    wl = small_case(42, dtype="bf16", lens=(40, 9), Hq=8, Hkv=2, write=False, pool_blocks=12)
+    before = run(h, wl)
+    used = wl.block_tables[wl.block_tables >= 0]
+    free = np.setdiff1d(np.arange(wl.num_blocks), used)[: len(used)]
+    packed = oracle.gather_blocks(wl.k_cache, wl.v_cache, used.astype(np.int64), handle=h)
+    oracle.scatter_blocks(wl.k_cache, wl.v_cache, packed, free.astype(np.int64), handle=h)
+    remap = dict(zip(used.tolist(), free.tolist()))
+    wl.block_tables = np.vectorize(lambda x: remap.get(int(x), -1))(wl.block_tables).astype(np.int32)
+    assert np.array_equal(run(h, wl), before)
+
+
 PINS = {
     "append_equals_write_then_decode": pin_append_equals_write_then_decode,
     "decoders_exhaustive": pin_decoders_exhaustive,
@@ -460,4 +527,7 @@ PINS = {
     "prefill_one_token_is_decode": pin_prefill_one_token_is_decode,
     "prefill_causality": pin_prefill_causality,
     "prefill_fresh_sequence": pin_prefill_fresh_sequence,
+    "copy_blocks": pin_copy_blocks,
+    "gather_scatter": pin_gather_scatter,
+    "moved_blocks_decode_unchanged": pin_moved_blocks_decode_unchanged,
 }

@@ -62,6 +62,18 @@ MUTANTS = {
     # multi-token: a row on a sequence boundary given to the previous sequence
     "prefill_sequence_search": ("while (query_start[b + 1] <= r)",
                                 "while (query_start[b + 1] < r)"),
+    # block copy: V taken from the K snapshot
+    "copy_v_from_k": ("memcpy((char *)v_cache + dst * block_bytes, vs + src * block_bytes",
+                      "memcpy((char *)v_cache + dst * block_bytes, ks + src * block_bytes"),
+    # block copy: sources read from the live pools (a chain copies twice)
+    "copy_no_snapshot": ("memcpy((char *)k_cache + dst * block_bytes, ks + src * block_bytes",
+                         "memcpy((char *)k_cache + dst * block_bytes, (char *)k_cache + src * block_bytes"),
+    # gather: the K half of a packed row taken from the V pool
+    "gather_k_from_v": ("memcpy(row, (const char *)k_cache + id * block_bytes",
+                        "memcpy(row, (const char *)v_cache + id * block_bytes"),
+    # scatter: K restored from the V half of the packed row
+    "scatter_k_offset": ("memcpy((char *)k_cache + id * block_bytes, row, ",
+                         "memcpy((char *)k_cache + id * block_bytes, row + block_bytes, "),
 }
 
 
