@@ -43,8 +43,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--path", default="decode", choices=["decode", "prefill"],
-                    help="decode step (the headline) or multi-token causal attention")
+    ap.add_argument("--path", default="decode", choices=["decode", "prefill", "blocks"],
+                    help="decode step (the headline), multi-token causal attention, or "
+                         "whole-block moves (preemption, paging)")
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
                     help="workload (decode: 2 = Llama-3.2-1B batch 16, the headline; "
                          "prefill: 2 = chunked prefill, 3 = drafted-token check)")
@@ -69,7 +70,8 @@ def log(msg):
 # the sources that define each kernel (hashed to tell whether a committed
 # counter summary still describes it)
 KERNEL_SOURCES = {"decode": ("paged_decode.hip", "cdna4.h"),
-                  "prefill": ("paged_prefill.hip", "cdna4.h")}
+                  "prefill": ("paged_prefill.hip", "cdna4.h"),
+                  "blocks": ("block_ops.hip",)}
 
 
 def kernel_source_sha(path_kind):
@@ -133,6 +135,8 @@ def main():
     pka.load_library()
     if args.path == "prefill":
         return run_prefill(args, dev)
+    if args.path == "blocks":
+        return run_blocks(args, dev)
 
     cfg = args.config
     host_pools = cfg in (2, 3)
@@ -498,6 +502,120 @@ def run_prefill(args, dev):
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+BLOCKS_TAG = "block_moves_llama3_1b"
+
+
+def run_blocks(args, dev):
+    """Whole-block moves on the Llama-3.2-1B layer shape (8 kv heads, block
+    16, head_dim 64, fp16: 16 KiB per block per pool) in pools of 16384
+    blocks: copy 4096 random disjoint (src, dst) pairs per launch (HBM
+    roofline: read + write of both pools' blocks); gather, scatter and the
+    swaps through pinned host memory are timed beside it."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+
+    NB, H, BS, D, n = 16384, 8, 16, 64, 4096
+    shape = (NB, H, BS, D)
+    kc = fill_pool(shape, torch.float16, 3000, dev)
+    vc = fill_pool(shape, torch.float16, 3001, dev)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(NB)
+    pairs_h = np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)
+    pairs = torch.from_numpy(pairs_h).to(dev)
+    ids = torch.from_numpy(perm[:n].astype(np.int64)).to(dev)
+    dst_ids = torch.from_numpy(perm[2 * n:3 * n].astype(np.int64)).to(dev)
+    bb = H * BS * D * 2
+    packed = torch.empty((n, 2, bb), dtype=torch.uint8, device=dev)
+    host = torch.empty((n, 2, bb), dtype=torch.uint8, pin_memory=True)
+    moved = 2 * n * bb  # bytes of blocks moved per launch (K and V)
+    if args.calibration_copy_mib > 0:
+        src_c = torch.ones(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+    use_graph = not args.eager
+    ms_copy = timed_calls(lambda: pka.copy_blocks(kc, vc, pairs), args.steps, args.warmup, use_graph)
+    ms_gather = timed_calls(lambda: pka.gather_blocks(kc, vc, ids, out=packed), args.steps,
+                            args.warmup, use_graph)
+    ms_scatter = timed_calls(lambda: pka.scatter_blocks(kc, vc, packed, dst_ids), args.steps,
+                             args.warmup, use_graph)
+    ms_out = timed_calls(lambda: pka.swap_out(kc, vc, ids, host=host), max(3, args.steps // 5),
+                         2, False)
+    ms_in = timed_calls(lambda: pka.swap_in(kc, vc, host, dst_ids), max(3, args.steps // 5), 2,
+                        False)
+    gbps = lambda ms, factor: factor * moved / (ms * 1e-3) / 1e9  # noqa: E731
+    copy_gbps = gbps(ms_copy, 2)  # read + write
+    alg = 2 * moved + n * 16      # blocks read and written, plus the (src, dst) pairs
+    achieved = alg / (ms_copy * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        kh = W_to_bits(kc)
+        vh = W_to_bits(vc)
+        m = 512  # a sample of the pairs
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.copy_blocks(kh, vh, pairs_h[:m])
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n_done >= 64:
+                break
+        cpu = {"value": round(2 * 2 * m * bb * n_done / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"copy of {m} of the {n} pairs (the oracle snapshots both 512 MiB pools "
+                         f"first), repeated {n_done}x in {el:.1f} s; single-threaded C"}
+
+    line = {
+        "metric": "paged KV block copy GB/s (read + write)",
+        "value": round(copy_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_copy, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (device-random pools, random disjoint block pairs)",
+        "config": {
+            "workload": f"block moves, Llama-3.2-1B layer pools: {NB} blocks of 8 kv heads x 16 "
+                        f"x 64 fp16 (16 KiB per pool), {n} blocks per launch",
+            "global_batch": n, "block_bytes_per_pool": bb,
+            "timing": "hip-graph replay" if use_graph else "eager",
+            "parallelism": "single GPU",
+        },
+        "us_copy": round(ms_copy * 1e3, 2),
+        "gather_gbps": round(gbps(ms_gather, 2), 2),
+        "scatter_gbps": round(gbps(ms_scatter, 2), 2),
+        "swap_out_gbps_pcie_inclusive": round(gbps(ms_out, 1), 2),
+        "swap_in_gbps_pcie_inclusive": round(gbps(ms_in, 1), 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(BLOCKS_TAG, "blocks"),
+            "traffic_source": f"profiles/{BLOCKS_TAG}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                              "copy-calibrated; null when the kernel changed since)",
+            "kernel": "move_blocks_kernel (copy mode, one launch)",
+            "us_per_launch": round(ms_copy * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(alg),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def W_to_bits(t):
+    from paged_kv_attention_24_amd import workloads as W
+
+    return W.to_numpy_bits(t, "f16")
 
 
 if __name__ == "__main__":

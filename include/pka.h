@@ -14,6 +14,8 @@
  *   - Its multi-token form, for prompts admitted chunk by chunk and for
  *     drafted tokens ("Continuous batching scheduler", "Roadmap")
  *     ->  pka_paged_attention_prefill.
+ *   - Block movement for preempted requests and paging
+ *     ->  pka_copy_blocks, pka_gather_blocks, pka_scatter_blocks.
  *
  * Conventions (same README, "Modern C++20 architecture": explicit error
  * results instead of exceptions, zero-copy borrowed buffers):
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 2
+#define PKA_ABI_VERSION 3
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -268,6 +270,39 @@ pka_status pka_paged_attention_prefill(void *out, pka_dtype out_dtype, const voi
                                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                                        int32_t block_size, float scale, pka_dtype kv_dtype,
                                        void *stream);
+
+/*
+ * Whole-block movement for preemption and paging between GPU and CPU memory
+ * (PhotonInfer README, Korean translation, "Continuous batching scheduler":
+ * requests can be PREEMPTED; JackerLab "vllm" tag page, PagedAttention: KV
+ * pages move between GPU and CPU memory).  A block is the contiguous run of
+ * block_bytes = num_kv_heads * block_size * head_dim * element-size bytes
+ * that one physical block holds in each pool.  All three are bit copies on
+ * `stream`; an id outside [0, num_blocks) skips its entry; block_bytes must
+ * be a multiple of 16 and every buffer 16-byte aligned.  Host transfers are
+ * not done here: a swap-out is pka_gather_blocks into a device buffer
+ * followed by one copy of that buffer to (pinned) host memory, a swap-in the
+ * reverse followed by pka_scatter_blocks.
+ *
+ * pka_copy_blocks   block_pairs: device int64 [num_pairs][2] (src, dst).
+ *                   Block dst of both pools becomes a copy of block src.
+ *                   Destinations must be distinct and no block may be both
+ *                   a source and a destination (else unspecified).
+ * pka_gather_blocks packed: device [num_ids][2][block_bytes] (K, then V),
+ *                   written; block_ids: device int64 [num_ids].  Entries with
+ *                   invalid ids are left unwritten.
+ * pka_scatter_blocks the inverse: block ids[i] of both pools take packed[i].
+ *                   Ids must be distinct (else unspecified).
+ */
+pka_status pka_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
+                           int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                           void *stream);
+pka_status pka_gather_blocks(void *packed, const void *k_cache, const void *v_cache,
+                             const int64_t *block_ids, int32_t num_ids, int32_t num_blocks,
+                             int64_t block_bytes, void *stream);
+pka_status pka_scatter_blocks(void *k_cache, void *v_cache, const void *packed,
+                              const int64_t *block_ids, int32_t num_ids, int32_t num_blocks,
+                              int64_t block_bytes, void *stream);
 
 /* Static English name of a status code. */
 const char *pka_status_string(pka_status status);

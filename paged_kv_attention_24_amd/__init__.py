@@ -18,6 +18,8 @@ Paged attention" and "Key features > GPU-optimised kernels"):
                           query_start, scale, num_kv_heads, block_size)
       its multi-token causal form (chunked prefill, drafted-token check;
       "Continuous batching scheduler" and "Roadmap" of the same README).
+  copy_blocks / gather_blocks / scatter_blocks / swap_out / swap_in
+      whole-block moves for preempted requests and GPU <-> CPU paging.
 
 Pools are [num_blocks, num_kv_heads, block_size, head_dim].
 
@@ -33,7 +35,8 @@ from typing import Optional
 
 __all__ = [
     "PkaError", "kv_cache_write", "paged_attention_decode", "paged_attention_decode_append",
-    "paged_attention_prefill",
+    "paged_attention_prefill", "copy_blocks", "gather_blocks", "scatter_blocks", "swap_out",
+    "swap_in",
     "decode_partition_size",
     "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
 ]
@@ -93,6 +96,12 @@ def load_library():
         P, ctypes.c_int, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
         ctypes.c_float, ctypes.c_int, P]
     lib.pka_paged_attention_prefill.restype = ctypes.c_int
+    lib.pka_copy_blocks.argtypes = [P, P, P, i32, i32, i64, P]
+    lib.pka_copy_blocks.restype = ctypes.c_int
+    lib.pka_gather_blocks.argtypes = [P, P, P, P, i32, i32, i64, P]
+    lib.pka_gather_blocks.restype = ctypes.c_int
+    lib.pka_scatter_blocks.argtypes = [P, P, P, P, i32, i32, i64, P]
+    lib.pka_scatter_blocks.restype = ctypes.c_int
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_last_error.argtypes = []
@@ -350,6 +359,97 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
         context_lens.data_ptr(), query_start.data_ptr(), B, N, int(max_query_len), Hq, Hkv, D,
         NB, bs, float(scale), _dtype_code(k_cache.dtype), _stream_ptr(q.device)))
     return out
+
+
+def _block_pools(k_cache, v_cache):
+    _require_gpu(k_cache, v_cache)
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
+        raise ValueError("K and V pools must be matching [num_blocks, Hkv, block_size, D] tensors")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    nb = k_cache.shape[0]
+    return nb, k_cache[0].numel() * k_cache.element_size()
+
+
+def _ids(t, width):
+    import torch
+
+    _require_gpu(t)
+    if t.dtype != torch.int64 or (t.dim() != (1 if width == 1 else 2)) or \
+            (width == 2 and t.shape[1] != 2):
+        raise ValueError("block ids must be int64 [n]" if width == 1 else
+                         "block pairs must be int64 [n, 2] (src, dst)")
+    return t.contiguous()
+
+
+def copy_blocks(k_cache, v_cache, block_pairs):
+    """Block dst of both pools becomes a copy of block src, for each (src,
+    dst) row of block_pairs (device int64 [n, 2]); destinations distinct and
+    never also sources."""
+    nb, bb = _block_pools(k_cache, v_cache)
+    pairs = _ids(block_pairs, 2)
+    if pairs.shape[0] == 0:
+        return
+    _check(load_library().pka_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(),
+                                          pairs.data_ptr(), pairs.shape[0], nb, bb,
+                                          _stream_ptr(k_cache.device)))
+
+
+def gather_blocks(k_cache, v_cache, block_ids, out=None):
+    """Blocks block_ids (device int64 [n]) of both pools packed into a device
+    uint8 tensor [n, 2, block_bytes] (K, then V)."""
+    import torch
+
+    nb, bb = _block_pools(k_cache, v_cache)
+    ids = _ids(block_ids, 1)
+    n = ids.shape[0]
+    if out is None:
+        out = torch.empty((n, 2, bb), dtype=torch.uint8, device=k_cache.device)
+    elif tuple(out.shape) != (n, 2, bb) or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 [{n}, 2, {bb}] tensor")
+    if n:
+        _check(load_library().pka_gather_blocks(out.data_ptr(), k_cache.data_ptr(),
+                                                v_cache.data_ptr(), ids.data_ptr(), n, nb, bb,
+                                                _stream_ptr(k_cache.device)))
+    return out
+
+
+def scatter_blocks(k_cache, v_cache, packed, block_ids):
+    """The inverse of gather_blocks: blocks block_ids (distinct) of both pools
+    take packed [n, 2, block_bytes] (a device tensor)."""
+    import torch
+
+    nb, bb = _block_pools(k_cache, v_cache)
+    ids = _ids(block_ids, 1)
+    n = ids.shape[0]
+    _require_gpu(packed)
+    if tuple(packed.shape) != (n, 2, bb) or packed.dtype != torch.uint8:
+        raise ValueError(f"packed must be uint8 [{n}, 2, {bb}]")
+    packed = packed.contiguous()
+    if n:
+        _check(load_library().pka_scatter_blocks(k_cache.data_ptr(), v_cache.data_ptr(),
+                                                 packed.data_ptr(), ids.data_ptr(), n, nb, bb,
+                                                 _stream_ptr(k_cache.device)))
+
+
+def swap_out(k_cache, v_cache, block_ids, host=None):
+    """Copy blocks block_ids of both pools to pinned host memory (one gather
+    launch, then one device-to-host copy); returns the host uint8 tensor
+    [n, 2, block_bytes].  Asynchronous: synchronise before reading it."""
+    import torch
+
+    staging = gather_blocks(k_cache, v_cache, block_ids)
+    if host is None:
+        host = torch.empty(staging.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(staging, non_blocking=True)
+    return host
+
+
+def swap_in(k_cache, v_cache, host, block_ids):
+    """Copy host rows [n, 2, block_bytes] (from swap_out) into blocks
+    block_ids of both pools: one host-to-device copy, then one scatter."""
+    staging = host.to(k_cache.device, non_blocking=True)
+    scatter_blocks(k_cache, v_cache, staging, block_ids)
 
 
 _WORKSPACES = {}

@@ -26,7 +26,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpka.so")
 
 ARCH = "gfx950"
-SOURCES = ["paged_decode.hip", "paged_prefill.hip", "kv_cache_write.hip", "abi.cpp"]
+SOURCES = ["paged_decode.hip", "paged_prefill.hip", "kv_cache_write.hip", "block_ops.hip",
+           "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 VARIANTS = {"vector_alu": ["-DPKA_MATRIX_CORES=0"]}
 

@@ -389,4 +389,62 @@ pka_status pka_paged_attention_prefill(void *out, pka_dtype out_dtype, const voi
     return ok();
 }
 
+static pka_status move_blocks(pka::BlockMove mode, void *k_cache, void *v_cache, void *packed,
+                              const int64_t *ids, int32_t n, int32_t num_blocks,
+                              int64_t block_bytes, void *stream, const char *what)
+{
+    if (n < 0 || num_blocks <= 0 || block_bytes <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "%s: n >= 0, num_blocks > 0, block_bytes > 0 required",
+                    what);
+    if (block_bytes % 16)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "%s: block_bytes %lld is not a multiple of 16", what,
+                    (long long)block_bytes);
+    if ((block_bytes + 16383) / 16384 > 65535)
+        return fail(PKA_ERR_UNSUPPORTED, "%s: blocks larger than 1 GiB", what);
+    if (n == 0)
+        return ok();
+    if (!k_cache || !v_cache || !ids || (mode != pka::BlockMove::Copy && !packed))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "%s: null pointer argument", what);
+    if (!aligned16(k_cache) || !aligned16(v_cache) || (packed && !aligned16(packed)))
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "%s: pools and the packed buffer must be 16-byte aligned", what);
+    pka::BlockMoveArgs a{};
+    a.mode = mode;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.packed = packed;
+    a.ids = ids;
+    a.num_entries = n;
+    a.num_blocks = num_blocks;
+    a.block_bytes = block_bytes;
+    hipError_t e = pka::launch_move_blocks(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+pka_status pka_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
+                           int32_t num_pairs, int32_t num_blocks, int64_t block_bytes, void *stream)
+{
+    return move_blocks(pka::BlockMove::Copy, k_cache, v_cache, nullptr, block_pairs, num_pairs,
+                       num_blocks, block_bytes, stream, "copy_blocks");
+}
+
+pka_status pka_gather_blocks(void *packed, const void *k_cache, const void *v_cache,
+                             const int64_t *block_ids, int32_t num_ids, int32_t num_blocks,
+                             int64_t block_bytes, void *stream)
+{
+    return move_blocks(pka::BlockMove::Gather, const_cast<void *>(k_cache),
+                       const_cast<void *>(v_cache), packed, block_ids, num_ids, num_blocks,
+                       block_bytes, stream, "gather_blocks");
+}
+
+pka_status pka_scatter_blocks(void *k_cache, void *v_cache, const void *packed,
+                              const int64_t *block_ids, int32_t num_ids, int32_t num_blocks,
+                              int64_t block_bytes, void *stream)
+{
+    return move_blocks(pka::BlockMove::Scatter, k_cache, v_cache, const_cast<void *>(packed),
+                       block_ids, num_ids, num_blocks, block_bytes, stream, "scatter_blocks");
+}
+
 }  // extern "C"

@@ -109,4 +109,18 @@ struct PrefillArgs {
 bool prefill_supported(DType kv, int head_dim, int block_size, int group);
 hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// Whole-block copies between and inside the pools (preemption, paging).
+enum class BlockMove : int { Copy = 0, Gather = 1, Scatter = 2 };
+struct BlockMoveArgs {
+    BlockMove mode;
+    void *k_cache, *v_cache;
+    void *packed;          // gather: written, scatter: read; [n][2][block_bytes]
+    const int64_t *ids;    // copy: [n][2] (src, dst); gather, scatter: [n]
+    int64_t num_entries;   // n
+    int64_t num_blocks;
+    int64_t block_bytes;   // multiple of 16
+};
+
+hipError_t launch_move_blocks(const BlockMoveArgs &a, hipStream_t stream);
+
 }  // namespace pka

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strings():
     lib = pka.load_library()
-    assert lib.pka_abi_version() == 2
+    assert lib.pka_abi_version() == 3
     assert lib.pka_status_string(0) == b"ok"
     assert lib.pka_status_string(3) == b"workspace too small"
     assert lib.pka_status_string(99) == b"unknown status"
@@ -187,3 +187,31 @@ def test_prefill_rejects(over, status):
 def test_prefill_empty_is_ok_without_launch():
     assert prefill(B=0, out=None, q=None)[0] == 0
     assert prefill(N=0, out=None, q=None)[0] == 0
+
+
+@pytest.mark.parametrize("fn", ["copy", "gather", "scatter"])
+@pytest.mark.parametrize("over,status", [
+    (dict(n=-1), 1), (dict(nb=0), 1), (dict(bb=0), 1), (dict(bb=1000), 1), (dict(ids=None), 1),
+    (dict(kc=None), 1), (dict(kc=FAKE + 8), 1), (dict(bb=1 << 40), 2),
+])
+def test_block_moves_reject(fn, over, status):
+    a = dict(kc=FAKE, vc=FAKE, pk=FAKE, ids=FAKE, n=4, nb=10, bb=16384)
+    a.update(over)
+    lib = pka.load_library()
+    if fn == "copy":
+        st = lib.pka_copy_blocks(a["kc"], a["vc"], a["ids"], a["n"], a["nb"], a["bb"], None)
+    elif fn == "gather":
+        st = lib.pka_gather_blocks(a["pk"], a["kc"], a["vc"], a["ids"], a["n"], a["nb"], a["bb"],
+                                   None)
+    else:
+        st = lib.pka_scatter_blocks(a["kc"], a["vc"], a["pk"], a["ids"], a["n"], a["nb"], a["bb"],
+                                    None)
+    assert st == status, (fn, over, st)
+    assert lib.pka_last_error()
+
+
+def test_block_moves_need_the_packed_buffer():
+    lib = pka.load_library()
+    assert lib.pka_gather_blocks(None, FAKE, FAKE, FAKE, 4, 10, 16384, None) == 1
+    assert lib.pka_scatter_blocks(FAKE, FAKE, None, FAKE, 4, 10, 16384, None) == 1
+    assert lib.pka_copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16384, None) == 0  # nothing to do
