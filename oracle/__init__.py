@@ -89,6 +89,11 @@ def _declare(h):
         P, P, P, P, ctypes.c_int, P, i32, P, P, i32, i32, i32, i32, i32, i32, f64, P, i32, i32]
     h.oracle_paged_attention_prefill.restype = ctypes.c_int
     h.oracle_kv_cache_write.argtypes = [P, P, i64, i64, P, i32, P, P, i32, i32, i32, i32, i32]
+    h.oracle_kv_cache_write_rope.argtypes = [P, P, i64, i64, P, P, i32, P, i32, i32, P, P, i32,
+                                             i32, i32, i32, ctypes.c_int]
+    h.oracle_kv_cache_write_rope.restype = ctypes.c_int
+    h.oracle_round_array.argtypes = [P, ctypes.c_int, i64, P]
+    h.oracle_round_array.restype = None
     h.oracle_copy_blocks.argtypes = [P, P, P, i32, i32, i64]
     h.oracle_copy_blocks.restype = ctypes.c_int
     h.oracle_gather_blocks.argtypes = [P, P, P, P, i32, i32, i64]
@@ -338,3 +343,43 @@ def scatter_blocks(k_cache, v_cache, packed, ids, handle=None) -> None:
                                  nb, bb)
     if rc != 0:
         raise OracleError(f"oracle scatter_blocks failed: {STATUS.get(rc, rc)}")
+
+
+# ---------------------------------------------------------------------------
+# KV-cache write with the rotary position embedding on the new keys
+# ---------------------------------------------------------------------------
+
+def round_floats(x, dtype, handle=None) -> np.ndarray:
+    """float32 -> uint16 bit patterns of dtype ("f16"/"bf16"), nearest even."""
+    h = handle or lib()
+    src = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(src.shape, dtype=np.uint16)
+    h.oracle_round_array(_ptr(src), DTYPE_CODE[dtype], src.size, _ptr(out))
+    return out
+
+
+def kv_cache_write_rope(k, v, slot_mapping, positions, cos_sin, k_cache, v_cache, dtype,
+                        handle=None) -> None:
+    """In place: the write of k, v [T, Hkv, D] at slot_mapping with K rotated
+    at positions (int32 [T]) by the table cos_sin (float32 [max_position,
+    rotary_dim]: cos then sin of each position's rotary_dim / 2 angles)."""
+    h = handle or lib()
+    want = np.float32 if dtype == "f32" else np.uint16
+    for a, w in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if a.dtype != want:
+            raise TypeError(f"{w}: expected {np.dtype(want)} storage")
+    NB, Hkv, bs, D = k_cache.shape
+    T = k.shape[0]
+    item = k.itemsize
+    for a in (k, v):
+        if a.shape[1:] != (Hkv, D) or a.strides[2] != item or a.strides[1] != D * item:
+            raise ValueError("k/v must be [T, Hkv, D] with contiguous heads")
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    cs = np.ascontiguousarray(cos_sin, dtype=np.float32)
+    rc = h.oracle_kv_cache_write_rope(
+        _ptr(k), _ptr(v), k.strides[0] // item if T else Hkv * D,
+        v.strides[0] // item if T else Hkv * D, _ptr(sm), _ptr(pos), T, _ptr(cs), cs.shape[0],
+        cs.shape[1], _ptr(k_cache), _ptr(v_cache), NB, bs, Hkv, D, DTYPE_CODE[dtype])
+    if rc != 0:
+        raise OracleError(f"oracle rope write failed: {STATUS.get(rc, rc)}")

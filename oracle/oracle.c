@@ -559,3 +559,156 @@ int oracle_scatter_blocks(void *k_cache, void *v_cache, const void *packed, cons
     }
     return ORACLE_OK;
 }
+
+/*
+ * Float to the 16-bit formats, rounding to nearest with ties to even,
+ * written from the formats' definitions in double arithmetic (every float
+ * is exact in double; rint() rounds half to even in the default rounding
+ * mode): find the quantum of the value's binade, count quanta, round.
+ * Magnitudes at or past the midpoint above the largest finite value become
+ * infinity; NaN becomes a quiet NaN with the sign and top payload bits.
+ */
+uint16_t oracle_f32_to_f16(float f)
+{
+    double x = (double)f;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x)) {
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        return (uint16_t)(sign | 0x7e00 | ((u >> 13) & 0x1ff));
+    }
+    if (a >= 65520.0) /* 65504 + half a quantum (2^5 / 2) and beyond */
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) { /* subnormal binade: quantum 2^-24 */
+        double q = rint(a / ldexp(1.0, -24));
+        return (uint16_t)(sign | (uint16_t)q); /* q == 1024 is the smallest normal */
+    }
+    int e;
+    frexp(a, &e); /* a = m 2^e, m in [0.5, 1): binade 2^(e-1) */
+    int expo = e - 1;
+    double q = rint(a / ldexp(1.0, expo - 10)); /* in [1024, 2048] */
+    if (q == 2048.0) {
+        q = 1024.0;
+        expo += 1;
+    }
+    if (expo > 15)
+        return sign | 0x7c00;
+    return (uint16_t)(sign | ((expo + 15) << 10) | ((int)q - 1024));
+}
+
+uint16_t oracle_f32_to_bf16(float f)
+{
+    double x = (double)f;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x)) {
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        return (uint16_t)((u >> 16) | 0x40);
+    }
+    /* largest finite bf16: (2 - 2^-7) 2^127; halfway to 2^128 and beyond */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))
+        return sign | 0x7f80;
+    if (a < ldexp(1.0, -126)) { /* subnormal binade: quantum 2^-133 */
+        double q = rint(a / ldexp(1.0, -133));
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e;
+    frexp(a, &e);
+    int expo = e - 1;
+    double q = rint(a / ldexp(1.0, expo - 7)); /* in [128, 256] */
+    if (q == 256.0) {
+        q = 128.0;
+        expo += 1;
+    }
+    if (expo > 127)
+        return sign | 0x7f80;
+    return (uint16_t)(sign | ((expo + 127) << 7) | ((int)q - 128));
+}
+
+/*
+ * The KV-cache write with the rotary position embedding applied to the new
+ * keys (PhotonInfer README, Korean translation, "Key features >
+ * GPU-optimised kernels": batched RoPE among the fused operations).  For
+ * each token i with a valid slot (as in oracle_kv_cache_write) and a
+ * position p = positions[i] in [0, max_position):
+ *   V rows are stored unchanged;
+ *   each K row x (head h) is stored as y with, for j < R/2 (R = rotary_dim),
+ *     c = cos_sin[p][j], s = cos_sin[p][R/2 + j],
+ *     y[j]       = x[j] c - x[j + R/2] s,
+ *     y[j + R/2] = x[j + R/2] c + x[j] s,
+ *   and y[d] = x[d] for d >= R,
+ * each product and each sum rounded to float (no fused multiply-add), then
+ * y rounded to nearest even into the pool dtype.  The table (cos then sin
+ * of each position's angles, [max_position][R] floats) is the caller's:
+ * the angle schedule (base, any frequency scaling) is not fixed here.  A
+ * token whose position is outside the table is skipped.
+ */
+int oracle_kv_cache_write_rope(const void *k, const void *v, int64_t k_token_stride,
+                               int64_t v_token_stride, const int64_t *slot_mapping,
+                               const int32_t *positions, int32_t num_tokens, const float *cos_sin,
+                               int32_t max_position, int32_t rotary_dim, void *k_cache,
+                               void *v_cache, int32_t num_blocks, int32_t block_size,
+                               int32_t num_kv_heads, int32_t head_dim, int dtype)
+{
+    if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || dtype < ORACLE_F32 || dtype > ORACLE_BF16 || rotary_dim < 0 ||
+        rotary_dim > head_dim || rotary_dim % 2 || max_position < 0)
+        return ORACLE_BAD_ARGUMENT;
+    int elt = dtype == ORACLE_F32 ? 4 : 2;
+    int half = rotary_dim / 2;
+    float *x = (float *)malloc(sizeof(float) * (size_t)head_dim);
+    float *y = (float *)malloc(sizeof(float) * (size_t)head_dim);
+    if (!x || !y) {
+        free(x);
+        free(y);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int64_t s = slot_mapping[i];
+        int32_t p = positions[i];
+        if (s < 0 || s >= (int64_t)num_blocks * block_size || p < 0 || p >= max_position)
+            continue;
+        int64_t blk = s / block_size;
+        int64_t off = s - blk * block_size;
+        const float *cs = cos_sin + (int64_t)p * rotary_dim;
+        for (int h = 0; h < num_kv_heads; ++h) {
+            int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * head_dim;
+            int64_t vsrc = (int64_t)i * v_token_stride + (int64_t)h * head_dim;
+            memcpy((char *)v_cache + dst * elt, (const char *)v + vsrc * elt, (size_t)head_dim * elt);
+            int64_t src = (int64_t)i * k_token_stride + (int64_t)h * head_dim;
+            for (int d = 0; d < head_dim; ++d)
+                x[d] = (float)load_elem(k, dtype, src + d);
+            for (int d = 0; d < head_dim; ++d)
+                y[d] = x[d];
+            for (int j = 0; j < half; ++j) {
+                float c = cs[j], sn = cs[half + j];
+                float a = x[j] * c, b = x[j + half] * sn;
+                float e = x[j + half] * c, f = x[j] * sn;
+                y[j] = a - b;
+                y[j + half] = e + f;
+            }
+            for (int d = 0; d < head_dim; ++d) {
+                char *out = (char *)k_cache + (dst + d) * elt;
+                if (dtype == ORACLE_F32) {
+                    memcpy(out, &y[d], 4);
+                } else {
+                    uint16_t hb = dtype == ORACLE_F16 ? oracle_f32_to_f16(y[d])
+                                                      : oracle_f32_to_bf16(y[d]);
+                    memcpy(out, &hb, 2);
+                }
+            }
+        }
+    }
+    free(x);
+    free(y);
+    return ORACLE_OK;
+}
+
+/* n floats to 16-bit bit patterns (to check the two conversions). */
+void oracle_round_array(const float *src, int dtype, int64_t n, uint16_t *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = dtype == ORACLE_F16 ? oracle_f32_to_f16(src[i]) : oracle_f32_to_bf16(src[i]);
+}

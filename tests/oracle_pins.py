@@ -508,6 +508,138 @@ def pin_moved_blocks_decode_unchanged(h):
     assert np.array_equal(run(h, wl), before)
 
 
+# ---------------------------------------------------------------------------
+# KV-cache write with the rotary embedding on the new keys
+# ---------------------------------------------------------------------------
+
+def _float_grid():
+    """Every fp16 value, the exact midpoints between neighbours (ties), random
+    floats over the subnormal to overflow range, and the overflow edges."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    h = h[np.isfinite(h)]
+    hs = np.sort(np.unique(h))
+    mids = ((hs[1:].astype(np.float64) + hs[:-1].astype(np.float64)) / 2).astype(np.float32)
+    rng = np.random.default_rng(3)
+    with np.errstate(over="ignore"):
+        r = (rng.standard_normal(200000) * np.exp2(rng.uniform(-140, 140, 200000))).astype(np.float32)
+    edges = np.array([65504, 65519.996, 65520, 65536, 1e9, 3.4e38, 2.0 ** -24, 2.0 ** -25,
+                      3 * 2.0 ** -26, 2.0 ** -149, 0.0, -0.0], dtype=np.float32)
+    x = np.concatenate([h, mids, r, edges, -edges])
+    return x[np.isfinite(x)]
+
+
+def pin_round_to_16bit(h):
+    """P-t: float -> fp16 and -> bf16 rounding (nearest, ties to even,
+    overflow to infinity, subnormals) equals numpy's and torch's conversions
+    bit for bit over every fp16 value, their midpoints and random floats."""
+    x = _float_grid()
+    f16 = oracle.round_floats(x, "f16", handle=h)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(f16, x.astype(np.float16).view(np.uint16))
+    bf = oracle.round_floats(x, "bf16", handle=h)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bf, ref)
+
+
+def _rope_table(max_pos, R, base=10000.0):
+    theta = base ** (-np.arange(0, R, 2, dtype=np.float64) / R)
+    ang = np.arange(max_pos)[:, None] * theta[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)
+
+
+def _rope_setup(seed, dtype, T=6, Hkv=2, D=64, bs=16, NB=8):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    if dtype != "f32":
+        k, v = W._round_to_dtype(k, dtype), W._round_to_dtype(v, dtype)
+    slots = rng.permutation(NB * bs)[:T].astype(np.int64)
+    zero = np.zeros((NB, Hkv, bs, D), dtype=k.dtype)
+    return k, v, slots, zero.copy(), zero.copy()
+
+
+def _stored_rows(cache, slots, bs):
+    return np.stack([cache[s // bs, :, s % bs, :] for s in slots])
+
+
+def pin_rope_write_numpy(h):
+    """P-u: the rotated keys equal numpy float32 arithmetic (each product and
+    sum rounded to float, pairs (j, j + R/2)) rounded by numpy / torch to the
+    pool dtype, bit for bit, over dtypes and partial rotary widths; values
+    are stored unchanged."""
+    for dtype, R in (("f32", 64), ("f16", 64), ("bf16", 32), ("f16", 16)):
+        k, v, slots, kc, vc = _rope_setup(50, dtype)
+        table = _rope_table(4096, R)
+        pos = np.array([0, 1, 7, 100, 4000, 2048], dtype=np.int32)
+        oracle.kv_cache_write_rope(k, v, slots, pos, table, kc, vc, dtype, handle=h)
+        x = f64(k, dtype).astype(np.float32)
+        c = table[pos][:, None, : R // 2]
+        sn = table[pos][:, None, R // 2:]
+        x1, x2 = x[..., : R // 2], x[..., R // 2: R]
+        y = x.copy()
+        y[..., : R // 2] = x1 * c - x2 * sn
+        y[..., R // 2: R] = x2 * c + x1 * sn
+        if dtype == "f32":
+            want = y
+        elif dtype == "f16":
+            want = y.astype(np.float16).view(np.uint16)
+        else:
+            want = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        got = _stored_rows(kc, slots, 16)
+        assert got.tobytes() == want.tobytes(), (dtype, R)
+        assert _stored_rows(vc, slots, 16).tobytes() == v.tobytes()
+
+
+def pin_rope_unit_vectors(h):
+    """P-v: a key with a single 1 at dim j < R/2 is stored as cos at j and sin
+    at j + R/2 of its position's angle, zero elsewhere (the pairing and the
+    direction of the rotation); a 1 at j + R/2 gives -sin at j, cos at
+    j + R/2."""
+    D, R = 64, 64
+    table = _rope_table(64, R)
+    T = 2 * (R // 2)
+    k = np.zeros((T, 1, D), dtype=np.float32)
+    for j in range(R // 2):
+        k[j, 0, j] = 1.0
+        k[R // 2 + j, 0, R // 2 + j] = 1.0
+    v = np.zeros_like(k)
+    slots = np.arange(T, dtype=np.int64)
+    pos = (np.arange(T) % 61 + 1).astype(np.int32)
+    kc = np.zeros((T // 16 + 1, 1, 16, D), dtype=np.float32)
+    vc = kc.copy()
+    oracle.kv_cache_write_rope(k, v, slots, pos, table, kc, vc, "f32", handle=h)
+    got = _stored_rows(kc, slots, 16)[:, 0]
+    for j in range(R // 2):
+        c, s = table[pos[j], j], table[pos[j], R // 2 + j]
+        want = np.zeros(D, dtype=np.float32)
+        want[j], want[R // 2 + j] = c, s
+        assert np.array_equal(got[j], want)
+        i = R // 2 + j
+        c, s = table[pos[i], j], table[pos[i], R // 2 + j]
+        want = np.zeros(D, dtype=np.float32)
+        want[j], want[R // 2 + j] = -s, c
+        assert np.array_equal(got[i], want)
+
+
+def pin_rope_identity_and_skip(h):
+    """P-w: position 0 of a table (angle 0: cos 1, sin 0) stores the keys
+    unrotated, bit for bit the plain write; a position outside the table
+    skips the token."""
+    k, v, slots, kc, vc = _rope_setup(51, "bf16")
+    table = _rope_table(16, 64)
+    oracle.kv_cache_write_rope(k, v, slots, np.zeros(len(slots), np.int32), table, kc, vc, "bf16",
+                               handle=h)
+    kc2, vc2 = np.zeros_like(kc), np.zeros_like(vc)
+    oracle.kv_cache_write(k, v, slots, kc2, vc2, "bf16", handle=h)
+    assert kc.tobytes() == kc2.tobytes() and vc.tobytes() == vc2.tobytes()
+    kc3, vc3 = np.zeros_like(kc), np.zeros_like(vc)
+    bad = np.array([16, -1, 5, 99, 0, 3], dtype=np.int32)
+    oracle.kv_cache_write_rope(k, v, slots, bad, table, kc3, vc3, "bf16", handle=h)
+    for i, p in enumerate(bad):
+        blk, off = divmod(int(slots[i]), 16)
+        assert kc3[blk, :, off].any() == (0 <= p < 16)
+
+
 PINS = {
     "append_equals_write_then_decode": pin_append_equals_write_then_decode,
     "decoders_exhaustive": pin_decoders_exhaustive,
@@ -530,4 +662,8 @@ PINS = {
     "copy_blocks": pin_copy_blocks,
     "gather_scatter": pin_gather_scatter,
     "moved_blocks_decode_unchanged": pin_moved_blocks_decode_unchanged,
+    "round_to_16bit": pin_round_to_16bit,
+    "rope_write_numpy": pin_rope_write_numpy,
+    "rope_unit_vectors": pin_rope_unit_vectors,
+    "rope_identity_and_skip": pin_rope_identity_and_skip,
 }

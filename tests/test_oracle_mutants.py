@@ -74,6 +74,22 @@ MUTANTS = {
     # scatter: K restored from the V half of the packed row
     "scatter_k_offset": ("memcpy((char *)k_cache + id * block_bytes, row, ",
                          "memcpy((char *)k_cache + id * block_bytes, row + block_bytes, "),
+    # rotary embedding: rotation in the wrong direction
+    "rope_sign": ("y[j] = a - b;", "y[j] = a + b;"),
+    # rotary embedding: pairs (j, j + 1) instead of (j, j + R/2)
+    "rope_pairing": ("float a = x[j] * c, b = x[j + half] * sn;",
+                     "float a = x[j] * c, b = x[j + 1] * sn;"),
+    # rotary embedding: sine read from the cosine half of the table
+    "rope_table_offset": ("float c = cs[j], sn = cs[half + j];", "float c = cs[j], sn = cs[j];"),
+    # fp16 rounding truncates (normal binades)
+    "f16_round_trunc": ("double q = rint(a / ldexp(1.0, expo - 10));",
+                        "double q = floor(a / ldexp(1.0, expo - 10));"),
+    # fp16 rounding truncates (subnormals)
+    "f16_subnormal_trunc": ("double q = rint(a / ldexp(1.0, -24));",
+                            "double q = floor(a / ldexp(1.0, -24));"),
+    # bf16 rounding truncates
+    "bf16_round_trunc": ("double q = rint(a / ldexp(1.0, expo - 7));",
+                         "double q = floor(a / ldexp(1.0, expo - 7));"),
 }
 
 
