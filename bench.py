@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--path", default="decode", choices=["decode", "prefill", "blocks"],
+    ap.add_argument("--path", default="decode", choices=["decode", "prefill", "blocks", "rope"],
                     help="decode step (the headline), multi-token causal attention, or "
                          "whole-block moves (preemption, paging)")
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
@@ -71,7 +71,8 @@ def log(msg):
 # counter summary still describes it)
 KERNEL_SOURCES = {"decode": ("paged_decode.hip", "cdna4.h"),
                   "prefill": ("paged_prefill.hip", "cdna4.h"),
-                  "blocks": ("block_ops.hip",)}
+                  "blocks": ("block_ops.hip",),
+                  "rope": ("kv_cache_write.hip", "cdna4.h")}
 
 
 def kernel_source_sha(path_kind):
@@ -137,6 +138,8 @@ def main():
         return run_prefill(args, dev)
     if args.path == "blocks":
         return run_blocks(args, dev)
+    if args.path == "rope":
+        return run_rope(args, dev)
 
     cfg = args.config
     host_pools = cfg in (2, 3)
@@ -604,6 +607,107 @@ def run_blocks(args, dev):
                               "copy-calibrated; null when the kernel changed since)",
             "kernel": "move_blocks_kernel (copy mode, one launch)",
             "us_per_launch": round(ms_copy * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(alg),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+ROPE_TAG = "kv_write_rope_llama3_1b"
+
+
+def run_rope(args, dev):
+    """The KV-cache write with the rotary embedding on the new keys, for one
+    prompt chunk of 16384 tokens on the Llama-3.2-1B layer shape (8 kv
+    heads, head_dim 64, rotary over all 64 dims, fp16, block 16, pool of
+    16384 blocks), beside the plain write of the same tokens."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+
+    NB, H, BS, D, T, R, MAXP = 16384, 8, 16, 64, 16384, 64, 131072
+    kc = fill_pool((NB, H, BS, D), torch.float16, 4000, dev)
+    vc = fill_pool((NB, H, BS, D), torch.float16, 4001, dev)
+    k = fill_pool((T, H, D), torch.float16, 4002, dev)
+    v = fill_pool((T, H, D), torch.float16, 4003, dev)
+    rng = np.random.default_rng(0)
+    slots = torch.from_numpy(rng.permutation(NB * BS)[:T].astype(np.int64)).to(dev)
+    pos = torch.from_numpy(rng.integers(0, MAXP, T).astype(np.int32)).to(dev)
+    theta = 500000.0 ** (-np.arange(0, R, 2, dtype=np.float64) / R)
+    ang = np.arange(MAXP)[:, None] * theta[None, :]
+    table = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)).to(dev)
+    if args.calibration_copy_mib > 0:
+        src_c = torch.ones(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+    use_graph = not args.eager
+    ms_rope = timed_calls(lambda: pka.kv_cache_write_rope(k, v, slots, pos, table, kc, vc),
+                          args.steps, args.warmup, use_graph)
+    ms_plain = timed_calls(lambda: pka.kv_cache_write(k, v, slots, kc, vc), args.steps,
+                           args.warmup, use_graph)
+    row = T * H * D * 2
+    alg = 2 * row * 2 + T * (8 + 4) + T * R * 4  # K, V in and out; slots, positions; table rows
+    gbps = alg / (ms_rope * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        from paged_kv_attention_24_amd import workloads as W
+
+        m = 2048  # a sample of the tokens, into a host copy of a pool slice
+        kh = W.to_numpy_bits(k[:m], "f16")
+        vh = W.to_numpy_bits(v[:m], "f16")
+        th = table.cpu().numpy()
+        ph = pos[:m].cpu().numpy()
+        sh = np.arange(m, dtype=np.int64)
+        kp = np.zeros((m // BS, H, BS, D), dtype=np.uint16)
+        vp = kp.copy()
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.kv_cache_write_rope(kh, vh, sh, ph, th, kp, vp, "f16")
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n_done >= 256:
+                break
+        cpu = {"value": round((2 * m * H * D * 2 * 2 + m * R * 4) * n_done / el / 1e9, 3),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{m} of the {T} tokens, repeated {n_done}x in {el:.1f} s; "
+                         "single-threaded C"}
+
+    line = {
+        "metric": "KV-cache write with rotary embedding, GB/s",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_rope, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (device-random rows and pools, random slots and positions)",
+        "config": {
+            "workload": f"RoPE KV write, Llama-3.2-1B layer: {T} tokens x 8 kv heads x 64 fp16, "
+                        f"rotary over 64 dims, base 500000 table of {MAXP} positions",
+            "global_batch": T, "timing": "hip-graph replay" if use_graph else "eager",
+            "parallelism": "single GPU",
+        },
+        "us_rope_write": round(ms_rope * 1e3, 3),
+        "us_plain_write": round(ms_plain * 1e3, 3),
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(ROPE_TAG, "rope"),
+            "traffic_source": f"profiles/{ROPE_TAG}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                              "copy-calibrated; null when the kernel changed since)",
+            "kernel": "kv_cache_write_rope_kernel (one launch)",
+            "us_per_launch": round(ms_rope * 1e3, 3),
             "algorithmic_bytes_per_launch": int(alg),
         },
         "cpu_baseline": cpu,

@@ -14,6 +14,8 @@
  *   - Its multi-token form, for prompts admitted chunk by chunk and for
  *     drafted tokens ("Continuous batching scheduler", "Roadmap")
  *     ->  pka_paged_attention_prefill.
+ *   - "Key features > GPU-optimised kernels" also lists batched RoPE among
+ *     the fused operations  ->  pka_kv_cache_write_rope.
  *   - Block movement for preempted requests and paging
  *     ->  pka_copy_blocks, pka_gather_blocks, pka_scatter_blocks.
  *
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 3
+#define PKA_ABI_VERSION 4
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -98,6 +100,35 @@ pka_status pka_kv_cache_write(const void *k, const void *v, int64_t k_token_stri
                               int32_t num_tokens, void *k_cache, void *v_cache,
                               int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                               int32_t head_dim, pka_dtype dtype, void *stream);
+
+/*
+ * pka_kv_cache_write_rope -- pka_kv_cache_write with the rotary position
+ * embedding applied to the new keys on their way into the pool (PhotonInfer
+ * README, Korean translation, "Key features > GPU-optimised kernels":
+ * batched RoPE among the fused operations).  Token i at position
+ * p = positions[i] has each K row x stored as y, for j < R/2
+ * (R = rotary_dim):
+ *   y[j]       = x[j] c_j - x[j + R/2] s_j,
+ *   y[j + R/2] = x[j + R/2] c_j + x[j] s_j,
+ *   c_j = cos_sin[p][j], s_j = cos_sin[p][R/2 + j],
+ * computed in fp32 (each product and sum rounded, no fused multiply-add) and
+ * rounded to nearest even into the pool dtype; dims >= R and the V rows are
+ * stored unchanged.  The table is the caller's, so the angle schedule (base,
+ * frequency scaling) is too.
+ *   positions   device, int32 [num_tokens].  A position outside
+ *               [0, max_position) skips the token (nothing is stored).
+ *   cos_sin     device, float [max_position][rotary_dim]: per position the
+ *               R/2 cosines, then the R/2 sines.
+ *   rotary_dim  even, <= head_dim, a multiple of 16 (fp16/bf16) or 8 (fp32).
+ * Everything else as for pka_kv_cache_write.
+ */
+pka_status pka_kv_cache_write_rope(const void *k, const void *v, int64_t k_token_stride,
+                                   int64_t v_token_stride, const int64_t *slot_mapping,
+                                   const int32_t *positions, int32_t num_tokens,
+                                   const float *cos_sin, int32_t max_position, int32_t rotary_dim,
+                                   void *k_cache, void *v_cache, int32_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                   pka_dtype dtype, void *stream);
 
 /*
  * pka_decode_partition_size -- the partition length (tokens, a multiple of

@@ -18,6 +18,9 @@ Paged attention" and "Key features > GPU-optimised kernels"):
                           query_start, scale, num_kv_heads, block_size)
       its multi-token causal form (chunked prefill, drafted-token check;
       "Continuous batching scheduler" and "Roadmap" of the same README).
+  kv_cache_write_rope(k, v, slot_mapping, positions, cos_sin, k_cache, v_cache)
+      the write with the rotary embedding applied to the new keys ("batched
+      RoPE" among the README's fused operations).
   copy_blocks / gather_blocks / scatter_blocks / swap_out / swap_in
       whole-block moves for preempted requests and GPU <-> CPU paging.
 
@@ -35,7 +38,7 @@ from typing import Optional
 
 __all__ = [
     "PkaError", "kv_cache_write", "paged_attention_decode", "paged_attention_decode_append",
-    "paged_attention_prefill", "copy_blocks", "gather_blocks", "scatter_blocks", "swap_out",
+    "paged_attention_prefill", "kv_cache_write_rope", "copy_blocks", "gather_blocks", "scatter_blocks", "swap_out",
     "swap_in",
     "decode_partition_size",
     "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
@@ -96,6 +99,9 @@ def load_library():
         P, ctypes.c_int, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
         ctypes.c_float, ctypes.c_int, P]
     lib.pka_paged_attention_prefill.restype = ctypes.c_int
+    lib.pka_kv_cache_write_rope.argtypes = [P, P, i64, i64, P, P, i32, P, i32, i32, P, P, i32,
+                                            i32, i32, i32, ctypes.c_int, P]
+    lib.pka_kv_cache_write_rope.restype = ctypes.c_int
     lib.pka_copy_blocks.argtypes = [P, P, P, i32, i32, i64, P]
     lib.pka_copy_blocks.restype = ctypes.c_int
     lib.pka_gather_blocks.argtypes = [P, P, P, P, i32, i32, i64, P]
@@ -359,6 +365,39 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
         context_lens.data_ptr(), query_start.data_ptr(), B, N, int(max_query_len), Hq, Hkv, D,
         NB, bs, float(scale), _dtype_code(k_cache.dtype), _stream_ptr(q.device)))
     return out
+
+
+def kv_cache_write_rope(k, v, slot_mapping, positions, cos_sin, k_cache, v_cache):
+    """kv_cache_write with the rotary embedding applied to the new keys:
+    token i at position positions[i] (int32 [T]; outside the table: skipped)
+    has each K row rotated by the angles of cos_sin (float32 [max_position,
+    rotary_dim]: per position the rotary_dim / 2 cosines, then the sines),
+    pairing dims j and j + rotary_dim / 2, in fp32 rounded to the pool
+    dtype.  V rows are stored unchanged."""
+    import torch
+
+    _require_gpu(k, v, slot_mapping, positions, cos_sin, k_cache, v_cache)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    NB, Hkv, bs, D = k_cache.shape
+    T = k.shape[0]
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, D) or t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} must be [T, {Hkv}, {D}] with contiguous heads")
+        if t.dtype != k_cache.dtype:
+            raise TypeError(f"{name} must have the pools' dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if positions.dtype != torch.int32 or positions.shape != (T,):
+        raise ValueError("positions must be int32 [T]")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2:
+        raise ValueError("cos_sin must be float32 [max_position, rotary_dim]")
+    cos_sin = cos_sin.contiguous()
+    _check(load_library().pka_kv_cache_write_rope(
+        k.data_ptr(), v.data_ptr(), k.stride(0), v.stride(0), slot_mapping.contiguous().data_ptr(),
+        positions.contiguous().data_ptr(), T, cos_sin.data_ptr(), cos_sin.shape[0],
+        cos_sin.shape[1], k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
+        _dtype_code(k_cache.dtype), _stream_ptr(k.device)))
 
 
 def _block_pools(k_cache, v_cache):

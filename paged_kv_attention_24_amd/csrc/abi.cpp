@@ -124,6 +124,56 @@ pka_status pka_kv_cache_write(const void *k, const void *v, int64_t k_token_stri
     return ok();
 }
 
+pka_status pka_kv_cache_write_rope(const void *k, const void *v, int64_t k_token_stride,
+                                   int64_t v_token_stride, const int64_t *slot_mapping,
+                                   const int32_t *positions, int32_t num_tokens,
+                                   const float *cos_sin, int32_t max_position, int32_t rotary_dim,
+                                   void *k_cache, void *v_cache, int32_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                   pka_dtype dtype, void *stream)
+{
+    if (valid_dtype(dtype)) {
+        const int vec = 16 / pka::dtype_bytes(to_internal(dtype));
+        if (rotary_dim <= 0 || rotary_dim > head_dim || rotary_dim % (2 * vec))
+            return fail(PKA_ERR_INVALID_ARGUMENT,
+                        "rotary_dim %d must be in (0, head_dim] and a multiple of %d", rotary_dim,
+                        2 * vec);
+    }
+    if (max_position <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "max_position must be positive");
+    // the checks of the plain write (they come first for the shapes)
+    const pka_status st = pka_kv_cache_write(nullptr, nullptr, k_token_stride, v_token_stride,
+                                             nullptr, 0, k_cache, v_cache, num_blocks,
+                                             block_size, num_kv_heads, head_dim, dtype, stream);
+    if (st != PKA_OK)
+        return st;
+    if (num_tokens < 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !slot_mapping || !positions || !cos_sin)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null k, v, slot_mapping, positions or cos_sin");
+    const int elt = pka::dtype_bytes(to_internal(dtype));
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (k_token_stride < row || v_token_stride < row)
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "token strides (%lld, %lld) must be >= num_kv_heads * head_dim = %lld",
+                    (long long)k_token_stride, (long long)v_token_stride, (long long)row);
+    if (!aligned16(k) || !aligned16(v) || (k_token_stride * elt) % 16 || (v_token_stride * elt) % 16)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "k/v rows must be 16-byte aligned");
+    pka::WriteArgs a{k, v, k_token_stride, v_token_stride, slot_mapping, num_tokens,
+                     k_cache, v_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                     to_internal(dtype)};
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.max_position = max_position;
+    a.rotary_dim = rotary_dim;
+    hipError_t e = pka::launch_kv_cache_write(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "kv_cache_write_rope launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                   int32_t max_context_len)
 {

@@ -21,6 +21,10 @@ struct WriteArgs {
     void *k_cache, *v_cache;
     int32_t num_blocks, block_size, num_kv_heads, head_dim;
     DType dtype;
+    // rotary embedding of the new keys (positions null: a plain write)
+    const int32_t *positions = nullptr;  // [num_tokens]
+    const float *cos_sin = nullptr;      // [max_position][rotary_dim]: cos, then sin
+    int32_t max_position = 0, rotary_dim = 0;
 };
 
 hipError_t launch_kv_cache_write(const WriteArgs &a, hipStream_t stream);

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strings():
     lib = pka.load_library()
-    assert lib.pka_abi_version() == 3
+    assert lib.pka_abi_version() == 4
     assert lib.pka_status_string(0) == b"ok"
     assert lib.pka_status_string(3) == b"workspace too small"
     assert lib.pka_status_string(99) == b"unknown status"
@@ -215,3 +215,31 @@ def test_block_moves_need_the_packed_buffer():
     assert lib.pka_gather_blocks(None, FAKE, FAKE, FAKE, 4, 10, 16384, None) == 1
     assert lib.pka_scatter_blocks(FAKE, FAKE, None, FAKE, 4, 10, 16384, None) == 1
     assert lib.pka_copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16384, None) == 0  # nothing to do
+
+
+def rope(**over):
+    a = dict(k=FAKE, v=FAKE, ks=512, vs=512, slots=FAKE, pos=FAKE, T=4, cs=FAKE, maxp=4096,
+             R=64, kc=FAKE, vc=FAKE, NB=10, bs=16, H=8, D=64, dt=1)
+    a.update(over)
+    lib = pka.load_library()
+    st = lib.pka_kv_cache_write_rope(a["k"], a["v"], a["ks"], a["vs"], a["slots"], a["pos"],
+                                     a["T"], a["cs"], a["maxp"], a["R"], a["kc"], a["vc"], a["NB"],
+                                     a["bs"], a["H"], a["D"], a["dt"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(R=0), 1), (dict(R=66), 1), (dict(R=24), 1), (dict(R=128), 1), (dict(maxp=0), 1),
+    (dict(pos=None), 1), (dict(cs=None), 1), (dict(slots=None), 1), (dict(T=-1), 1),
+    (dict(dt=7), 1), (dict(D=96, R=32), 2), (dict(bs=8), 2), (dict(kc=None), 1),
+    (dict(ks=100), 1), (dict(k=FAKE + 4), 1),
+])
+def test_rope_write_rejects(over, status):
+    st, msg = rope(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+def test_rope_write_fp32_allows_rotary_multiples_of_8():
+    assert rope(dt=0, R=24, T=0)[0] == 0   # fp32: 4 elements per 16 bytes -> multiples of 8
+    assert rope(dt=1, R=24, T=0)[0] == 1   # fp16: multiples of 16
