@@ -15,8 +15,9 @@
 // sequence).  Its 64 columns are (new token, query head) pairs: G heads of
 // 64 / G consecutive new tokens, 16 columns per wave.  It streams the
 // sequence's K and V from position 0 to the block's last position in chunks
-// (4 KiB of K and of V), which the waves copy by DMA (global_load_lds) into
-// two LDS buffers shared by the workgroup, one chunk ahead.  Per 16-token tile
+// (8 KiB of K and of V: two 1 KiB loads per wave and tensor, the measured
+// best against one and four), which the waves copy by DMA (global_load_lds)
+// into two LDS buffers shared by the workgroup, one chunk ahead.  Per 16-token tile
 // each wave computes
 //   S^T (16 tokens x 16 columns) = K_tile . Q^T        D/32 MFMAs 16x16x32
 //   the online softmax on S^T, with the causal bound t <= p applied per
@@ -32,6 +33,10 @@
 
 #include "cdna4.h"
 #include "pka_internal.h"
+
+#ifndef PKA_PREFILL_LOADS_PER_WAVE
+#define PKA_PREFILL_LOADS_PER_WAVE 2
+#endif
 
 namespace pka {
 namespace {
@@ -55,7 +60,8 @@ struct PShape {
     static constexpr int LPR = D * ELT / 16;  // lanes per token row
     static constexpr int TPL = kWave / LPR;   // token rows per 1 KiB wave load
     static constexpr int NW = 4;              // waves per workgroup
-    static constexpr int NL = NW;             // 1 KiB loads per tensor per chunk: one per wave
+    static constexpr int LPW = PKA_PREFILL_LOADS_PER_WAVE;  // 1 KiB loads per tensor per wave per chunk
+    static constexpr int NL = NW * LPW;       // 1 KiB loads per tensor per chunk
     static constexpr int CT = NL * TPL;       // tokens per chunk
     static constexpr int TPC = CT / 16;       // 16-token tiles per chunk
     static constexpr int KS = D / 32;         // 32-dim steps of QK^T
@@ -179,15 +185,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
     const int64_t head_off = (int64_t)h * S::TILE;
     const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
     auto stage_share = [&](int k, int buf) __attribute__((always_inline)) {
-        const int t0 = k * CT + w * TPL;
-        int bi = t0 / BS;
-        bi = bi < last_blk ? bi : last_blk;  // rows past the end re-read the last block
-        const int blk = block_id(bi);
-        const int64_t row = (int64_t)blk * block_stride + head_off + (t0 % BS) * R;
-        const int rr = w * TPL + tg;
-        const uint32_t kd = stage_lds + buf * (2 * CHUNK) + w * 1024;
-        load_to_lds(p.k_cache + row + tg * R + 16 * (cl ^ swk(rr)), kd);
-        load_to_lds(p.v_cache + row + tg * R + 16 * (cl ^ swv(rr)), kd + CHUNK);
+#pragma unroll
+        for (int l = 0; l < S::LPW; ++l) {
+            const int li = w * S::LPW + l;  // this load's index in the chunk
+            const int t0 = k * CT + li * TPL;
+            int bi = t0 / BS;
+            bi = bi < last_blk ? bi : last_blk;  // rows past the end re-read the last block
+            const int blk = block_id(bi);
+            const int64_t row = (int64_t)blk * block_stride + head_off + (t0 % BS) * R;
+            const int rr = li * TPL + tg;
+            const uint32_t kd = stage_lds + buf * (2 * CHUNK) + li * 1024;
+            load_to_lds(p.k_cache + row + tg * R + 16 * (cl ^ swk(rr)), kd);
+            load_to_lds(p.v_cache + row + tg * R + 16 * (cl ^ swv(rr)), kd + CHUNK);
+        }
     };
 
     float4_t O[MT];
@@ -203,12 +213,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
         char *vd = kd + CHUNK;
         const int tc = k * CT;
         wait_vmem();  // this wave's share of chunk k is in LDS
-        {
+        if (tc + CT > L) {
             // rows at or past L hold stale or NaN slots: zero their V (K is
-            // masked by selects)
-            const int t = tc + w * TPL + tg;
-            if (tc + CT > L && t >= L)
-                *reinterpret_cast<uint4 *>(vd + w * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+            // masked by selects); each wave clears the rows it staged
+#pragma unroll
+            for (int l = 0; l < S::LPW; ++l) {
+                const int li = w * S::LPW + l;
+                if (tc + li * TPL + tg >= L)
+                    *reinterpret_cast<uint4 *>(vd + li * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+            }
         }
         __syncthreads();  // every share landed; chunk k - 1's buffer is free
         const bool work = wave_any && tc <= wave_last;
