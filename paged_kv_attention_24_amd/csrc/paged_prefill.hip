@@ -37,6 +37,9 @@
 #ifndef PKA_PREFILL_LOADS_PER_WAVE
 #define PKA_PREFILL_LOADS_PER_WAVE 2
 #endif
+#ifndef PKA_PREFILL_COL_TILES
+#define PKA_PREFILL_COL_TILES 1
+#endif
 
 namespace pka {
 namespace {
@@ -69,7 +72,8 @@ struct PShape {
     static constexpr int R = D * ELT;         // bytes per token row
     static constexpr int CHUNK = NL * 1024;   // bytes of one tensor's chunk
     static constexpr int TILE = BS * D * ELT; // bytes of one (block, head) tile
-    static constexpr int QB = NW * 16 / G;    // new tokens per workgroup
+    static constexpr int NCT = PKA_PREFILL_COL_TILES;  // 16-column tiles per wave
+    static constexpr int QB = NW * NCT * 16 / G;  // new tokens per workgroup
     static_assert(TPC >= 1 && CT % 16 == 0, "a chunk holds whole 16-token tiles");
     static_assert(BS % TPL == 0, "a wave load stays inside one block");
 };
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
 {
     using S = PShape<T, D, BS, G>;
     constexpr int LPR = S::LPR, TPL = S::TPL, TPC = S::TPC, KS = S::KS, MT = S::MT, CT = S::CT;
-    constexpr int R = S::R, CHUNK = S::CHUNK;
+    constexpr int R = S::R, CHUNK = S::CHUNK, NCT = S::NCT;
     constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the reference max by
     __shared__ __attribute__((aligned(1024))) char stage[2 * 2 * CHUNK];  // [buffer][K, V]
 
@@ -101,26 +105,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
     L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
     const int base = L - nq;  // position of new token 0
 
-    // this lane's column: new token qi, query head h*G + g, position pos
-    const int col = 16 * w + n;
-    const int qi = q0 + col / G, g = col % G;
-    const bool col_ok = qi < nq && base + qi >= 0;
-    const int pos = base + qi;
+    // This lane's columns, one per column tile ct of the wave: new token
+    // qi[ct], query head h*G + g[ct], position pos[ct].
+    int qi[NCT], pos[NCT];
+    bool col_ok[NCT];
+    int64_t orow[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = 16 * (w * NCT + ct) + n;
+        qi[ct] = q0 + col / G;
+        pos[ct] = base + qi[ct];
+        col_ok[ct] = qi[ct] < nq && pos[ct] >= 0;
+        orow[ct] = ((int64_t)(r0 + qi[ct]) * p.num_q_heads + h * G + col % G) * D;
+    }
     // last position of the workgroup and of this wave (wave-uniform)
     const int qlast = (q0 + S::QB < nq ? q0 + S::QB : nq) - 1;
     const int n_tok = base + qlast + 1;  // tokens the workgroup streams
-    const int wq1 = q0 + (16 * w + 15) / G;
+    const int wq1 = q0 + (16 * NCT * (w + 1) - 1) / G;
     const int wave_last = base + (wq1 < nq ? wq1 : nq - 1);
-    const bool wave_any = q0 + (16 * w) / G < nq;
+    const bool wave_any = q0 + (16 * NCT * w) / G < nq;
 
-    const int64_t orow = ((int64_t)(r0 + qi) * p.num_q_heads + h * G + g) * D;
     if (n_tok <= 0) {
         // no token precedes any of these queries (more new tokens than cached
         // ones): zero rows
-        if (qi < nq)
-            for (int d = 4 * quad; d < D; d += 16)
-                for (int i = 0; i < 4; ++i)
-                    store_out(p.out, orow + d + i, 0.0f, p.out_kind);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            if (qi[ct] < nq)
+                for (int d = 4 * quad; d < D; d += 16)
+                    for (int i = 0; i < 4; ++i)
+                        store_out(p.out, orow[ct] + d + i, 0.0f, p.out_kind);
         return;
     }
     const int nch = (n_tok + CT - 1) / CT;
@@ -131,11 +144,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
     const float c = fabsf(p.scale_log2);
     const uint32_t qflip = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
 
-    // Q^T operand: column n, dims 32 st + 8 quad .. + 7
-    uint4 qop[KS];
-    {
-        // columns without a query read row 0 (in bounds) and are zeroed
-        const char *qrow = p.q + ((col_ok ? orow : 0) + 8 * quad) * S::ELT;
+    // Q^T operands: column n of each tile, dims 32 st + 8 quad .. + 7
+    // (columns without a query read row 0, in bounds, and are zeroed)
+    uint4 qop[NCT][KS];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const char *qrow = p.q + ((col_ok[ct] ? orow[ct] : 0) + 8 * quad) * S::ELT;
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
             uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * st * S::ELT);
@@ -143,7 +157,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
             v.y ^= qflip;
             v.z ^= qflip;
             v.w ^= qflip;
-            qop[st] = select4(col_ok, v, make_uint4(0, 0, 0, 0));
+            qop[ct][st] = select4(col_ok[ct], v, make_uint4(0, 0, 0, 0));
         }
     }
 
@@ -179,8 +193,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
         return __builtin_amdgcn_readlane(ids, bi - win0);
     };
 
-    // This wave's share of chunk k: token rows [k CT + w TPL, + TPL) of K
-    // and of V into buffer buf (lane l fills physical unit l % LPR of its row).
+    // This wave's share of chunk k: its LPW loads of K and of V (token rows
+    // [k CT + li TPL, + TPL) for load li) into buffer buf; lane l fills
+    // physical unit l % LPR of its row.
     const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(lds_address(stage));
     const int64_t head_off = (int64_t)h * S::TILE;
     const int64_t block_stride = (int64_t)p.num_kv_heads * S::TILE;
@@ -200,11 +215,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
         }
     };
 
-    float4_t O[MT];
+    float4_t O[NCT][MT];
+    float mref[NCT], lsum[NCT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        O[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float mref = -INFINITY, lsum = 0.0f;
+    for (int ct = 0; ct < NCT; ++ct) {
+        mref[ct] = -INFINITY;
+        lsum[ct] = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            O[ct][mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     stage_share(0, 0);
     for (int k = 0; k < nch; ++k) {
@@ -244,81 +264,90 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
             continue;
 #pragma unroll
         for (int t = 0; t < TPC; ++t) {
-            float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < KS; ++st)
-                sacc = mma_qk(T{}, kop[t][st], qop[st], sacc);
             const int tok0 = tc + 16 * t + 4 * quad;
-            bool ok[4];
-            float sv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ok[i] = col_ok && tok0 + i <= pos;
-                sv[i] = ok[i] ? sacc[i] : -INFINITY;
-            }
-            const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            if (__builtin_amdgcn_ballot_w64(mx * c > mref * c + kSlack)) {
-                // new reference: the column's maximum over its four lanes
-                float mh = fmaxf(mx, swz_xor16(mx));
-                mh = fmaxf(mh, xor32(mh));
-                const float mnew = fmaxf(mref, mh);
-                const float corr =
-                    mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mref - mnew) * c);
-                lsum *= corr;
+            for (int ct = 0; ct < NCT; ++ct) {
+                float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    O[mt] *= corr;
-                mref = mnew;
-            }
-            const float nmc = mref == -INFINITY ? 0.0f : -mref * c;
-            float pr[4];
+                for (int st = 0; st < KS; ++st)
+                    sacc = mma_qk(T{}, kop[t][st], qop[ct][st], sacc);
+                bool ok[4];
+                float sv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pr[i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(sv[i], c, nmc)) : 0.0f;
-            if constexpr (std::is_same<T, TF16>::value) {
-                const half2_t h01 = {(_Float16)pr[0], (_Float16)pr[1]};
-                const half2_t h23 = {(_Float16)pr[2], (_Float16)pr[3]};
-                const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
-                                            __builtin_bit_cast(uint32_t, h23));
-                lsum += ((float)h01.x + (float)h01.y) + ((float)h23.x + (float)h23.y);
+                for (int i = 0; i < 4; ++i) {
+                    ok[i] = col_ok[ct] && tok0 + i <= pos[ct];
+                    sv[i] = ok[i] ? sacc[i] : -INFINITY;
+                }
+                const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                if (__builtin_amdgcn_ballot_w64(mx * c > mref[ct] * c + kSlack)) {
+                    // new reference: the column's maximum over its four lanes
+                    float mh = fmaxf(mx, swz_xor16(mx));
+                    mh = fmaxf(mh, xor32(mh));
+                    const float mnew = fmaxf(mref[ct], mh);
+                    const float corr = mref[ct] == -INFINITY
+                                           ? 0.0f
+                                           : __builtin_amdgcn_exp2f((mref[ct] - mnew) * c);
+                    lsum[ct] *= corr;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    O[mt] = mma_pv(T{}, vop[t][mt], ph, O[mt]);
-            } else {
-                // P as a bf16 hi + lo pair: 16 significant bits
-                const bf162_t h01 = {(__bf16)pr[0], (__bf16)pr[1]};
-                const bf162_t h23 = {(__bf16)pr[2], (__bf16)pr[3]};
-                const bf162_t l01 = {(__bf16)(pr[0] - (float)h01.x), (__bf16)(pr[1] - (float)h01.y)};
-                const bf162_t l23 = {(__bf16)(pr[2] - (float)h23.x), (__bf16)(pr[3] - (float)h23.y)};
-                const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
-                                            __builtin_bit_cast(uint32_t, h23));
-                const uint2 pl = make_uint2(__builtin_bit_cast(uint32_t, l01),
-                                            __builtin_bit_cast(uint32_t, l23));
-                lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                    for (int mt = 0; mt < MT; ++mt)
+                        O[ct][mt] *= corr;
+                    mref[ct] = mnew;
+                }
+                const float nmc = mref[ct] == -INFINITY ? 0.0f : -mref[ct] * c;
+                float pr[4];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    O[mt] = mma_pv(T{}, vop[t][mt], ph, O[mt]);
-                    O[mt] = mma_pv(T{}, vop[t][mt], pl, O[mt]);
+                for (int i = 0; i < 4; ++i)
+                    pr[i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(sv[i], c, nmc)) : 0.0f;
+                if constexpr (std::is_same<T, TF16>::value) {
+                    const half2_t h01 = {(_Float16)pr[0], (_Float16)pr[1]};
+                    const half2_t h23 = {(_Float16)pr[2], (_Float16)pr[3]};
+                    const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                                __builtin_bit_cast(uint32_t, h23));
+                    lsum[ct] += ((float)h01.x + (float)h01.y) + ((float)h23.x + (float)h23.y);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        O[ct][mt] = mma_pv(T{}, vop[t][mt], ph, O[ct][mt]);
+                } else {
+                    // P as a bf16 hi + lo pair: 16 significant bits
+                    const bf162_t h01 = {(__bf16)pr[0], (__bf16)pr[1]};
+                    const bf162_t h23 = {(__bf16)pr[2], (__bf16)pr[3]};
+                    const bf162_t l01 = {(__bf16)(pr[0] - (float)h01.x),
+                                         (__bf16)(pr[1] - (float)h01.y)};
+                    const bf162_t l23 = {(__bf16)(pr[2] - (float)h23.x),
+                                         (__bf16)(pr[3] - (float)h23.y)};
+                    const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                                __builtin_bit_cast(uint32_t, h23));
+                    const uint2 pl = make_uint2(__builtin_bit_cast(uint32_t, l01),
+                                                __builtin_bit_cast(uint32_t, l23));
+                    lsum[ct] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        O[ct][mt] = mma_pv(T{}, vop[t][mt], ph, O[ct][mt]);
+                        O[ct][mt] = mma_pv(T{}, vop[t][mt], pl, O[ct][mt]);
+                    }
                 }
             }
         }
     }
 
-    // the column's sum over its four lanes, then the normalised row: lane
-    // holds dims 16 mt + 4 quad + i of its column
-    float lh = lsum + swz_xor16(lsum);
-    lh += xor32(lh);
-    if (qi < nq) {
-        const float inv = col_ok && lh > 0.0f ? 1.0f / lh : 0.0f;
+    // each column's sum over its four lanes, then the normalised rows: the
+    // lane holds dims 16 mt + 4 quad + i of its columns
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int64_t o = orow + 16 * mt + 4 * quad;
-            if (p.out_kind == 0) {
-                *reinterpret_cast<float4_t *>(static_cast<float *>(p.out) + o) = O[mt] * inv;
-            } else {
+    for (int ct = 0; ct < NCT; ++ct) {
+        float lh = lsum[ct] + swz_xor16(lsum[ct]);
+        lh += xor32(lh);
+        if (qi[ct] < nq) {
+            const float inv = col_ok[ct] && lh > 0.0f ? 1.0f / lh : 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    store_out(p.out, o + i, O[mt][i] * inv, p.out_kind);
+            for (int mt = 0; mt < MT; ++mt) {
+                const int64_t o = orow[ct] + 16 * mt + 4 * quad;
+                if (p.out_kind == 0) {
+                    *reinterpret_cast<float4_t *>(static_cast<float *>(p.out) + o) = O[ct][mt] * inv;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        store_out(p.out, o + i, O[ct][mt][i] * inv, p.out_kind);
+                }
             }
         }
     }
