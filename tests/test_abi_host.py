@@ -14,6 +14,18 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 FAKE = 0x10000
 
 
+def _no_gpu_visible():
+    import torch
+
+    return torch.cuda.device_count() == 0  # counts devices without initialising one
+
+
+# Calls with fake pointers run only where no GPU is visible: should a case
+# ever pass validation, it must not reach a device.
+fake_pointers = pytest.mark.skipif(not _no_gpu_visible(),
+                                   reason="fake-pointer ABI checks run on hosts without a GPU")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -47,6 +59,7 @@ def write(**over):
     return st, lib.pka_last_error().decode()
 
 
+@fake_pointers
 @pytest.mark.parametrize("over,status", [
     (dict(T=-1), 1), (dict(dt=7), 1), (dict(NB=0), 1), (dict(H=0), 1),
     (dict(D=96), 2), (dict(bs=8), 2), (dict(kc=None), 1), (dict(vc=FAKE + 8), 1),
@@ -59,14 +72,17 @@ def test_write_rejects(over, status):
     assert msg
 
 
+@fake_pointers
 def test_write_zero_tokens_is_ok_without_launch():
     st, _ = write(T=0, k=None, v=None, slots=None)
     assert st == 0
 
 
 def decode(**over):
-    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=64, cl=FAKE, B=16, Hq=32,
-             Hkv=8, D=64, NB=1000, bs=16, scale=0.125, kdt=1, maxl=1024, P=0, ws=FAKE,
+    # maxl 2048: several partitions, so a workspace is required (every case
+    # below must fail validation before any launch)
+    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=128, cl=FAKE, B=16, Hq=32,
+             Hkv=8, D=64, NB=1000, bs=16, scale=0.125, kdt=1, maxl=2048, P=0, ws=FAKE,
              wsb=1 << 30)
     a.update(over)
     lib = pka.load_library()
@@ -77,6 +93,7 @@ def decode(**over):
     return st, lib.pka_last_error().decode()
 
 
+@fake_pointers
 @pytest.mark.parametrize("over,status", [
     (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(NB=0), 1),
     (dict(MB=0), 1), (dict(B=-1), 1), (dict(D=80), 2), (dict(bs=64), 2), (dict(Hq=128), 2),
@@ -90,6 +107,7 @@ def test_decode_rejects(over, status):
     assert msg
 
 
+@fake_pointers
 def test_decode_empty_batch_is_ok_without_launch():
     st, _ = decode(B=0, out=None, q=None)
     assert st == 0
@@ -100,7 +118,10 @@ def test_partition_heuristic():
                         (256, 8, 32, 32768), (1, 1, 32, 5), (4096, 8, 16, 100)]:
         P = pka.decode_partition_size(B, H, bs, L)
         assert P % bs == 0 and bs <= P <= 1024, (B, H, bs, L, P)
-    assert pka.decode_partition_size(16, 8, 16, 1024) == 512
+    # batch 16 x 8 kv heads, up to 1024 tokens: one partition per sequence
+    assert pka.decode_partition_size(16, 8, 16, 1024) == 1024
+    assert pka.decode_partition_size(16, 8, 16, 1000) == 1008
+    assert pka.decode_partition_size(64, 8, 16, 1024) == 512   # pairs exceed the compute units
     assert pka.decode_partition_size(128, 8, 16, 8192) == 512
     # one long sequence: split finer so that the work items cover the GPU
     assert pka.decode_partition_size(1, 8, 16, 4096) == 128
@@ -136,9 +157,11 @@ def test_python_binding_refuses_cpu_tensors():
 
 
 def append(**over):
+    # maxl 2048: several partitions, so a workspace is required (every case
+    # below must fail validation before any launch)
     a = dict(out=FAKE, odt=0, q=FAKE, kn=FAKE, vn=FAKE, ks=512, vs=512, sl=FAKE, kc=FAKE,
-             vc=FAKE, bt=FAKE, MB=64, cl=FAKE, B=16, Hq=32, Hkv=8, D=64, NB=1000, bs=16,
-             scale=0.125, kdt=1, maxl=1024, P=0, ws=FAKE, wsb=1 << 30)
+             vc=FAKE, bt=FAKE, MB=128, cl=FAKE, B=16, Hq=32, Hkv=8, D=64, NB=1000, bs=16,
+             scale=0.125, kdt=1, maxl=2048, P=0, ws=FAKE, wsb=1 << 30)
     a.update(over)
     lib = pka.load_library()
     st = lib.pka_paged_attention_decode_append(
@@ -148,6 +171,7 @@ def append(**over):
     return st, lib.pka_last_error().decode()
 
 
+@fake_pointers
 @pytest.mark.parametrize("over,status", [
     (dict(kn=None), 1), (dict(vn=None), 1), (dict(sl=None), 1), (dict(ks=511), 1),
     (dict(vs=8), 1), (dict(kn=FAKE + 4), 1), (dict(ks=516), 1), (dict(D=96), 2),
@@ -171,6 +195,7 @@ def prefill(**over):
     return st, lib.pka_last_error().decode()
 
 
+@fake_pointers
 @pytest.mark.parametrize("over,status", [
     (dict(kdt=0), 2), (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1),
     (dict(NB=0), 1), (dict(MB=0), 1), (dict(B=-1), 1), (dict(N=-1), 1), (dict(D=96), 2),
@@ -184,11 +209,13 @@ def test_prefill_rejects(over, status):
     assert msg
 
 
+@fake_pointers
 def test_prefill_empty_is_ok_without_launch():
     assert prefill(B=0, out=None, q=None)[0] == 0
     assert prefill(N=0, out=None, q=None)[0] == 0
 
 
+@fake_pointers
 @pytest.mark.parametrize("fn", ["copy", "gather", "scatter"])
 @pytest.mark.parametrize("over,status", [
     (dict(n=-1), 1), (dict(nb=0), 1), (dict(bb=0), 1), (dict(bb=1000), 1), (dict(ids=None), 1),
@@ -210,6 +237,7 @@ def test_block_moves_reject(fn, over, status):
     assert lib.pka_last_error()
 
 
+@fake_pointers
 def test_block_moves_need_the_packed_buffer():
     lib = pka.load_library()
     assert lib.pka_gather_blocks(None, FAKE, FAKE, FAKE, 4, 10, 16384, None) == 1
@@ -228,6 +256,7 @@ def rope(**over):
     return st, lib.pka_last_error().decode()
 
 
+@fake_pointers
 @pytest.mark.parametrize("over,status", [
     (dict(R=0), 1), (dict(R=66), 1), (dict(R=24), 1), (dict(R=128), 1), (dict(maxp=0), 1),
     (dict(pos=None), 1), (dict(cs=None), 1), (dict(slots=None), 1), (dict(T=-1), 1),
@@ -240,6 +269,7 @@ def test_rope_write_rejects(over, status):
     assert msg
 
 
+@fake_pointers
 def test_rope_write_fp32_allows_rotary_multiples_of_8():
     assert rope(dt=0, R=24, T=0)[0] == 0   # fp32: 4 elements per 16 bytes -> multiples of 8
     assert rope(dt=1, R=24, T=0)[0] == 1   # fp16: multiples of 16
