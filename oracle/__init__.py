@@ -101,6 +101,15 @@ def _declare(h):
     h.oracle_scatter_blocks.argtypes = [P, P, P, P, i32, i32, i64]
     h.oracle_scatter_blocks.restype = ctypes.c_int
     h.oracle_kv_cache_write.restype = ctypes.c_int
+    h.oracle_quantize_group.argtypes = [P, i32, P]
+    h.oracle_quantize_group.restype = ctypes.c_float
+    h.oracle_kv_cache_write_int8.argtypes = [P, P, i64, i64, ctypes.c_int, P, i32, P, P, P, P,
+                                             i32, i32, i32, i32, i32]
+    h.oracle_kv_cache_write_int8.restype = ctypes.c_int
+    h.oracle_paged_attention_decode_int8.argtypes = [
+        P, P, ctypes.c_int, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f64, i32,
+        P, i32, i32]
+    h.oracle_paged_attention_decode_int8.restype = ctypes.c_int
     return h
 
 
@@ -383,3 +392,98 @@ def kv_cache_write_rope(k, v, slot_mapping, positions, cos_sin, k_cache, v_cache
         cs.shape[1], _ptr(k_cache), _ptr(v_cache), NB, bs, Hkv, D, DTYPE_CODE[dtype])
     if rc != 0:
         raise OracleError(f"oracle rope write failed: {STATUS.get(rc, rc)}")
+
+
+# ---------------------------------------------------------------------------
+# group-quantised INT8 KV cache (PhotonInfer README, "Technical details >
+# INT8 quantisation": groups of 32, 64 or 128; applied here to the KV rows)
+# ---------------------------------------------------------------------------
+
+def quantize_group(x, handle=None):
+    """One group of float32 values -> (int8 codes, float32 scale):
+    s = amax / 127 and c = rint(x / s) in float32 (ties to even)."""
+    h = handle or lib()
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(a.size, dtype=np.int8)
+    s = h.oracle_quantize_group(_ptr(a), a.size, _ptr(codes))
+    return codes, np.float32(s)
+
+
+def int8_pools(num_blocks, num_kv_heads, block_size, head_dim, group_size, fill_code=0,
+               fill_scale=np.nan):
+    """Empty INT8 pools: (k_codes [NB,Hkv,bs,D], v_codes [NB,Hkv,D,bs],
+    k_scales, v_scales [NB,Hkv,bs,D/group_size]) filled with the given values."""
+    G = head_dim // group_size
+    kc = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill_code, dtype=np.int8)
+    vc = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill_code, dtype=np.int8)
+    ks = np.full((num_blocks, num_kv_heads, block_size, G), fill_scale, dtype=np.float32)
+    vs = np.full((num_blocks, num_kv_heads, block_size, G), fill_scale, dtype=np.float32)
+    return kc, vc, ks, vs
+
+
+def _check_int8_pools(k_codes, v_codes, k_scales, v_scales):
+    NB, Hkv, bs, D = k_codes.shape
+    if k_codes.dtype != np.int8 or v_codes.dtype != np.int8 or v_codes.shape != (NB, Hkv, D, bs):
+        raise ValueError("k_codes int8 [NB,Hkv,bs,D] and v_codes int8 [NB,Hkv,D,bs] expected")
+    if k_scales.dtype != np.float32 or v_scales.shape != k_scales.shape or \
+            k_scales.shape[:3] != (NB, Hkv, bs) or D % k_scales.shape[3]:
+        raise ValueError("k_scales / v_scales float32 [NB,Hkv,bs,D/group] expected")
+    for a in (k_codes, v_codes, k_scales, v_scales):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("INT8 pools must be C-contiguous")
+    return NB, Hkv, bs, D, D // k_scales.shape[3]
+
+
+def kv_cache_write_int8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, dtype,
+                        handle=None) -> None:
+    """In-place quantised write of k, v [T, Hkv, D] (stored bits of ``dtype``)
+    into the INT8 pools at ``slot_mapping``."""
+    h = handle or lib()
+    NB, Hkv, bs, D, gs = _check_int8_pools(k_codes, v_codes, k_scales, v_scales)
+    want = np.float32 if dtype == "f32" else np.uint16
+    T = k.shape[0]
+    item = k.itemsize
+    for a in (k, v):
+        if a.dtype != want or a.shape[1:] != (Hkv, D) or a.strides[2] != item or \
+                a.strides[1] != D * item:
+            raise ValueError("k/v must be [T, Hkv, D] stored bits with contiguous heads")
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    rc = h.oracle_kv_cache_write_int8(
+        _ptr(k), _ptr(v), k.strides[0] // item if T else Hkv * D,
+        v.strides[0] // item if T else Hkv * D, DTYPE_CODE[dtype], _ptr(sm), T, _ptr(k_codes),
+        _ptr(v_codes), _ptr(k_scales), _ptr(v_scales), NB, bs, Hkv, D, gs)
+    if rc != 0:
+        raise OracleError(f"oracle INT8 write failed: {STATUS.get(rc, rc)}")
+
+
+def paged_attention_decode_int8(q, q_dtype, k_codes, v_codes, k_scales, v_scales, block_tables,
+                                context_lens, scale, num_kv_heads, block_size, *, rows=None,
+                                partition_size: int = 0, threads: int = 0,
+                                handle=None) -> np.ndarray:
+    """fp64 decode over INT8 pools (values code * scale); q [B, Hq, D] holds
+    stored bits of ``q_dtype``.  ``rows``, ``partition_size`` and ``threads``
+    as for paged_attention_decode."""
+    h = handle or lib()
+    _check_stored(q, q_dtype, "q")
+    NB, Hkv, bs, D, gs = _check_int8_pools(k_codes, v_codes, k_scales, v_scales)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, D2 = q.shape
+    if D2 != D or Hkv != num_kv_heads or bs != block_size:
+        raise ValueError("pool shape does not match the arguments")
+    if bt.ndim != 2 or bt.shape[0] != B or cl.shape != (B,):
+        raise ValueError("block_tables / context_lens do not match q")
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        out = np.empty((r.shape[0], D), dtype=np.float64)
+        rp, nr = _ptr(r), r.shape[0]
+    else:
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    rc = h.oracle_paged_attention_decode_int8(
+        _ptr(out), _ptr(q), DTYPE_CODE[q_dtype], _ptr(k_codes), _ptr(v_codes), _ptr(k_scales),
+        _ptr(v_scales), _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, Hkv, D, NB, bs, gs,
+        float(scale), int(partition_size), rp, nr, int(threads))
+    if rc != 0:
+        raise OracleError(f"oracle INT8 decode failed: {STATUS.get(rc, rc)}")
+    return out

@@ -113,7 +113,18 @@ typedef struct {
     int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
     int32_t num_blocks, block_size;
     double scale;
+    /* group-quantised INT8 pools (k_codes non-NULL): the K and V values are
+     * code * scale (see the INT8 section below); q then has dtype q_dtype */
+    const int8_t *k_codes, *v_codes;
+    const float *k_scales, *v_scales;
+    int32_t group_size;
+    int q_dtype;
 } decode_args;
+
+/* Element dtype of q: the pools' dtype, or q_dtype over INT8 pools. */
+static int query_dtype(const decode_args *a) { return a->k_codes ? a->q_dtype : a->dtype; }
+
+static double int8_kv_elem(const decode_args *a, int is_value, int64_t blk, int h, int off, int d);
 
 /* Index of element (block, head, offset, d) in a pool. */
 static int64_t pool_index(const decode_args *a, int64_t block, int h, int off, int d)
@@ -153,6 +164,8 @@ static double kv_elem(const decode_args *a, int is_value, int b, int h, int64_t 
     }
     int64_t blk = block_of(a, b, t);
     int off = (int)(t % a->block_size);
+    if (a->k_codes)
+        return int8_kv_elem(a, is_value, blk, h, off, d);
     return load_elem(is_value ? a->v_cache : a->k_cache, a->dtype, pool_index(a, blk, h, off, d));
 }
 
@@ -164,7 +177,7 @@ static void logits(const decode_args *a, int b, int hq, int h, int64_t t0, int64
     for (int64_t t = t0; t < t1; ++t) {
         double dot = 0.0;
         for (int d = 0; d < a->head_dim; ++d)
-            dot += load_elem(a->q, a->dtype, qbase + d) * kv_elem(a, 0, b, h, t, d);
+            dot += load_elem(a->q, query_dtype(a), qbase + d) * kv_elem(a, 0, b, h, t, d);
         s[t - t0] = a->scale * dot;
     }
 }
@@ -254,6 +267,9 @@ static int decode_row(const decode_args *a, int b, int hq, int32_t partition_siz
     return ORACLE_OK;
 }
 
+static int decode_rows(const decode_args *ap, int32_t partition_size, const int32_t *rows,
+                       int32_t n_rows, int32_t num_threads, double *out);
+
 /*
  * Decode every (sequence, q head) row, or only the rows listed in `rows`
  * (n_rows pairs b, hq; then out is [n_rows, head_dim]).  out is double.
@@ -279,6 +295,15 @@ static int decode_all(double *out, const void *q, const void *k_cache, const voi
     decode_args a = {q, k_cache, v_cache, k_new, v_new, k_new_stride, v_new_stride,
                      dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, scale};
+    return decode_rows(&a, partition_size, rows, n_rows, num_threads, out);
+}
+
+/* decode_row for every row (or the listed rows) of the arguments in a. */
+static int decode_rows(const decode_args *ap, int32_t partition_size, const int32_t *rows,
+                       int32_t n_rows, int32_t num_threads, double *out)
+{
+    const decode_args a = *ap;
+    const int32_t num_seqs = a.num_seqs, num_q_heads = a.num_q_heads, head_dim = a.head_dim;
     int64_t n = rows ? n_rows : (int64_t)num_seqs * num_q_heads;
     if (rows) {
         for (int64_t r = 0; r < n; ++r)
@@ -384,7 +409,7 @@ static int prefill_row(const decode_args *a, const int32_t *query_start, int64_t
     for (int64_t t = 0; t < n; ++t) {
         double acc = 0.0;
         for (int e = 0; e < a->head_dim; ++e)
-            acc += load_elem(a->q, a->dtype, qbase + e) * kv_elem(a, 0, b, kvh, t, e);
+            acc += load_elem(a->q, query_dtype(a), qbase + e) * kv_elem(a, 0, b, kvh, t, e);
         s[t] = a->scale * acc;
     }
     double m, l;
@@ -711,4 +736,191 @@ void oracle_round_array(const float *src, int dtype, int64_t n, uint16_t *dst)
 {
     for (int64_t i = 0; i < n; ++i)
         dst[i] = dtype == ORACLE_F16 ? oracle_f32_to_f16(src[i]) : oracle_f32_to_bf16(src[i]);
+}
+
+/* ---------------------------------------------------------------------------
+ * Group-quantised INT8 KV cache.
+ *
+ * PhotonInfer README (Korean translation), "Key features > GPU-optimised
+ * kernels" and "Technical details > INT8 quantisation": quantisation to INT8
+ * in groups, with a configurable group size of 32, 64 or 128.  The README
+ * applies it to weights; here the same scheme stores the KV cache (a
+ * reading: the pages do not quantise KV).  Each new token's row of one kv
+ * head is cut into head_dim / group_size groups of consecutive elements, and
+ * each group is stored as
+ *
+ *     amax = max_i |x_i|                   (float32, from the exact inputs)
+ *     s    = amax / 127                    (one float32 division)
+ *     c_i  = rint(x_i / s)                 (float32 division, ties to even)
+ *
+ * with c_i in [-127, 127] (s = 0 gives c_i = 0).  The cached value stands
+ * for c_i * s.  Inputs are finite (non-finite inputs leave the codes
+ * unspecified).
+ *
+ * Layouts (one physical block of one kv head is contiguous in each array):
+ *   k_codes   int8    [num_blocks][num_kv_heads][block_size][head_dim]
+ *   v_codes   int8    [num_blocks][num_kv_heads][head_dim][block_size]
+ *   k_scales, v_scales
+ *             float32 [num_blocks][num_kv_heads][block_size][head_dim/group_size]
+ * V's codes are dim-major inside a block: the block_size codes of one
+ * dimension are adjacent.
+ * ------------------------------------------------------------------------- */
+
+static int64_t int8_code_index(const decode_args *a, int is_value, int64_t blk, int h, int off,
+                               int d)
+{
+    int64_t base = (blk * a->num_kv_heads + h) * (int64_t)a->block_size * a->head_dim;
+    return is_value ? base + (int64_t)d * a->block_size + off
+                    : base + (int64_t)off * a->head_dim + d;
+}
+
+static int64_t int8_scale_index(int32_t num_kv_heads, int32_t block_size, int32_t groups,
+                                int64_t blk, int h, int off, int g)
+{
+    return ((blk * num_kv_heads + h) * block_size + off) * groups + g;
+}
+
+/* The value an INT8 pool holds for element d: code * scale, in double. */
+static double int8_kv_elem(const decode_args *a, int is_value, int64_t blk, int h, int off, int d)
+{
+    const int8_t *codes = is_value ? a->v_codes : a->k_codes;
+    const float *scales = is_value ? a->v_scales : a->k_scales;
+    int groups = a->head_dim / a->group_size;
+    double c = (double)codes[int8_code_index(a, is_value, blk, h, off, d)];
+    double s = (double)scales[int8_scale_index(a->num_kv_heads, a->block_size, groups, blk, h, off,
+                                               d / a->group_size)];
+    return c * s;
+}
+
+/* One group: n float32 values -> n codes and the group's scale. */
+float oracle_quantize_group(const float *x, int32_t n, int8_t *codes)
+{
+    float amax = 0.0f;
+    for (int32_t i = 0; i < n; ++i) {
+        float m = fabsf(x[i]);
+        if (m > amax)
+            amax = m;
+    }
+    float s = amax / 127.0f;
+    for (int32_t i = 0; i < n; ++i) {
+        float c = s > 0.0f ? rintf(x[i] / s) : 0.0f;
+        if (c > 127.0f)
+            c = 127.0f;
+        if (c < -127.0f)
+            c = -127.0f;
+        codes[i] = (int8_t)c;
+    }
+    return s;
+}
+
+/*
+ * The batched write into INT8 pools: for each new token i whose slot
+ * s = slot_mapping[i] lies in [0, num_blocks * block_size) (others are
+ * skipped), every kv head's K and V rows (dtype elements, token strides in
+ * elements, heads head_dim apart) are quantised group by group and stored at
+ * block s / block_size, offset s % block_size of the four arrays.  Every
+ * other byte is left as it was.
+ */
+int oracle_kv_cache_write_int8(const void *k, const void *v, int64_t k_token_stride,
+                               int64_t v_token_stride, int dtype, const int64_t *slot_mapping,
+                               int32_t num_tokens, int8_t *k_codes, int8_t *v_codes,
+                               float *k_scales, float *v_scales, int32_t num_blocks,
+                               int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t group_size)
+{
+    if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || group_size <= 0 || head_dim % group_size || dtype < ORACLE_F32 ||
+        dtype > ORACLE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    if (num_tokens > 0 && (!k || !v || !slot_mapping || !k_codes || !v_codes || !k_scales ||
+                           !v_scales))
+        return ORACLE_BAD_ARGUMENT;
+    decode_args a;
+    memset(&a, 0, sizeof a);
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    int groups = head_dim / group_size;
+    float *x = (float *)malloc(sizeof(float) * (size_t)group_size);
+    int8_t *c = (int8_t *)malloc((size_t)group_size);
+    if (!x || !c) {
+        free(x); free(c);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int64_t s = slot_mapping[i];
+        if (s < 0 || s >= (int64_t)num_blocks * block_size)
+            continue;
+        int64_t blk = s / block_size;
+        int off = (int)(s % block_size);
+        for (int h = 0; h < num_kv_heads; ++h) {
+            for (int is_value = 0; is_value < 2; ++is_value) {
+                const void *src = is_value ? v : k;
+                int64_t row = (int64_t)i * (is_value ? v_token_stride : k_token_stride) +
+                              (int64_t)h * head_dim;
+                int8_t *codes = is_value ? v_codes : k_codes;
+                float *scales = is_value ? v_scales : k_scales;
+                for (int g = 0; g < groups; ++g) {
+                    for (int e = 0; e < group_size; ++e)
+                        x[e] = (float)load_elem(src, dtype, row + (int64_t)g * group_size + e);
+                    scales[int8_scale_index(num_kv_heads, block_size, groups, blk, h, off, g)] =
+                        oracle_quantize_group(x, group_size, c);
+                    for (int e = 0; e < group_size; ++e)
+                        codes[int8_code_index(&a, is_value, blk, h, off, g * group_size + e)] = c[e];
+                }
+            }
+        }
+    }
+    free(x);
+    free(c);
+    return ORACLE_OK;
+}
+
+/*
+ * Decode over INT8 pools: the plain definition evaluated on the values the
+ * pools stand for (code * scale, exact in double), with q stored as q_dtype
+ * (float32, fp16 or bf16 bits).  Row selection, partition_size
+ * and threads as for oracle_paged_attention_decode.
+ */
+int oracle_paged_attention_decode_int8(double *out, const void *q, int q_dtype,
+                                       const int8_t *k_codes, const int8_t *v_codes,
+                                       const float *k_scales, const float *v_scales,
+                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t num_blocks, int32_t block_size, int32_t group_size,
+                                       double scale, int32_t partition_size, const int32_t *rows,
+                                       int32_t n_rows, int32_t num_threads)
+{
+    if (!out || !q || !k_codes || !v_codes || !k_scales || !v_scales || !block_tables ||
+        !context_lens)
+        return ORACLE_BAD_ARGUMENT;
+    if (q_dtype < ORACLE_F32 || q_dtype > ORACLE_BF16 || num_seqs < 0 || num_kv_heads <= 0 ||
+        num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 ||
+        group_size <= 0 || head_dim % group_size || block_size <= 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return ORACLE_BAD_ARGUMENT;
+    decode_args a;
+    memset(&a, 0, sizeof a);
+    a.q = q;
+    a.k_cache = k_codes;
+    a.v_cache = v_codes;
+    a.dtype = q_dtype;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.scale = scale;
+    a.k_codes = k_codes;
+    a.v_codes = v_codes;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.group_size = group_size;
+    a.q_dtype = q_dtype;
+    return decode_rows(&a, partition_size, rows, n_rows, num_threads, out);
 }

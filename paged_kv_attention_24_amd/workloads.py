@@ -368,6 +368,127 @@ def make_prefill_config(n: int, *, seed: Optional[int] = None, poison: bool = Tr
 # ---------------------------------------------------------------------------
 # Device transfer (data movement only)
 # ---------------------------------------------------------------------------
+# Group-quantised INT8 pools (codes and per-group float32 scales)
+# ---------------------------------------------------------------------------
+
+INT8_POISON_CODE = -128  # never produced by the quantiser (codes lie in [-127, 127])
+
+
+@dataclass
+class Int8Workload(Workload):
+    """Decode inputs over INT8 pools.  ``dtype`` is the dtype of q (and of
+    the new tokens); k_cache / v_cache are unused (None).  Layouts:
+    k_codes int8 [NB, Hkv, bs, D]; v_codes int8 [NB, Hkv, D, bs] (dim-major
+    inside a block); k_scales, v_scales float32 [NB, Hkv, bs, D / group_size]."""
+
+    group_size: int = 0
+    k_codes: Optional[np.ndarray] = None
+    v_codes: Optional[np.ndarray] = None
+    k_scales: Optional[np.ndarray] = None
+    v_scales: Optional[np.ndarray] = None
+
+    def kv_bytes(self) -> int:
+        """Codes and scales a decode must stream: per token and kv head,
+        2 * D one-byte codes and 2 * D / group_size four-byte scales."""
+        total_tokens = int(self.context_lens.astype(np.int64).clip(min=0).sum())
+        per = 2 * self.head_dim + 2 * (self.head_dim // self.group_size) * 4
+        return total_tokens * self.num_kv_heads * per
+
+
+def make_int8_case(seed: int, *, q_dtype: str, context_lens: Sequence[int], num_q_heads: int,
+                   num_kv_heads: int, head_dim: int, block_size: int, group_size: int,
+                   pool_blocks: Optional[int] = None, pool_factor: float = 1.25,
+                   scale: Optional[float] = None, write: bool = True, poison: bool = True,
+                   max_blocks_per_seq: Optional[int] = None, name: str = "int8-case",
+                   rng: Optional[np.random.Generator] = None,
+                   scale_range=(0.005, 0.03)) -> Int8Workload:
+    """Like make_case, with INT8 pools in place of the half/fp32 ones.
+
+    Draw order: steps 1, 2, 5, 6 of make_case (lengths, pool permutation, q
+    and the new tokens, all in q_dtype), then 7. the K codes, 8. the V codes
+    (uniform integers in [-127, 127]), 9. the K scales, 10. the V scales
+    (float32 uniform in ``scale_range``).  With ``poison`` every scale of an
+    unused block, of the tail slots >= L_b and of the slot the write will
+    fill is NaN, and the codes there are INT8_POISON_CODE."""
+    if head_dim % group_size:
+        raise ValueError("group_size must divide head_dim")
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    base = make_case(seed, dtype=q_dtype, context_lens=context_lens, num_q_heads=num_q_heads,
+                     num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                     pool_blocks=pool_blocks, pool_factor=pool_factor, scale=scale, write=write,
+                     poison=False, max_blocks_per_seq=max_blocks_per_seq, name=name, rng=rng,
+                     pools=False)
+    NB, Hkv, bs, D = base.num_blocks, num_kv_heads, block_size, head_dim
+    ng = D // group_size
+    k_codes = rng.integers(-127, 128, size=(NB, Hkv, bs, D), dtype=np.int8)
+    v_codes = rng.integers(-127, 128, size=(NB, Hkv, D, bs), dtype=np.int8)
+    lo, hi = scale_range
+    k_scales = rng.uniform(lo, hi, size=(NB, Hkv, bs, ng)).astype(np.float32)
+    v_scales = rng.uniform(lo, hi, size=(NB, Hkv, bs, ng)).astype(np.float32)
+    if poison:
+        lens = base.context_lens.astype(np.int64)
+        nblk = np.where(lens > 0, (lens + bs - 1) // bs, 0)
+        in_use = np.zeros(NB, dtype=bool)
+        for b in range(base.num_seqs):
+            in_use[base.block_tables[b, : nblk[b]]] = True
+        dead = np.zeros((NB, bs), dtype=bool)
+        dead[~in_use] = True
+        for b in range(base.num_seqs):
+            n = int(nblk[b])
+            if n:
+                dead[int(base.block_tables[b, n - 1]), int(lens[b]) - (n - 1) * bs:] = True
+        if write:
+            for s in base.slot_mapping:
+                if s >= 0:
+                    dead[int(s) // bs, int(s) % bs] = True
+        blk, off = np.nonzero(dead)
+        k_scales[blk, :, off, :] = np.nan
+        v_scales[blk, :, off, :] = np.nan
+        k_codes[blk, :, off, :] = INT8_POISON_CODE
+        v_codes[blk, :, :, off] = INT8_POISON_CODE
+    fields = {f: getattr(base, f) for f in Workload.__dataclass_fields__}
+    return Int8Workload(**fields, group_size=group_size, k_codes=k_codes, v_codes=v_codes,
+                        k_scales=k_scales, v_scales=v_scales)
+
+
+def make_int8_config(cfg: int, *, group_size: int = 32, seed: Optional[int] = None,
+                     poison: bool = True, write: bool = True) -> Int8Workload:
+    """Named workload ``cfg`` (1..5) over INT8 pools: its lengths, shapes and
+    pool permutation, with q in the workload's dtype (fp32 for workload 1)."""
+    seed = cfg if seed is None else seed
+    rng = np.random.default_rng(seed)
+    lens = config_lens(cfg, rng)
+    shape = dict(CONFIG_SHAPES[cfg])
+    q_dtype = shape.pop("dtype")
+    shape.pop("partition_size", None)
+    wl = make_int8_case(seed, q_dtype=q_dtype, context_lens=lens, group_size=group_size,
+                        poison=poison, write=write, rng=rng, name=f"cfg{cfg}-int8", **shape)
+    wl.meta["config"] = cfg
+    wl.meta["description"] = CONFIG_NAMES[cfg] + f", INT8 KV (groups of {group_size})"
+    return wl
+
+
+def int8_device_inputs(wl: Int8Workload, device="cuda"):
+    """The INT8 workload's arrays as device tensors."""
+    import torch
+
+    d = dict(
+        q=as_torch(wl.q, wl.dtype, device),
+        k_codes=torch.from_numpy(wl.k_codes).to(device),
+        v_codes=torch.from_numpy(wl.v_codes).to(device),
+        k_scales=torch.from_numpy(wl.k_scales).to(device),
+        v_scales=torch.from_numpy(wl.v_scales).to(device),
+        block_tables=torch.from_numpy(wl.block_tables).to(device),
+        context_lens=torch.from_numpy(wl.context_lens).to(device),
+    )
+    if wl.new_k is not None:
+        d["new_k"] = as_torch(wl.new_k, wl.dtype, device)
+        d["new_v"] = as_torch(wl.new_v, wl.dtype, device)
+        d["slot_mapping"] = torch.from_numpy(wl.slot_mapping).to(device)
+    return d
+
+
+# ---------------------------------------------------------------------------
 
 def torch_dtype(dtype: str):
     import torch

@@ -640,6 +640,197 @@ def pin_rope_identity_and_skip(h):
         assert kc3[blk, :, off].any() == (0 <= p < 16)
 
 
+
+# ---------------------------------------------------------------------------
+# group-quantised INT8 KV cache
+# ---------------------------------------------------------------------------
+
+def int8_dequantized(wl):
+    """fp64 K and V pools [NB, Hkv, bs, D] from the INT8 arrays, read through
+    the documented layouts (K codes token-major, V codes dim-major, one
+    float32 scale per group of group_size consecutive dims)."""
+    gs = wl.group_size
+    ks = np.repeat(wl.k_scales.astype(np.float64), gs, axis=3)
+    vs = np.repeat(wl.v_scales.astype(np.float64), gs, axis=3)
+    k = wl.k_codes.astype(np.float64) * ks
+    v = np.transpose(wl.v_codes, (0, 1, 3, 2)).astype(np.float64) * vs
+    return k, v
+
+
+def int8_sdpa_reference(wl):
+    """torch fp64 SDPA per sequence over the dequantized, gathered K/V."""
+    kc, vc = int8_dequantized(wl)
+    out = np.zeros((wl.num_seqs, wl.num_q_heads, wl.head_dim))
+    for b in range(wl.num_seqs):
+        if wl.context_lens[b] == 0:
+            continue
+        K = torch.from_numpy(gather(wl, kc, b)).permute(1, 0, 2)[None]
+        V = torch.from_numpy(gather(wl, vc, b)).permute(1, 0, 2)[None]
+        Q = torch.from_numpy(f64(wl.q[b], wl.dtype))[None, :, None, :]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            Q, K.contiguous(), V.contiguous(), scale=float(wl.scale), enable_gqa=True)
+        out[b] = o[0, :, 0, :].numpy()
+    return out
+
+
+def run_int8(h, wl, **kw):
+    return oracle.paged_attention_decode_int8(
+        wl.q, wl.dtype, wl.k_codes, wl.v_codes, wl.k_scales, wl.v_scales, wl.block_tables,
+        wl.context_lens, wl.scale, wl.num_kv_heads, wl.block_size, handle=h, **kw)
+
+
+def int8_case(seed, q_dtype="f16", lens=(5, 37, 16, 1, 33), Hq=4, Hkv=2, D=64, bs=16, gs=32,
+              **kw):
+    return W.make_int8_case(seed, q_dtype=q_dtype, context_lens=lens, num_q_heads=Hq,
+                            num_kv_heads=Hkv, head_dim=D, block_size=bs, group_size=gs,
+                            write=False, **kw)
+
+
+def pin_int8_quantize_bounds(h):
+    """P-q1: for groups of many magnitudes, every code lies in [-127, 127],
+    |c * s - x| <= s / 2 (plus the float32 division's rounding), the
+    largest-magnitude element gets code +-127, s * 127 equals amax to float32
+    rounding, and codes keep the sign and order of their inputs."""
+    rng = np.random.default_rng(61)
+    for n in (32, 64, 128):
+        for mag in (1e-30, 1e-6, 1.0, 3.0e3, 1e30):
+            x = (rng.standard_normal(n) * mag).astype(np.float32)
+            c, s = oracle.quantize_group(x, handle=h)
+            amax = np.max(np.abs(x.astype(np.float64)))
+            assert np.all(np.abs(c.astype(np.int32)) <= 127)
+            assert abs(float(s) * 127.0 - amax) <= amax * 2.0 ** -23, (n, mag)
+            err = np.abs(c.astype(np.float64) * float(s) - x.astype(np.float64))
+            assert np.all(err <= float(s) * (0.5 + 1e-5)), (n, mag, err.max() / s)
+            i = int(np.argmax(np.abs(x)))
+            assert abs(int(c[i])) == 127 and np.sign(c[i]) == np.sign(x[i])
+            assert np.all((c == 0) | (np.sign(c) == np.sign(x)))
+            order = np.argsort(x, kind="stable")
+            assert np.all(np.diff(c[order].astype(np.int32)) >= 0)
+
+
+def pin_int8_quantize_exact_grid(h):
+    """P-q2: closed forms.  Values k * 2^e with integer k and max |k| = 127
+    give codes k and scale 2^e exactly; halfway values (k + 1/2) * 2^e round
+    to the even neighbour; an all-zero group gives scale 0 and codes 0; a
+    group with one non-zero value a gives +-127 there, 0 elsewhere and
+    s = |a| / 127."""
+    rng = np.random.default_rng(62)
+    for e in (-20, -3, 0, 5):
+        k = rng.integers(-127, 128, size=32)
+        k[7] = -127
+        c, s = oracle.quantize_group((k * 2.0 ** e).astype(np.float32), handle=h)
+        assert float(s) == 2.0 ** e and np.array_equal(c.astype(np.int64), k), e
+        half = np.array([127, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, 126.5, -125.5], np.float64)
+        c, s = oracle.quantize_group((half * 2.0 ** e).astype(np.float32), handle=h)
+        assert float(s) == 2.0 ** e
+        assert list(c) == [127, 2, 4, -2, -4, 0, 0, 2, 126, -126], (e, list(c))
+    c, s = oracle.quantize_group(np.zeros(64, np.float32), handle=h)
+    assert float(s) == 0.0 and not c.any()
+    x = np.zeros(64, np.float32)
+    x[9] = -0.3
+    c, s = oracle.quantize_group(x, handle=h)
+    assert c[9] == -127 and np.count_nonzero(c) == 1
+    assert s == np.float32(np.float32(0.3) / np.float32(127))
+
+
+def pin_int8_write_layout(h):
+    """P-q3: the quantised write stores, for each written token and head,
+    codes and scales at the documented places (K token-major, V dim-major,
+    scales [blk, h, off, d // group]) whose product is within s / 2 of the
+    input; skipped slots and every other byte keep their sentinels; the
+    order of distinct slots does not matter."""
+    for dtype, D, gs, bs in (("f16", 64, 32, 16), ("bf16", 128, 64, 32), ("f32", 128, 128, 16)):
+        rng = np.random.default_rng(63 + D + gs)
+        T, Hkv, NB = 9, 3, 7
+        k = W._round_to_dtype(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 2, dtype)
+        v = W._round_to_dtype(rng.standard_normal((T, Hkv, D), dtype=np.float32), dtype)
+        slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+        slots[2], slots[5] = -1, NB * bs + 3  # padding and out of the pool
+        pools = oracle.int8_pools(NB, Hkv, bs, D, gs, fill_code=W.INT8_POISON_CODE)
+        oracle.kv_cache_write_int8(k, v, slots, *pools, dtype, handle=h)
+        kc, vc, ks, vs = pools
+        written = np.zeros((NB, bs), dtype=bool)
+        for i, sl in enumerate(slots):
+            if not 0 <= sl < NB * bs:
+                continue
+            blk, off = divmod(int(sl), bs)
+            written[blk, off] = True
+            for name, x, codes, sc in (("k", k, kc[blk, :, off, :], ks[blk, :, off, :]),
+                                       ("v", v, vc[blk, :, :, off], vs[blk, :, off, :])):
+                xv = f64(x[i], dtype)  # [Hkv, D]
+                srep = np.repeat(sc.astype(np.float64), gs, axis=1)
+                err = np.abs(codes.astype(np.float64) * srep - xv)
+                assert np.all(err <= srep * (0.5 + 1e-5)), (dtype, name)
+                amax = np.abs(xv).reshape(Hkv, D // gs, gs).max(axis=2)
+                assert np.allclose(sc.astype(np.float64) * 127, amax, rtol=2.0 ** -22, atol=0)
+        blk, off = np.nonzero(~written)
+        assert np.all(kc[blk, :, off, :] == W.INT8_POISON_CODE)
+        assert np.all(vc[blk, :, :, off] == W.INT8_POISON_CODE)
+        assert np.all(np.isnan(ks[blk, :, off, :])) and np.all(np.isnan(vs[blk, :, off, :]))
+        perm = rng.permutation(T)
+        pools2 = oracle.int8_pools(NB, Hkv, bs, D, gs, fill_code=W.INT8_POISON_CODE)
+        oracle.kv_cache_write_int8(np.ascontiguousarray(k[perm]), np.ascontiguousarray(v[perm]),
+                                   slots[perm], *pools2, dtype, handle=h)
+        for a, b2 in zip(pools, pools2):
+            assert a.tobytes() == b2.tobytes()
+
+
+def pin_int8_decode_sdpa(h):
+    """P-q4: decode over INT8 pools == torch fp64 SDPA on the dequantized,
+    gathered K/V (the survey's dequantize-then-attend reading), over q dtypes,
+    group sizes, head dims, block sizes and GQA groups; poisoned tail and
+    unused slots never reach the output."""
+    cases = [
+        dict(q_dtype="f16", lens=(5, 37, 16, 1, 33), Hq=4, Hkv=2, D=64, bs=16, gs=32),
+        dict(q_dtype="bf16", lens=(33, 7, 50), Hq=8, Hkv=4, D=128, bs=32, gs=64),
+        dict(q_dtype="bf16", lens=(70, 2), Hq=16, Hkv=8, D=128, bs=16, gs=128),
+        dict(q_dtype="f32", lens=(40, 3), Hq=32, Hkv=4, D=64, bs=16, gs=64),
+        dict(q_dtype="f16", lens=(100,), Hq=8, Hkv=8, D=128, bs=16, gs=32),
+    ]
+    for i, c in enumerate(cases):
+        wl = int8_case(300 + i, **c)
+        got = run_int8(h, wl)
+        assert np.all(np.isfinite(got)), c
+        err = np.max(np.abs(got - int8_sdpa_reference(wl)))
+        assert err <= 1e-12, (c, err)
+        split = run_int8(h, wl, partition_size=16)
+        assert np.max(np.abs(split - got)) <= 1e-13, c
+
+
+def pin_int8_matches_half_decode(h):
+    """P-q5: when every value code * scale is exactly an fp16 number (scales
+    powers of two), the INT8 decode equals, bit for bit, the plain decode
+    of the fp16 pools holding those values: the INT8 path adds nothing but
+    the dequantization to the pinned definition."""
+    wl = int8_case(71, q_dtype="f16", lens=(9, 40, 17), Hq=8, Hkv=2, D=64, bs=16, gs=32)
+    rng = np.random.default_rng(72)
+    for a in (wl.k_scales, wl.v_scales):
+        a[...] = np.where(np.isnan(a), a, 2.0 ** rng.integers(-9, -4, size=a.shape)).astype(np.float32)
+    kd, vd = int8_dequantized(wl)
+    k16 = kd.astype(np.float16)
+    v16 = vd.astype(np.float16)
+    assert np.array_equal(np.isnan(k16), np.isnan(kd))
+    fin = ~np.isnan(kd)
+    assert np.array_equal(k16[fin].astype(np.float64), kd[fin])
+    got = run_int8(h, wl)
+    ref = oracle.paged_attention_decode(
+        wl.q, np.ascontiguousarray(k16.view(np.uint16)), np.ascontiguousarray(v16.view(np.uint16)),
+        wl.block_tables, wl.context_lens, wl.scale, wl.num_kv_heads, wl.block_size, "f16",
+        handle=h)
+    assert np.array_equal(got, ref)
+
+
+def pin_int8_single_token(h):
+    """P-q6: with L = 1 the output is the dequantized V_0 exactly."""
+    wl = int8_case(73, q_dtype="bf16", lens=(1, 1), Hq=8, Hkv=2, D=128, bs=32, gs=64)
+    got = run_int8(h, wl)
+    _, vd = int8_dequantized(wl)
+    for b in range(wl.num_seqs):
+        blk = wl.block_tables[b, 0]
+        for hq in range(wl.num_q_heads):
+            assert np.array_equal(got[b, hq], vd[blk, hq // 4, 0, :])
+
+
 PINS = {
     "append_equals_write_then_decode": pin_append_equals_write_then_decode,
     "decoders_exhaustive": pin_decoders_exhaustive,
@@ -666,4 +857,10 @@ PINS = {
     "rope_write_numpy": pin_rope_write_numpy,
     "rope_unit_vectors": pin_rope_unit_vectors,
     "rope_identity_and_skip": pin_rope_identity_and_skip,
+    "int8_quantize_bounds": pin_int8_quantize_bounds,
+    "int8_quantize_exact_grid": pin_int8_quantize_exact_grid,
+    "int8_write_layout": pin_int8_write_layout,
+    "int8_decode_sdpa": pin_int8_decode_sdpa,
+    "int8_matches_half_decode": pin_int8_matches_half_decode,
+    "int8_single_token": pin_int8_single_token,
 }

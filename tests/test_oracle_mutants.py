@@ -23,8 +23,8 @@ MUTANTS = {
     "table_index": ("[(int64_t)b * a->max_blocks_per_seq + t / a->block_size]",
                     "[(int64_t)b * a->max_blocks_per_seq + t % a->max_blocks_per_seq]"),
     # wrong in-block offset in the gather
-    "kv_offset": ("    int off = (int)(t % a->block_size);\n    return load_elem(",
-                  "    int off = (int)((t + 1) % a->block_size);\n    return load_elem("),
+    "kv_offset": ("    int off = (int)(t % a->block_size);\n    if (a->k_codes)",
+                  "    int off = (int)((t + 1) % a->block_size);\n    if (a->k_codes)"),
     # head and offset swapped in the pool index
     "pool_index_order": ("((block * a->num_kv_heads + h) * a->block_size + off)",
                          "((block * a->block_size + off) * a->num_kv_heads + h)"),
@@ -90,6 +90,20 @@ MUTANTS = {
     # bf16 rounding truncates
     "bf16_round_trunc": ("double q = rint(a / ldexp(1.0, expo - 7));",
                          "double q = floor(a / ldexp(1.0, expo - 7));"),
+    # INT8: V codes stored and read token-major (the documented layout is dim-major)
+    "int8_v_token_major": ("return is_value ? base + (int64_t)d * a->block_size + off",
+                           "return is_value ? base + (int64_t)off * a->head_dim + d"),
+    # INT8: scale group taken modulo the group count instead of d / group_size
+    "int8_scale_group": ("d / a->group_size)];", "d % (a->head_dim / a->group_size))];"),
+    # INT8: K values scaled by the V scales
+    "int8_k_scale_from_v": ("const float *scales = is_value ? a->v_scales : a->k_scales;",
+                            "const float *scales = is_value ? a->v_scales : a->v_scales;"),
+    # INT8: halfway quotients rounded away from zero
+    "int8_round_half_away": ("rintf(x[i] / s)", "roundf(x[i] / s)"),
+    # INT8: scale amax / 128 (code 127 never reached)
+    "int8_scale_128": ("float s = amax / 127.0f;", "float s = amax / 128.0f;"),
+    # INT8: codes read as unsigned bytes (two's complement sign dropped)
+    "int8_code_sign": ("double c = (double)codes[", "double c = (double)(uint8_t)codes["),
 }
 
 
