@@ -18,6 +18,9 @@
  *     the fused operations  ->  pka_kv_cache_write_rope.
  *   - Block movement for preempted requests and paging
  *     ->  pka_copy_blocks, pka_gather_blocks, pka_scatter_blocks.
+ *   - "Technical details > INT8 quantisation" (group-wise INT8 with groups
+ *     of 32, 64 or 128), applied to the KV cache
+ *     ->  pka_kv_cache_write_int8, pka_paged_attention_decode_int8.
  *
  * Conventions (same README, "Modern C++20 architecture": explicit error
  * results instead of exceptions, zero-copy borrowed buffers):
@@ -54,7 +57,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 4
+#define PKA_ABI_VERSION 5
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -334,6 +337,111 @@ pka_status pka_gather_blocks(void *packed, const void *k_cache, const void *v_ca
 pka_status pka_scatter_blocks(void *k_cache, void *v_cache, const void *packed,
                               const int64_t *block_ids, int32_t num_ids, int32_t num_blocks,
                               int64_t block_bytes, void *stream);
+
+/*
+ * Group-quantised INT8 KV cache.  The PhotonInfer README (Korean
+ * translation), "Key features > GPU-optimised kernels" and "Technical
+ * details > INT8 quantisation", quantises to INT8 group by group with a
+ * configurable group size of 32, 64 or 128; it does so for weights, and
+ * these calls apply the same scheme to the KV rows (a reading: the pages do
+ * not quantise KV).  Each new token's row of one kv head is cut into
+ * head_dim / group_size groups of consecutive elements; a group stores
+ *   s = amax / 127          (amax = largest |x| of the group; float32
+ *                            division, correctly rounded)
+ *   c = rint(x / s)         (float32 division, ties to even), c in [-127, 127]
+ * (s = 0 stores c = 0) and stands for c * s.  Inputs must be finite.
+ *
+ * INT8 pool layout (four arrays, each 16-byte aligned, one physical block
+ * of one kv head contiguous in each):
+ *   k_codes   int8    [num_blocks][num_kv_heads][block_size][head_dim]
+ *   v_codes   int8    [num_blocks][num_kv_heads][head_dim][block_size]
+ *                     (dim-major inside a block)
+ *   k_scales, v_scales
+ *             float32 [num_blocks][num_kv_heads][block_size][head_dim / group_size]
+ * Slots and block tables address tokens exactly as for the other pools.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32}; group_size in
+ * {32, 64, 128} and <= head_dim.
+ */
+
+/*
+ * pka_kv_cache_write_int8 -- quantise and store the K and V rows of
+ * num_tokens new tokens of any number of sequences in one launch.  For each
+ * token i with s = slot_mapping[i] in [0, num_blocks * block_size) (others
+ * are skipped: padding), every kv head's rows k[i * k_token_stride + h *
+ * head_dim + d] and v[...] (dtype elements) are quantised group by group
+ * and stored at block s / block_size, offset s % block_size of the four
+ * arrays; every other byte is left untouched.  Two tokens with one slot race.
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim] of dtype
+ *                 (F32, F16 or BF16), token strides in elements (>=
+ *                 num_kv_heads * head_dim), heads head_dim apart; aligned to
+ *                 the element size.
+ *   slot_mapping  device, int64 [num_tokens].
+ *   k_codes, v_codes, k_scales, v_scales: device INT8 pools (layout above),
+ *                 written in place.
+ */
+pka_status pka_kv_cache_write_int8(const void *k, const void *v, int64_t k_token_stride,
+                                   int64_t v_token_stride, pka_dtype dtype,
+                                   const int64_t *slot_mapping, int32_t num_tokens,
+                                   int8_t *k_codes, int8_t *v_codes, float *k_scales,
+                                   float *v_scales, int32_t num_blocks, int32_t block_size,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t group_size,
+                                   void *stream);
+
+/*
+ * pka_decode_int8_partition_size -- the partition length (tokens, a
+ * multiple of block_size) pka_paged_attention_decode_int8 uses when its
+ * partition_size argument is 0.  Pure host function of the shapes.
+ */
+int32_t pka_decode_int8_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t block_size, int32_t max_context_len);
+
+/*
+ * pka_decode_int8_workspace_bytes -- device scratch of the INT8 decode for
+ * these shapes and this (resolved) partition length; 0 when every sequence
+ * fits one partition.  The workspace needs no initialisation: each call
+ * writes everything it reads.
+ */
+size_t pka_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pka_paged_attention_decode_int8 -- pka_paged_attention_decode over INT8
+ * pools: every cached K and V element is code * scale, and
+ *
+ *   out[b][hq][:] = sum_{t < L_b} softmax_t(scale * q[b][hq][:] . K_t) V_t
+ *
+ * with the stable softmax and fp32 accumulation.  Products run on the
+ * matrix cores in fp16 (codes are exact in fp16; bf16 queries are scaled by
+ * a power of two per head so that they are exact in fp16 too; the
+ * probabilities times the V scales enter the second product rounded to fp16).
+ * L_b <= 0 yields a zero row.  Long sequences are cut into partitions; with
+ * more than one, a planning launch, the decode and a merge launch run on
+ * `stream` (exact log-sum-exp merge).
+ *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (F32,
+ *                 or q_dtype rounded to nearest even), 16-byte aligned.
+ *   q             device [num_seqs][num_q_heads][head_dim] of q_dtype (F16 or
+ *                 BF16; F32 returns PKA_ERR_UNSUPPORTED), 16-byte aligned.
+ *   block_tables, max_blocks_per_seq, context_lens, num_blocks, block_size,
+ *   scale, max_context_len: as for pka_paged_attention_decode (used table
+ *                 entries are clamped into [0, num_blocks); lengths into
+ *                 [0, min(max_blocks_per_seq * block_size, the partitions
+ *                 that max_context_len spans)]).
+ *   partition_size 0: pka_decode_int8_partition_size(); else a positive
+ *                 multiple of block_size, at most 1024.
+ *   workspace     device, >= pka_decode_int8_workspace_bytes(...) bytes,
+ *                 256-byte aligned; may be NULL when that is 0.  Calls that
+ *                 share a workspace on different streams race.
+ * Supported: as for the INT8 pools above, num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8}.
+ */
+pka_status pka_paged_attention_decode_int8(
+    void *out, pka_dtype out_dtype, const void *q, pka_dtype q_dtype, const int8_t *k_codes,
+    const int8_t *v_codes, const float *k_scales, const float *v_scales,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream);
 
 /* Static English name of a status code. */
 const char *pka_status_string(pka_status status);

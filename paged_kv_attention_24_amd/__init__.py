@@ -23,6 +23,9 @@ Paged attention" and "Key features > GPU-optimised kernels"):
       RoPE" among the README's fused operations).
   copy_blocks / gather_blocks / scatter_blocks / swap_out / swap_in
       whole-block moves for preempted requests and GPU <-> CPU paging.
+  kv_cache_write_int8 / paged_attention_decode_int8
+      the write and the decode over group-quantised INT8 pools ("Technical
+      details > INT8 quantisation": groups of 32, 64 or 128).
 
 Pools are [num_blocks, num_kv_heads, block_size, head_dim].
 
@@ -42,6 +45,8 @@ __all__ = [
     "swap_in",
     "decode_partition_size",
     "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
+    "kv_cache_write_int8", "paged_attention_decode_int8", "decode_int8_partition_size",
+    "decode_int8_workspace_bytes", "int8_pools",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +113,17 @@ def load_library():
     lib.pka_gather_blocks.restype = ctypes.c_int
     lib.pka_scatter_blocks.argtypes = [P, P, P, P, i32, i32, i64, P]
     lib.pka_scatter_blocks.restype = ctypes.c_int
+    lib.pka_kv_cache_write_int8.argtypes = [P, P, i64, i64, ctypes.c_int, P, i32, P, P, P, P,
+                                            i32, i32, i32, i32, i32, P]
+    lib.pka_kv_cache_write_int8.restype = ctypes.c_int
+    lib.pka_decode_int8_partition_size.argtypes = [i32, i32, i32, i32]
+    lib.pka_decode_int8_partition_size.restype = i32
+    lib.pka_decode_int8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pka_decode_int8_workspace_bytes.restype = ctypes.c_size_t
+    lib.pka_paged_attention_decode_int8.argtypes = [
+        P, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
+        i32, ctypes.c_float, i32, i32, P, ctypes.c_size_t, P]
+    lib.pka_paged_attention_decode_int8.restype = ctypes.c_int
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_last_error.argtypes = []
@@ -540,3 +556,149 @@ class PagedKVCache:
         return paged_attention_decode_append(q, k_new, v_new, slot_mapping, self.k_cache,
                                              self.v_cache, block_tables, context_lens, scale,
                                              self.num_kv_heads, self.block_size, **kw)
+
+
+# ---------------------------------------------------------------------------
+# group-quantised INT8 pools
+# ---------------------------------------------------------------------------
+
+_INT8_WORKSPACES = {}
+
+
+def int8_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+               group_size: int, device="cuda"):
+    """Empty INT8 pools (k_codes, v_codes, k_scales, v_scales):
+    int8 [NB, Hkv, bs, D], int8 [NB, Hkv, D, bs] (dim-major inside a block),
+    float32 [NB, Hkv, bs, D / group_size] twice."""
+    import torch
+
+    if head_dim % group_size:
+        raise ValueError("group_size must divide head_dim")
+    ng = head_dim // group_size
+    return (torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=torch.int8,
+                        device=device),
+            torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=torch.int8,
+                        device=device),
+            torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32,
+                        device=device),
+            torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32,
+                        device=device))
+
+
+def _int8_pool_shapes(k_codes, v_codes, k_scales, v_scales):
+    import torch
+
+    _require_gpu(k_codes, v_codes, k_scales, v_scales)
+    if k_codes.dim() != 4 or k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
+        raise ValueError("k_codes / v_codes must be int8 [NB, Hkv, bs, D] / [NB, Hkv, D, bs]")
+    NB, Hkv, bs, D = k_codes.shape
+    if tuple(v_codes.shape) != (NB, Hkv, D, bs):
+        raise ValueError(f"v_codes must be [{NB}, {Hkv}, {D}, {bs}] (dim-major)")
+    if k_scales.dtype != torch.float32 or k_scales.dim() != 4 or \
+            tuple(k_scales.shape[:3]) != (NB, Hkv, bs) or v_scales.shape != k_scales.shape:
+        raise ValueError("k_scales / v_scales must be float32 [NB, Hkv, bs, D / group_size]")
+    ng = k_scales.shape[3]
+    if ng <= 0 or D % ng:
+        raise ValueError("the scale arrays' last dim must divide head_dim")
+    for t in (k_codes, v_codes, k_scales, v_scales):
+        if not t.is_contiguous():
+            raise ValueError("INT8 pools must be contiguous")
+    return NB, Hkv, bs, D, D // ng
+
+
+def kv_cache_write_int8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales) -> None:
+    """Quantise k, v [T, Hkv, D] (float32, float16 or bfloat16) group by
+    group and store them at slot_mapping (int64 [T]) in the INT8 pools;
+    negative slots are skipped.  Mutates the four arrays."""
+    import torch
+
+    NB, Hkv, bs, D, gs = _int8_pool_shapes(k_codes, v_codes, k_scales, v_scales)
+    _require_gpu(k, v, slot_mapping, k_codes)
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, D):
+            raise ValueError(f"{name} must be [T, {Hkv}, {D}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} must have contiguous heads (strides [*, {D}, 1])")
+        if t.dtype != k.dtype:
+            raise TypeError("k and v must share one dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k.shape[0],) or \
+            v.shape[0] != k.shape[0]:
+        raise ValueError("slot_mapping must be int64 [T] with T = k.shape[0] = v.shape[0]")
+    slot_mapping = slot_mapping.contiguous()
+    T = k.shape[0]
+    lib = load_library()
+    _check(lib.pka_kv_cache_write_int8(
+        k.data_ptr(), v.data_ptr(), k.stride(0) if T else Hkv * D, v.stride(0) if T else Hkv * D,
+        _dtype_code(k.dtype), slot_mapping.data_ptr(), T, k_codes.data_ptr(), v_codes.data_ptr(),
+        k_scales.data_ptr(), v_scales.data_ptr(), NB, bs, Hkv, D, gs,
+        _stream_ptr(k_codes.device)))
+
+
+def decode_int8_partition_size(num_seqs: int, num_kv_heads: int, block_size: int,
+                               max_context_len: int) -> int:
+    return int(load_library().pka_decode_int8_partition_size(num_seqs, num_kv_heads, block_size,
+                                                             max_context_len))
+
+
+def decode_int8_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                                max_context_len: int, partition_size: int) -> int:
+    return int(load_library().pka_decode_int8_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                              max_context_len, partition_size))
+
+
+def paged_attention_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_tables,
+                                context_lens, scale: float, num_kv_heads: int, block_size: int,
+                                *, out=None, out_dtype=None, partition_size: int = 0,
+                                max_context_len: int = 0, workspace=None):
+    """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache,
+    K and V being code * scale of the INT8 pools.  q [B, Hq, D] float16 or
+    bfloat16; returns out [B, Hq, D] (float32 unless ``out_dtype`` or ``out``
+    says q's dtype).  Other arguments as for paged_attention_decode; the
+    workspace needs no initialisation."""
+    import torch
+
+    NB, Hkv, bs, D, gs = _int8_pool_shapes(k_codes, v_codes, k_scales, v_scales)
+    _require_gpu(q, block_tables, context_lens, k_codes)
+    if Hkv != num_kv_heads or bs != block_size:
+        raise ValueError(f"pool shape does not match num_kv_heads={num_kv_heads}, "
+                         f"block_size={block_size}")
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError(f"q must be [B, Hq, {D}]")
+    q = q.contiguous()
+    B, Hq, _ = q.shape
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    block_tables = block_tables.contiguous()
+    context_lens = context_lens.contiguous()
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32 if out_dtype is None else out_dtype,
+                          device=q.device)
+    elif tuple(out.shape) != (B, Hq, D) or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor on q's device")
+    if B == 0:
+        return out
+    hint = max_context_len if max_context_len > 0 else MB * bs
+    hint = min(hint, MB * bs)
+    P = partition_size if partition_size > 0 else decode_int8_partition_size(B, Hkv, bs, hint)
+    need = decode_int8_workspace_bytes(B, Hq, D, hint, P)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = _INT8_WORKSPACES.get(q.device)
+            if workspace is None or workspace.numel() < need:
+                workspace = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=q.device)
+                _INT8_WORKSPACES[q.device] = workspace
+        elif workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {need} needed")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check(lib.pka_paged_attention_decode_int8(
+        out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), _dtype_code(q.dtype),
+        k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
+        block_tables.data_ptr(), MB, context_lens.data_ptr(), B, Hq, Hkv, D, NB, bs, gs,
+        float(scale), hint, P, ws_ptr, ws_bytes, _stream_ptr(q.device)))
+    return out

@@ -27,12 +27,13 @@ LIB_PATH = os.path.join(PKG, "libpka.so")
 
 ARCH = "gfx950"
 SOURCES = ["paged_decode.hip", "paged_prefill.hip", "kv_cache_write.hip", "block_ops.hip",
-           "abi.cpp"]
+           "paged_int8.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 VARIANTS = {"vector_alu": ["-DPKA_MATRIX_CORES=0"]}
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-I", INCLUDE, "-I", CSRC, "-Wall"]
 
 

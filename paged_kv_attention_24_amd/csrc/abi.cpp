@@ -505,3 +505,228 @@ pka_status pka_scatter_blocks(void *k_cache, void *v_cache, const void *packed,
 }
 
 }  // extern "C"
+
+
+// ---------------------------------------------------------------------------
+// Group-quantised INT8 KV cache
+// ---------------------------------------------------------------------------
+
+pka::Int8WorkspaceLayout pka::int8_workspace_layout(int64_t num_seqs, int64_t num_q_heads,
+                                                    int64_t head_dim, int64_t num_partitions)
+{
+    Int8WorkspaceLayout w{0, 0, 0, 0, 0};
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_partitions <= 1)
+        return w;
+    const int64_t rows = num_seqs * num_q_heads * num_partitions;
+    w.header_offset = 0;
+    w.items_offset = 256;
+    w.ml_offset = w.items_offset + (size_t)round256(num_seqs * num_partitions * 8);
+    w.o_offset = w.ml_offset + (size_t)round256(rows * 2 * 4);
+    w.total = w.o_offset + (size_t)round256(rows * head_dim * 4);
+    return w;
+}
+
+namespace {
+
+bool int8_group_ok(int32_t head_dim, int32_t group_size)
+{
+    return (group_size == 32 || group_size == 64 || group_size == 128) && group_size <= head_dim;
+}
+
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+pka_status pka_kv_cache_write_int8(const void *k, const void *v, int64_t k_token_stride,
+                                   int64_t v_token_stride, pka_dtype dtype,
+                                   const int64_t *slot_mapping, int32_t num_tokens,
+                                   int8_t *k_codes, int8_t *v_codes, float *k_scales,
+                                   float *v_scales, int32_t num_blocks, int32_t block_size,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t group_size,
+                                   void *stream)
+{
+    if (num_tokens < 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (!valid_dtype(dtype))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (num_blocks <= 0 || num_kv_heads <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_blocks and num_kv_heads must be positive");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+    if (block_size != 16 && block_size != 32)
+        return fail(PKA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+    if (!int8_group_ok(head_dim, group_size))
+        return fail(PKA_ERR_UNSUPPORTED, "group_size %d not in {32, 64, 128} or above head_dim %d",
+                    group_size, head_dim);
+    if (!k_codes || !v_codes || !k_scales || !v_scales)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null code or scale array");
+    if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) || !aligned16(v_scales))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "code and scale arrays must be 16-byte aligned");
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !slot_mapping)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null k, v or slot_mapping");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (k_token_stride < row || v_token_stride < row)
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "token strides (%lld, %lld) must be >= num_kv_heads * head_dim = %lld",
+                    (long long)k_token_stride, (long long)v_token_stride, (long long)row);
+    const int elt = pka::dtype_bytes(to_internal(dtype));
+    if (elt == 4 ? (!aligned4(k) || !aligned4(v)) : ((reinterpret_cast<uintptr_t>(k) |
+                                                      reinterpret_cast<uintptr_t>(v)) & 1u))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "k/v not aligned to their element size");
+    pka::Int8WriteArgs a{k, v, k_token_stride, v_token_stride, to_internal(dtype), slot_mapping,
+                         num_tokens, k_codes, v_codes, k_scales, v_scales, num_blocks,
+                         block_size, num_kv_heads, head_dim, group_size};
+    hipError_t e = pka::launch_kv_cache_write_int8(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "kv_cache_write_int8 launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int32_t pka_decode_int8_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t block_size, int32_t max_context_len)
+{
+    // One partition (no merge launch) while the longest sequence fits 256
+    // tokens; else 512 tokens, halved down to 128 while the (sequence, kv
+    // head, partition) units would number fewer than 16 per compute unit.
+    if (block_size <= 0)
+        return 0;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+    const int64_t lmax = max_context_len > 0 ? max_context_len : 1;
+    if (lmax <= 256)
+        return (int32_t)(ceil_div(lmax, block_size) * block_size);
+    int64_t P = kDefaultPartition;
+    while (P > 128 && pairs * ceil_div(lmax, P) < 16 * kComputeUnits)
+        P /= 2;
+    return (int32_t)(ceil_div(P, block_size) * block_size);
+}
+
+size_t pka_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size)
+{
+    if (partition_size <= 0 || max_context_len <= partition_size)
+        return 0;
+    return pka::int8_workspace_layout(num_seqs, num_q_heads, head_dim,
+                                      ceil_div(max_context_len, partition_size))
+        .total;
+}
+
+pka_status pka_paged_attention_decode_int8(
+    void *out, pka_dtype out_dtype, const void *q, pka_dtype q_dtype, const int8_t *k_codes,
+    const int8_t *v_codes, const float *k_scales, const float *v_scales,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream)
+{
+    if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (q_dtype == PKA_F32)
+        return fail(PKA_ERR_UNSUPPORTED, "INT8 decode takes F16 or BF16 queries");
+    if (out_dtype != PKA_F32 && out_dtype != q_dtype)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "out dtype must be F32 or the query dtype");
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0)
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "num_seqs >= 0 and positive num_q_heads, num_kv_heads, num_blocks, "
+                    "max_blocks_per_seq required");
+    if (num_q_heads % num_kv_heads)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "num_q_heads %d not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    const int group = num_q_heads / num_kv_heads;
+    if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32) ||
+        (group != 1 && group != 2 && group != 4 && group != 8))
+        return fail(PKA_ERR_UNSUPPORTED,
+                    "head_dim %d / block_size %d / group %d outside {64,128} x {16,32} x {1,2,4,8}",
+                    head_dim, block_size, group);
+    if (!int8_group_ok(head_dim, group_size))
+        return fail(PKA_ERR_UNSUPPORTED, "group_size %d not in {32, 64, 128} or above head_dim %d",
+                    group_size, head_dim);
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return fail(PKA_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535");
+    if (!(scale == scale))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "partition_size %d must be 0 or a positive multiple of block_size %d",
+                    partition_size, block_size);
+    if (partition_size > pka::kMaxPartition)
+        return fail(PKA_ERR_UNSUPPORTED, "partition_size %d exceeds %d", partition_size,
+                    pka::kMaxPartition);
+    if (num_seqs == 0)
+        return ok();
+    if (!out || !q || !k_codes || !v_codes || !k_scales || !v_scales || !block_tables ||
+        !context_lens)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) ||
+        !aligned16(k_scales) || !aligned16(v_scales))
+        return fail(PKA_ERR_INVALID_ARGUMENT,
+                    "out, q, the code and the scale arrays must be 16-byte aligned");
+    const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
+    int64_t lmax = max_context_len > 0 ? max_context_len : table_cap;
+    if (lmax > table_cap)
+        lmax = table_cap;
+    if (lmax > INT32_MAX / 2)
+        return fail(PKA_ERR_UNSUPPORTED, "context length beyond 2^30");
+    if (partition_size == 0)
+        partition_size = pka_decode_int8_partition_size(num_seqs, num_kv_heads, block_size,
+                                                        (int32_t)lmax);
+    if (partition_size > pka::kMaxPartition)
+        partition_size = pka::kMaxPartition / block_size * block_size;
+    const int64_t parts = lmax > 0 ? ceil_div(lmax, partition_size) : 1;
+    if ((int64_t)num_seqs * parts > 0x7fffffff / 8)
+        return fail(PKA_ERR_UNSUPPORTED, "too many (sequence, partition) items");
+    const size_t need = pka_decode_int8_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                        (int32_t)lmax, partition_size);
+    if (need > 0) {
+        if (!workspace)
+            return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);
+        if (workspace_bytes < need)
+            return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got %zu",
+                        need, workspace_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(PKA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    }
+    pka::Int8DecodeArgs a{};
+    a.out = out;
+    a.out_kind = out_dtype == PKA_F32 ? 0 : (out_dtype == PKA_F16 ? 1 : 2);
+    a.q = q;
+    a.q_dtype = to_internal(q_dtype);
+    a.k_codes = k_codes;
+    a.v_codes = v_codes;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.group_size = group_size;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    a.partition_size = partition_size;
+    a.num_partitions = (int32_t)parts;
+    a.len_cap = (int32_t)(parts * partition_size < table_cap ? parts * partition_size : table_cap);
+    if (need > 0) {
+        const pka::Int8WorkspaceLayout w =
+            pka::int8_workspace_layout(num_seqs, num_q_heads, head_dim, parts);
+        char *base = static_cast<char *>(workspace);
+        a.wl_header = reinterpret_cast<int32_t *>(base + w.header_offset);
+        a.items = reinterpret_cast<int2 *>(base + w.items_offset);
+        a.ws_ml = reinterpret_cast<float *>(base + w.ml_offset);
+        a.ws_o = reinterpret_cast<float *>(base + w.o_offset);
+    }
+    hipError_t e = pka::launch_paged_decode_int8(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "paged_attention_decode_int8 launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

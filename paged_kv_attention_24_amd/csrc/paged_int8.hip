@@ -1,0 +1,719 @@
+// Group-quantised INT8 KV cache for gfx950: the quantising batched write
+// and the paged decode over it.
+//
+// What is stored (PhotonInfer README, Korean translation, "Key features >
+// GPU-optimised kernels" and "Technical details > INT8 quantisation":
+// INT8 quantisation in groups of a configurable size, 32, 64 or 128; the
+// README quantises weights, this library applies the scheme to the KV rows):
+// each new token's row of one kv head is cut into groups of GS consecutive
+// dims; a group keeps one float32 scale s = amax / 127 and codes
+// c = rint(x / s) in [-127, 127], and stands for c * s.
+//
+// Layouts (one physical block of one kv head is contiguous in each array):
+//   k_codes  int8 [NB][Hkv][BS][D]      token-major, like the half pools
+//   v_codes  int8 [NB][Hkv][D][BS]      dim-major inside a block
+//   k_scales, v_scales  f32 [NB][Hkv][BS][D/GS]
+//
+// Decode design (CDNA4-first):
+//  * Work unit = (sequence, partition, kv head), one wave each; the G query
+//    heads of the kv head share every code and scale read.  Four waves per
+//    workgroup run four independent units; no LDS.
+//  * The wave streams its tokens in steps of two 16-token tiles straight
+//    into registers, the next step's loads in flight while the current one
+//    is computed.  Per tile and lane: 8 K codes per 32-dim slab (one token,
+//    the MFMA A operand), 4 V codes per 16-dim block (four tokens of one dim,
+//    contiguous because V is dim-major), and the 4 tokens' scales.
+//  * Codes become fp16 exactly (1024 + (c + 128) is an fp16 whose low byte
+//    is the offset code), so both products run as fp16 MFMAs with fp32
+//    accumulation.  bf16 queries are brought into fp16 by a per-head power
+//    of two (exact), folded back into the score multiplier.
+//  * Scores: one 16x16x32 MFMA per slab gives S^T (16 tokens x 16 heads);
+//    slabs of a group accumulate together, then each group is multiplied by
+//    its K scale.  The softmax is online in log2 units.
+//  * PV: the V scale varies per token inside the reduction, so it goes into
+//    the probability operand: P'' = p * s_v * r_g, with r_g a power of two
+//    per step and group that keeps P'' in [0, 2) for fp16; the step's MFMA
+//    result is multiplied back by 1 / r_g (exact) as it is added to O.
+//  * One partition per sequence: the wave writes the output.  Several: it
+//    writes (max, sum, O / sum) rows, and a merge launch combines them; a
+//    one-workgroup planning launch lists the (sequence, partition) items.
+//  * Tokens past the unit's end are excluded by selects (scores to -inf,
+//    probabilities and scales to 0), so poisoned scales never reach O.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "cdna4.h"
+#include "pka_internal.h"
+
+namespace pka {
+namespace {
+
+constexpr int kI8Waves = 4;             // waves (independent units) per workgroup
+constexpr int kI8PlanThreads = 1024;    // planning workgroup
+
+// ---- quantising write ------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ float lanes_max(float x)
+{
+    // max over aligned groups of N consecutive lanes (N = 16, 32 or 64)
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    if constexpr (N >= 32) x = fmaxf(x, swz_xor16(x));
+    if constexpr (N >= 64) x = fmaxf(x, xor32(x));
+    return x;
+}
+
+__device__ __forceinline__ float load_as_f32(TF32, const void *p, int64_t i)
+{
+    return static_cast<const float *>(p)[i];
+}
+__device__ __forceinline__ float load_as_f32(TF16, const void *p, int64_t i)
+{
+    return (float)static_cast<const _Float16 *>(p)[i];
+}
+__device__ __forceinline__ float load_as_f32(TBF16, const void *p, int64_t i)
+{
+    return as_f((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+}
+
+// One wave per (new token, kv head, tensor): lane l quantises dims
+// [l*E, l*E + E), E = D / 64; a group spans GS / E lanes.
+template <class T, int D, int GS>
+__global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
+{
+    constexpr int E = D / kWave;
+    constexpr int NG = D / GS;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;
+    if (wid >= 2 * rows)
+        return;
+    const int is_value = (int)(wid / rows);
+    const int64_t r = wid % rows;
+    const int64_t i = r / a.num_kv_heads;
+    const int h = (int)(r % a.num_kv_heads);
+    const int64_t slot = a.slot_mapping[i];
+    if (slot < 0 || slot >= (int64_t)a.num_blocks * a.block_size)
+        return;
+    const int64_t blk = slot / a.block_size;
+    const int off = (int)(slot % a.block_size);
+    const void *src = is_value ? a.v : a.k;
+    const int64_t row = i * (is_value ? a.v_token_stride : a.k_token_stride) + (int64_t)h * D;
+    float x[E];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        x[e] = load_as_f32(T{}, src, row + lane * E + e);
+        amax = fmaxf(amax, fabsf(x[e]));
+    }
+    amax = lanes_max<GS / E>(amax);
+    const float s = amax / 127.0f;  // IEEE division (correctly rounded)
+    int8_t c[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float q = s > 0.0f ? rintf(x[e] / s) : 0.0f;
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        c[e] = (int8_t)q;
+    }
+    const int64_t tile = blk * a.num_kv_heads + h;
+    if (!is_value) {
+        int8_t *dst = a.k_codes + (tile * a.block_size + off) * D + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            dst[e] = c[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a.v_codes[(tile * D + lane * E + e) * a.block_size + off] = c[e];
+    }
+    if ((lane * E) % GS == 0) {
+        float *scales = is_value ? a.v_scales : a.k_scales;
+        scales[(tile * a.block_size + off) * NG + lane * E / GS] = s;
+    }
+}
+
+// ---- decode ----------------------------------------------------------------
+
+// 4 codes (one dword, token or dim order kept) -> 4 fp16 values, exact:
+// the byte c + 128 under the exponent byte 0x64 is the fp16 1024 + c + 128.
+__device__ __forceinline__ uint2 codes_to_f16(uint32_t w)
+{
+    const uint32_t u = w ^ 0x80808080u;
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const half2_t a = __builtin_bit_cast(half2_t, lo) - bias;
+    const half2_t b = __builtin_bit_cast(half2_t, hi) - bias;
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b)
+{
+    const half2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// max over the four lanes that share lane % 16 (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float column_max(float x)
+{
+    x = fmaxf(x, swz_xor16(x));
+    return fmaxf(x, xor32(x));
+}
+__device__ __forceinline__ float column_sum(float x)
+{
+    x += swz_xor16(x);
+    return x + xor32(x);
+}
+
+// Exact power-of-two normaliser of a non-negative bound sigma: r with
+// sigma * r in [0, 2) (or smaller when sigma is tiny), and 1 / r exactly.
+__device__ __forceinline__ void pow2_normaliser(float sigma, float &r, float &inv_r)
+{
+    int e = (int)((__builtin_bit_cast(uint32_t, sigma) >> 23) & 0xff);
+    e = e < 1 ? 1 : (e > 253 ? 253 : e);
+    r = as_f((uint32_t)(254 - e) << 23);
+    inv_r = as_f((uint32_t)e << 23);
+}
+
+template <int D, int NG>
+struct StepRegs {
+    uint2 k[2][D / 32];     // per tile and slab: 8 K codes of token lane%16
+    uint32_t v[2][D / 16];  // per tile and 16-dim block: 4 V codes (tokens 4j..4j+3)
+    float4 ks[2][NG];       // per tile: K scales of tokens 4j..4j+3 ([token][group])
+    float4 vs[2][NG];
+};
+
+template <int D, int BS, int GS>
+struct I8Shape {
+    static constexpr int NG = D / GS;
+    static constexpr int SLABS = D / 32;
+    static constexpr int DB = D / 16;  // 16-dim blocks of the output
+    static constexpr int SLABS_PER_GROUP = GS / 32;
+};
+
+// Issue the loads of the two tiles starting at token ts (only tiles that
+// start before t_end; the block of a tile is ids lane (ts - t_part0) / BS).
+template <int D, int BS, int GS>
+__device__ __forceinline__ void load_step(const Int8DecodeArgs &a, StepRegs<D, D / GS> &R,
+                                          int ids, int t_part0, int ts, int t_end, int h,
+                                          int lane)
+{
+    using S = I8Shape<D, BS, GS>;
+    const int r16 = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        const int t0 = ts + 16 * tile;
+        if (t0 >= t_end)
+            break;
+        const int blk = __builtin_amdgcn_readfirstlane(
+            __builtin_amdgcn_readlane(ids, (t0 - t_part0) / BS));
+        const int off0 = t0 % BS;
+        const int64_t tile_idx = (int64_t)blk * a.num_kv_heads + h;
+        const int8_t *kp = a.k_codes + (tile_idx * BS + off0 + r16) * D + 8 * j;
+#pragma unroll
+        for (int c = 0; c < S::SLABS; ++c)
+            R.k[tile][c] = *reinterpret_cast<const uint2 *>(kp + 32 * c);
+        const int8_t *vp = a.v_codes + (tile_idx * D + r16) * BS + off0 + 4 * j;
+#pragma unroll
+        for (int m = 0; m < S::DB; ++m)
+            R.v[tile][m] = *reinterpret_cast<const uint32_t *>(vp + 16 * m * BS);
+        const int64_t srow = (tile_idx * BS + off0 + 4 * j) * S::NG;
+#pragma unroll
+        for (int g = 0; g < S::NG; ++g) {
+            R.ks[tile][g] = reinterpret_cast<const float4 *>(a.k_scales + srow)[g];
+            R.vs[tile][g] = reinterpret_cast<const float4 *>(a.v_scales + srow)[g];
+        }
+    }
+}
+
+__device__ __forceinline__ float f4(const float4 &v, int i)
+{
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Scale of token 4j+i of a tile, group g, from the [token][group] rows a
+// lane holds (NG float4 = 4 tokens x NG groups).
+template <int NG>
+__device__ __forceinline__ float scale_of(const float4 (&rows)[NG], int i, int g)
+{
+    const int flat = i * NG + g;
+    return f4(rows[flat / 4], flat % 4);
+}
+
+template <int D, int BS, int GS>
+struct UnitState {
+    float4_t o[D / 16];  // O^T[dim 16m + 4j + i][head lane%16]
+    float m;             // running max (log2 units) of head lane%16
+    float l;             // this lane's share of the running sum
+};
+
+// Compute one step (two tiles starting at ts) from loaded registers.
+template <int D, int BS, int GS>
+__device__ __forceinline__ void compute_step(const StepRegs<D, D / GS> &R,
+                                             UnitState<D, BS, GS> &st, const uint4 (&qf)[D / 32],
+                                             float qmul, int ts, int t_end, int lane)
+{
+    using S = I8Shape<D, BS, GS>;
+    constexpr int NG = S::NG;
+    const int j = lane >> 4;
+    float s[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        float4_t acc[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            acc[g] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = g * S::SLABS_PER_GROUP; c < (g + 1) * S::SLABS_PER_GROUP; ++c) {
+                const uint2 lo = codes_to_f16(R.k[tile][c].x);
+                const uint2 hi = codes_to_f16(R.k[tile][c].y);
+                acc[g] = mma_qk(TF16{}, make_uint4(lo.x, lo.y, hi.x, hi.y), qf[c], acc[g]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = 0.0f;
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                x = fmaf(acc[g][i], scale_of<NG>(R.ks[tile], i, g), x);
+            const bool valid = ts + 16 * tile + 4 * j + i < t_end;
+            s[tile][i] = valid ? x * qmul : -INFINITY;
+        }
+    }
+    // online softmax over the step's 32 tokens
+    float mx = s[0][0];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mx = fmaxf(mx, s[tile][i]);
+    mx = column_max(mx);
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[tile][i] = __builtin_amdgcn_exp2f(s[tile][i] - m_new);
+            psum += p[tile][i];
+        }
+    st.l = fmaf(st.l, alpha, psum);
+    // per-group power-of-two normalisers of the step's V scales
+    float r[NG], inv_r[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float sig = 0.0f;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = ts + 16 * tile + 4 * j + i < t_end;
+                sig = fmaxf(sig, valid ? scale_of<NG>(R.vs[tile], i, g) : 0.0f);
+            }
+        pow2_normaliser(column_max(sig), r[g], inv_r[g]);
+    }
+    uint2 pp[2][NG];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            float w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = ts + 16 * tile + 4 * j + i < t_end;
+                w[i] = valid ? p[tile][i] * scale_of<NG>(R.vs[tile], i, g) * r[g] : 0.0f;
+            }
+            pp[tile][g] = make_uint2(pack_f16(w[0], w[1]), pack_f16(w[2], w[3]));
+        }
+#pragma unroll
+    for (int m = 0; m < S::DB; ++m) {
+        constexpr int dims_per_group = GS;
+        const int g = (16 * m) / dims_per_group;
+        float4_t t = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile)
+            t = mma_pv(TF16{}, codes_to_f16(R.v[tile][m]), pp[tile][g], t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.o[m][i] = fmaf(st.o[m][i], alpha, t[i] * inv_r[g]);
+    }
+}
+
+// q operand of the score MFMAs for head lane%16 (zero past G) as fp16, and
+// the multiplier that turns the MFMA result into log2-unit scores.
+template <class QT, int D, int G>
+__device__ __forceinline__ float load_query(const Int8DecodeArgs &a, int b, int h, int lane,
+                                            uint4 (&qf)[D / 32])
+{
+    const int n = lane & 15, j = lane >> 4;
+    const bool live = n < G;
+    const int hq = h * G + (live ? n : 0);
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((int64_t)b * a.num_q_heads + hq) * D + 8 * j;
+    uint4 raw[D / 32];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+        raw[c] = *reinterpret_cast<const uint4 *>(qp + 32 * c);
+        if (!live)
+            raw[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if constexpr (std::is_same<QT, TF16>::value) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+            qf[c] = raw[c];
+        return a.scale_log2;
+    } else {
+        // bf16: widen, bring the head's largest magnitude into [1, 2) by a
+        // power of two (exact), round to fp16
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                amax = fmaxf(amax, fabsf(as_f(w[k] << 16)));
+                amax = fmaxf(amax, fabsf(as_f(w[k] & 0xffff0000u)));
+            }
+        }
+        amax = column_max(amax);
+        float r, inv_r;
+        pow2_normaliser(amax, r, inv_r);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = pack_f16(as_f(w[k] << 16) * r, as_f(w[k] & 0xffff0000u) * r);
+            qf[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        return a.scale_log2 * inv_r;
+    }
+}
+
+__device__ __forceinline__ int clamped_len(const Int8DecodeArgs &a, int b)
+{
+    int L = a.context_lens[b];
+    const int cap = a.len_cap;
+    return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Tokens [jp * P, min((jp+1) * P, L)) of sequence b, kv head h.
+template <class QT, int D, int BS, int G, int GS>
+__device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp, int h, int L,
+                                         int lane)
+{
+    const int P = a.partition_size;
+    const int t_begin = jp * P;
+    const int t_end = min(t_begin + P, L);
+    // the partition's block ids, one per lane (clamped into the table row
+    // and into the pool, so every access stays in bounds)
+    const int nb = (t_end - t_begin + BS - 1) / BS;
+    const int col = t_begin / BS + (lane < nb ? lane : nb - 1);
+    int ids = a.block_tables[(int64_t)b * a.max_blocks_per_seq + col];
+    ids = ids < 0 ? 0 : (ids >= a.num_blocks ? a.num_blocks - 1 : ids);
+
+    uint4 qf[D / 32];
+    const float qmul = load_query<QT, D, G>(a, b, h, lane, qf);
+
+    UnitState<D, BS, GS> st;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m)
+        st.o[m] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+
+    StepRegs<D, D / GS> A, B;
+    load_step<D, BS, GS>(a, A, ids, t_begin, t_begin, t_end, h, lane);
+    int ts = t_begin;
+    for (; ts + 32 < t_end; ts += 32) {
+        load_step<D, BS, GS>(a, B, ids, t_begin, ts + 32, t_end, h, lane);
+        compute_step<D, BS, GS>(A, st, qf, qmul, ts, t_end, lane);
+        A = B;
+    }
+    compute_step<D, BS, GS>(A, st, qf, qmul, ts, t_end, lane);
+
+    const float l = column_sum(st.l);
+    const int n = lane & 15, j = lane >> 4;
+    if (n >= G)
+        return;
+    const int hq = h * G + n;
+    const float inv_l = 1.0f / l;
+    if (a.num_partitions == 1 || L <= P) {
+        const int64_t base = ((int64_t)b * a.num_q_heads + hq) * D + 4 * j;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                store_out(a.out, base + 16 * m + i, st.o[m][i] * inv_l, a.out_kind);
+    } else {
+        const int64_t row = ((int64_t)b * a.num_q_heads + hq) * a.num_partitions + jp;
+        float *o = a.ws_o + row * D + 4 * j;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m)
+            *reinterpret_cast<float4 *>(o + 16 * m) =
+                make_float4(st.o[m][0] * inv_l, st.o[m][1] * inv_l, st.o[m][2] * inv_l,
+                            st.o[m][3] * inv_l);
+        if (j == 0)
+            *reinterpret_cast<float2 *>(a.ws_ml + 2 * row) = make_float2(st.m, l);
+    }
+}
+
+__device__ __forceinline__ void store_zero_rows(const Int8DecodeArgs &a, int b, int h, int G,
+                                                int D, int lane)
+{
+    for (int e = lane; e < G * D; e += kWave)
+        store_out(a.out, ((int64_t)b * a.num_q_heads + h * G) * D + e, 0.0f, a.out_kind);
+}
+
+// Dense mode (one partition covers every sequence): wave u handles unit
+// (b = u / Hkv, h = u % Hkv).  Work-list mode: the planned items (b, jp),
+// crossed with the kv heads, dealt round-robin to all waves of the grid.
+template <class QT, int D, int BS, int G, int GS, bool WORKLIST>
+__global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8DecodeArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t w0 = (int64_t)blockIdx.x * kI8Waves + wave;
+    if constexpr (!WORKLIST) {
+        if (w0 >= (int64_t)a.num_seqs * a.num_kv_heads)
+            return;
+        const int b = (int)(w0 / a.num_kv_heads), h = (int)(w0 % a.num_kv_heads);
+        const int L = clamped_len(a, b);
+        if (L == 0) {
+            store_zero_rows(a, b, h, G, D, lane);
+            return;
+        }
+        run_unit<QT, D, BS, G, GS>(a, b, 0, h, L, lane);
+    } else {
+        const int64_t units = (int64_t)__builtin_amdgcn_readfirstlane(a.wl_header[0]) *
+                              a.num_kv_heads;
+        const int64_t stride = (int64_t)gridDim.x * kI8Waves;
+        for (int64_t u = w0; u < units; u += stride) {
+            const int2 it = a.items[u / a.num_kv_heads];
+            const int b = __builtin_amdgcn_readfirstlane(it.x);
+            const int jp = __builtin_amdgcn_readfirstlane(it.y);
+            const int h = (int)(u % a.num_kv_heads);
+            run_unit<QT, D, BS, G, GS>(a, b, jp, h, clamped_len(a, b), lane);
+        }
+    }
+}
+
+// One workgroup: items (b, jp) for jp < ceil(L_b / P), sequences in order,
+// written to a.items; their count to a.wl_header[0].
+__global__ __launch_bounds__(kI8PlanThreads) void int8_plan_kernel(Int8DecodeArgs a)
+{
+    __shared__ int sums[kI8PlanThreads / kWave];
+    __shared__ int base;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    if (t == 0)
+        base = 0;
+    __syncthreads();
+    for (int b0 = 0; b0 < a.num_seqs; b0 += kI8PlanThreads) {
+        const int b = b0 + t;
+        const int n = b < a.num_seqs ? (clamped_len(a, b) + a.partition_size - 1) / a.partition_size
+                                     : 0;
+        // inclusive scan within the wave, then across waves
+        int x = n;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if (lane >= d)
+                x += y;
+        }
+        if (lane == kWave - 1)
+            sums[wave] = x;
+        __syncthreads();
+        int before = base;
+        for (int w = 0; w < wave; ++w)
+            before += sums[w];
+        const int start = before + x - n;
+        for (int k = 0; k < n; ++k)
+            a.items[start + k] = make_int2(b, k);
+        __syncthreads();
+        if (t == kI8PlanThreads - 1)
+            base = start + n;
+        __syncthreads();
+    }
+    if (t == 0)
+        a.wl_header[0] = base;
+}
+
+// out[b][hq] from the partition rows of sequence b: exact log-sum-exp
+// merge; zero rows for L_b = 0; nothing for one partition (written by the
+// decode).  One workgroup of D threads per (b, hq).
+template <int D>
+__global__ __launch_bounds__(D) void int8_merge_kernel(Int8DecodeArgs a)
+{
+    const int64_t r = blockIdx.x;
+    const int b = (int)(r / a.num_q_heads);
+    const int d = threadIdx.x;
+    const int L = clamped_len(a, b);
+    const int n = (L + a.partition_size - 1) / a.partition_size;
+    if (L == 0) {
+        store_out(a.out, r * D + d, 0.0f, a.out_kind);
+        return;
+    }
+    if (n <= 1)
+        return;
+    const int64_t row0 = r * a.num_partitions;
+    float M = -INFINITY;
+    for (int jp = 0; jp < n; ++jp)
+        M = fmaxf(M, a.ws_ml[2 * (row0 + jp)]);
+    float num = 0.0f, den = 0.0f;
+    for (int jp = 0; jp < n; ++jp) {
+        const float w = a.ws_ml[2 * (row0 + jp) + 1] * __builtin_amdgcn_exp2f(a.ws_ml[2 * (row0 + jp)] - M);
+        num = fmaf(w, a.ws_o[(row0 + jp) * D + d], num);
+        den += w;
+    }
+    store_out(a.out, r * D + d, num / den, a.out_kind);
+}
+
+int compute_units()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        cached[dev] = cus > 0 ? cus : 256;
+    }
+    return cached[dev];
+}
+
+template <class QT, int D, int BS, int G, int GS>
+hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
+{
+    if (a.num_partitions == 1) {
+        const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
+        const int64_t grid = (waves + kI8Waves - 1) / kI8Waves;
+        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, false>), dim3((unsigned)grid),
+                           dim3(kI8Waves * kWave), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(int8_plan_kernel, dim3(1), dim3(kI8PlanThreads), 0, stream, a);
+    static int per_cu_cache[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int per_cu = dev >= 0 && dev < 64 ? per_cu_cache[dev] : 0;
+    if (per_cu == 0) {
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, int8_decode_kernel<QT, D, BS, G, GS, true>, kI8Waves * kWave, 0);
+        per_cu = per_cu > 0 ? per_cu : 1;
+        if (dev >= 0 && dev < 64)
+            per_cu_cache[dev] = per_cu;
+    }
+    const int64_t max_units = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
+    int64_t grid = (int64_t)compute_units() * per_cu;
+    const int64_t need = (max_units + kI8Waves - 1) / kI8Waves;
+    grid = grid < need ? grid : need;
+    hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, true>), dim3((unsigned)grid),
+                       dim3(kI8Waves * kWave), 0, stream, a);
+    hipLaunchKernelGGL(int8_merge_kernel<D>, dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
+                       dim3(D), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class QT, int D, int BS, int G>
+hipError_t dispatch_gs(const Int8DecodeArgs &a, hipStream_t s)
+{
+    switch (a.group_size) {
+    case 32: return launch_decode_t<QT, D, BS, G, 32>(a, s);
+    case 64: return launch_decode_t<QT, D, BS, G, 64>(a, s);
+    case 128:
+        if constexpr (D >= 128)
+            return launch_decode_t<QT, D, BS, G, 128>(a, s);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class QT, int D, int BS>
+hipError_t dispatch_g(const Int8DecodeArgs &a, hipStream_t s)
+{
+    switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return dispatch_gs<QT, D, BS, 1>(a, s);
+    case 2: return dispatch_gs<QT, D, BS, 2>(a, s);
+    case 4: return dispatch_gs<QT, D, BS, 4>(a, s);
+    case 8: return dispatch_gs<QT, D, BS, 8>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class QT, int D>
+hipError_t dispatch_bs(const Int8DecodeArgs &a, hipStream_t s)
+{
+    return a.block_size == 16 ? dispatch_g<QT, D, 16>(a, s) : dispatch_g<QT, D, 32>(a, s);
+}
+
+template <class QT>
+hipError_t dispatch_d(const Int8DecodeArgs &a, hipStream_t s)
+{
+    return a.head_dim == 64 ? dispatch_bs<QT, 64>(a, s) : dispatch_bs<QT, 128>(a, s);
+}
+
+template <class T, int D>
+hipError_t launch_write_t(const Int8WriteArgs &a, hipStream_t stream)
+{
+    const int64_t waves = 2 * (int64_t)a.num_tokens * a.num_kv_heads;
+    const int64_t grid = (waves + 3) / 4;
+    switch (a.group_size) {
+    case 32:
+        hipLaunchKernelGGL((quantize_write_kernel<T, D, 32>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, a);
+        break;
+    case 64:
+        hipLaunchKernelGGL((quantize_write_kernel<T, D, 64>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, a);
+        break;
+    default:
+        if constexpr (D >= 128) {
+            hipLaunchKernelGGL((quantize_write_kernel<T, D, 128>), dim3((unsigned)grid), dim3(256),
+                               0, stream, a);
+            break;
+        }
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_write_d(const Int8WriteArgs &a, hipStream_t s)
+{
+    return a.head_dim == 64 ? launch_write_t<T, 64>(a, s) : launch_write_t<T, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_kv_cache_write_int8(const Int8WriteArgs &a, hipStream_t stream)
+{
+    if (a.num_tokens == 0)
+        return hipSuccess;
+    if ((int64_t)a.num_tokens * a.num_kv_heads * 2 > (int64_t)4 * 0x7fffffff)
+        return hipErrorInvalidValue;
+    switch (a.dtype) {
+    case DType::F32: return launch_write_d<TF32>(a, stream);
+    case DType::F16: return launch_write_d<TF16>(a, stream);
+    case DType::BF16: return launch_write_d<TBF16>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_decode_int8(const Int8DecodeArgs &a, hipStream_t stream)
+{
+    if (a.num_seqs == 0)
+        return hipSuccess;
+    return a.q_dtype == DType::F16 ? dispatch_d<TF16>(a, stream) : dispatch_d<TBF16>(a, stream);
+}
+
+}  // namespace pka

@@ -127,4 +127,50 @@ struct BlockMoveArgs {
 
 hipError_t launch_move_blocks(const BlockMoveArgs &a, hipStream_t stream);
 
+// Group-quantised INT8 pools: k_codes [NB][Hkv][BS][D], v_codes
+// [NB][Hkv][D][BS], k_scales / v_scales f32 [NB][Hkv][BS][D / group_size].
+struct Int8WriteArgs {
+    const void *k, *v;
+    int64_t k_token_stride, v_token_stride;  // elements
+    DType dtype;                              // of k and v
+    const int64_t *slot_mapping;
+    int32_t num_tokens;
+    int8_t *k_codes, *v_codes;
+    float *k_scales, *v_scales;
+    int32_t num_blocks, block_size, num_kv_heads, head_dim, group_size;
+};
+
+hipError_t launch_kv_cache_write_int8(const Int8WriteArgs &a, hipStream_t stream);
+
+struct Int8DecodeArgs {
+    void *out;
+    int out_kind;  // 0 f32, 1 f16, 2 bf16
+    const void *q;
+    DType q_dtype;  // F16 or BF16
+    const int8_t *k_codes, *v_codes;
+    const float *k_scales, *v_scales;
+    const int32_t *block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+    int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, group_size;
+    float scale_log2;         // scale * log2(e)
+    int32_t len_cap;          // lengths are clamped to [0, len_cap]
+    int32_t partition_size;   // tokens, multiple of block_size, <= kMaxPartition
+    int32_t num_partitions;   // ceil(max length / partition_size)
+    // workspace (num_partitions > 1)
+    float *ws_o;              // [B][Hq][num_partitions][D]
+    float *ws_ml;             // [B][Hq][num_partitions][2]: max (log2 units), sum
+    int2 *items;              // [B * num_partitions] planned (b, partition)
+    int32_t *wl_header;       // [0]: item count
+};
+
+// Byte offsets of the INT8 decode workspace (zero total for one partition).
+struct Int8WorkspaceLayout {
+    size_t header_offset, items_offset, ml_offset, o_offset, total;
+};
+Int8WorkspaceLayout int8_workspace_layout(int64_t num_seqs, int64_t num_q_heads,
+                                          int64_t head_dim, int64_t num_partitions);
+
+hipError_t launch_paged_decode_int8(const Int8DecodeArgs &a, hipStream_t stream);
+
 }  // namespace pka

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strings():
     lib = pka.load_library()
-    assert lib.pka_abi_version() == 4
+    assert lib.pka_abi_version() == 5
     assert lib.pka_status_string(0) == b"ok"
     assert lib.pka_status_string(3) == b"workspace too small"
     assert lib.pka_status_string(99) == b"unknown status"
@@ -273,3 +273,72 @@ def test_rope_write_rejects(over, status):
 def test_rope_write_fp32_allows_rotary_multiples_of_8():
     assert rope(dt=0, R=24, T=0)[0] == 0   # fp32: 4 elements per 16 bytes -> multiples of 8
     assert rope(dt=1, R=24, T=0)[0] == 1   # fp16: multiples of 16
+
+
+def write_int8(**over):
+    args = dict(k=FAKE, v=FAKE, ks=512, vs=512, dt=1, slots=FAKE, T=4, kc=FAKE, vc=FAKE,
+                ksc=FAKE, vsc=FAKE, NB=10, bs=16, H=8, D=64, gs=32)
+    args.update(over)
+    lib = pka.load_library()
+    st = lib.pka_kv_cache_write_int8(args["k"], args["v"], args["ks"], args["vs"], args["dt"],
+                                     args["slots"], args["T"], args["kc"], args["vc"],
+                                     args["ksc"], args["vsc"], args["NB"], args["bs"], args["H"],
+                                     args["D"], args["gs"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@fake_pointers
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-1), 1), (dict(dt=7), 1), (dict(NB=0), 1), (dict(H=0), 1), (dict(D=96), 2),
+    (dict(bs=8), 2), (dict(gs=16), 2), (dict(gs=128), 2), (dict(kc=None), 1),
+    (dict(vsc=FAKE + 4), 1), (dict(k=None), 1), (dict(slots=None), 1), (dict(ks=511), 1),
+    (dict(k=FAKE + 1), 1),
+])
+def test_write_int8_rejects(over, status):
+    st, msg = write_int8(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+@fake_pointers
+def test_write_int8_zero_tokens_is_ok_without_launch():
+    st, _ = write_int8(T=0, k=None, v=None, slots=None)
+    assert st == 0
+
+
+def decode_int8(**over):
+    args = dict(out=FAKE, odt=0, q=FAKE, qdt=1, kc=FAKE, vc=FAKE, ksc=FAKE, vsc=FAKE, bt=FAKE,
+                MB=64, cl=FAKE, B=4, Hq=32, Hkv=8, D=64, NB=100, bs=16, gs=32, scale=0.125,
+                hint=1024, P=0, ws=FAKE, wsb=1 << 30)
+    args.update(over)
+    lib = pka.load_library()
+    st = lib.pka_paged_attention_decode_int8(
+        args["out"], args["odt"], args["q"], args["qdt"], args["kc"], args["vc"], args["ksc"],
+        args["vsc"], args["bt"], args["MB"], args["cl"], args["B"], args["Hq"], args["Hkv"],
+        args["D"], args["NB"], args["bs"], args["gs"], args["scale"], args["hint"], args["P"],
+        args["ws"], args["wsb"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@fake_pointers
+@pytest.mark.parametrize("over,status", [
+    (dict(qdt=0), 2), (dict(qdt=5), 1), (dict(odt=2), 1), (dict(Hq=12), 1), (dict(Hq=24, Hkv=2), 2),
+    (dict(D=96), 2), (dict(bs=64), 2), (dict(gs=128), 2), (dict(gs=48), 2), (dict(B=-1), 1),
+    (dict(scale=float("nan")), 1), (dict(P=24), 1), (dict(P=2048), 2), (dict(kc=None), 1),
+    (dict(vsc=FAKE + 4), 1), (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=FAKE + 16), 1),
+])
+def test_decode_int8_rejects(over, status):
+    st, msg = decode_int8(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+def test_int8_workspace_and_partition_helpers():
+    lib = pka.load_library()
+    assert lib.pka_decode_int8_partition_size(16, 8, 16, 200) == 208
+    assert lib.pka_decode_int8_partition_size(128, 8, 16, 8192) == 512
+    assert lib.pka_decode_int8_partition_size(16, 8, 16, 1024) == 128
+    assert lib.pka_decode_int8_workspace_bytes(4, 32, 64, 512, 512) == 0
+    n = lib.pka_decode_int8_workspace_bytes(4, 32, 64, 1024, 256)
+    # header + items + (max, sum) rows + output rows, each 256-aligned
+    assert n == 256 + 256 + 4096 + 4 * 32 * 4 * 64 * 4
