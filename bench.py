@@ -43,9 +43,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--path", default="decode", choices=["decode", "prefill", "blocks", "rope"],
+    ap.add_argument("--path", default="decode",
+                    choices=["decode", "prefill", "blocks", "rope", "int8"],
                     help="decode step (the headline), multi-token causal attention, or "
-                         "whole-block moves (preemption, paging)")
+                         "whole-block moves (preemption, paging), the RoPE write, or the "
+                         "decode over group-quantised INT8 pools")
+    ap.add_argument("--group-size", type=int, default=64,
+                    help="INT8 path: quantisation group (32, 64 or 128 dims)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="INT8 path: skip timing the fp16/bf16 decode of the same shape")
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
                     help="workload (decode: 2 = Llama-3.2-1B batch 16, the headline; "
                          "prefill: 2 = chunked prefill, 3 = drafted-token check)")
@@ -72,7 +78,8 @@ def log(msg):
 KERNEL_SOURCES = {"decode": ("paged_decode.hip", "cdna4.h"),
                   "prefill": ("paged_prefill.hip", "cdna4.h"),
                   "blocks": ("block_ops.hip",),
-                  "rope": ("kv_cache_write.hip", "cdna4.h")}
+                  "rope": ("kv_cache_write.hip", "cdna4.h"),
+                  "int8": ("paged_int8.hip", "cdna4.h")}
 
 
 def kernel_source_sha(path_kind):
@@ -140,6 +147,8 @@ def main():
         return run_blocks(args, dev)
     if args.path == "rope":
         return run_rope(args, dev)
+    if args.path == "int8":
+        return run_int8(args, dev)
 
     cfg = args.config
     host_pools = cfg in (2, 3)
@@ -725,6 +734,173 @@ def run_rope(args, dev):
                               "copy-calibrated; null when the kernel changed since)",
             "kernel": "kv_cache_write_rope_kernel (one launch)",
             "us_per_launch": round(ms_rope * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(alg),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+INT8_TAGS = {2: "paged_decode_int8_llama3_1b_b16", 3: "paged_decode_int8_mix_b64",
+             4: "paged_decode_int8_qwen3_b128", 5: "paged_decode_int8_skewed_b256"}
+
+
+def run_int8(args, dev):
+    """Decode over group-quantised INT8 pools (codes + float32 group scales)
+    for workload 2-5's shapes and lengths, over enough layer pools to exceed
+    1 GB (16 for workload 2), one call per layer (the decode launch, or the
+    planning, decode and merge launches when a sequence spans several
+    partitions); beside it, the plain fp16/bf16 decode of the same shape."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+    from paged_kv_attention_24_amd import workloads as W
+
+    cfg, gs = args.config, args.group_size
+    wl = W.make_config(cfg, pools=False, poison=False, write=False)
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    NB, ng = wl.num_blocks, D // gs
+    q = W.as_torch(wl.q, wl.dtype, dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    pool_bytes = 2 * NB * Hkv * bs * (D + 4 * ng)
+    R = args.layers if args.layers > 0 else (16 if cfg == 2 else max(1, int(np.ceil(1.0e9 / pool_bytes))))
+    log(f"INT8 workload {cfg} (groups of {gs}): {wl.meta['description']}; pools per step {R} "
+        f"({R * pool_bytes / 1e6:.0f} MB)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000 + cfg)
+    pools = []
+    for r in range(R):
+        kc = torch.randint(-127, 128, (NB, Hkv, bs * D), generator=g, device=dev, dtype=torch.int8)
+        vc = torch.randint(-127, 128, (NB, Hkv, bs * D), generator=g, device=dev, dtype=torch.int8)
+        ks = torch.empty((NB, Hkv, bs, ng), device=dev).uniform_(0.005, 0.03, generator=g)
+        vs = torch.empty((NB, Hkv, bs, ng), device=dev).uniform_(0.005, 0.03, generator=g)
+        pools.append((kc, vc, ks, vs))
+    L = wl.max_context_len
+    P = args.partition_size or pka.decode_int8_partition_size(B, Hkv, bs, L)
+    ws = torch.empty(max(pka.decode_int8_workspace_bytes(B, Hq, D, L, P), 256), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
+    if args.calibration_copy_mib > 0:
+        src_c = torch.ones(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+    torch.cuda.synchronize()
+
+    def step():
+        for r in range(R):
+            kc, vc, ks, vs = pools[r]
+            pka.paged_attention_decode_int8(q, kc, vc, ks, vs, bt, cl, float(wl.scale), Hkv, bs,
+                                            out=outs[r], partition_size=P, max_context_len=L,
+                                            workspace=ws)
+
+    use_graph = not args.eager
+    ms_step = timed_calls(step, args.steps, args.warmup, use_graph)
+    us_layer = ms_step * 1e3 / R
+    wl8 = W.Int8Workload(**{f: getattr(wl, f) for f in W.Workload.__dataclass_fields__},
+                         group_size=gs)
+    kv_bytes = wl8.kv_bytes()
+    value = kv_bytes * R / (ms_step * 1e-3) / 1e9
+    nblk = int(np.sum((wl.context_lens.astype(np.int64) + bs - 1) // bs))
+    alg = kv_bytes + B * Hq * D * (2 + 4) + nblk * 4 + B * 4
+    achieved = alg / (us_layer * 1e-6) / 1e9
+    nparts = -(-L // P)
+    log(f"INT8 decode {us_layer:.2f} us per layer, {value:.0f} GB/s effective, P={P} "
+        f"({nparts} partitions)")
+    del pools
+    torch.cuda.empty_cache()
+
+    half = None
+    if not args.no_compare:  # the fp16/bf16 decode of the same shape, over >= 1 GB of pools
+        tdt = W.torch_dtype(wl.dtype)
+        hbytes = 2 * NB * Hkv * bs * D * wl.elt_bytes
+        Rh = 16 if cfg == 2 else max(1, int(np.ceil(1.0e9 / hbytes)))
+        hp = [(fill_pool((NB, Hkv, bs, D), tdt, 8000 + 2 * r, dev),
+               fill_pool((NB, Hkv, bs, D), tdt, 8001 + 2 * r, dev)) for r in range(Rh)]
+        Ph = pka.decode_partition_size(B, Hkv, bs, L) if cfg != 5 else 512
+        wsh = torch.zeros(max(pka.decode_workspace_bytes(B, Hq, D, L, Ph), 256),
+                          dtype=torch.uint8, device=dev)
+        oh = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+
+        def half_step():
+            for kc, vc in hp:
+                pka.paged_attention_decode(q, kc, vc, bt, cl, float(wl.scale), Hkv, bs, out=oh,
+                                           partition_size=Ph, max_context_len=L, workspace=wsh)
+
+        ms_h = timed_calls(half_step, args.steps, args.warmup, use_graph)
+        half = {"us_per_layer": round(ms_h * 1e3 / Rh, 3), "kv_dtype": wl.dtype,
+                "layers_per_step": Rh, "partition_size": int(Ph),
+                "effective_kv_gbps": round(wl.kv_bytes() * Rh / (ms_h * 1e-3) / 1e9, 2)}
+        log(f"{wl.dtype} decode of the same shape: {half['us_per_layer']:.2f} us per layer")
+        del hp
+
+    cpu = None
+    if not args.no_cpu_baseline and cfg in (2, 3):
+        import oracle
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+        rng = np.random.default_rng(cfg)
+        hk = rng.integers(-127, 128, (NB, Hkv, bs * D), dtype=np.int8)
+        hv = rng.integers(-127, 128, (NB, Hkv, bs * D), dtype=np.int8)
+        hks = rng.uniform(0.005, 0.03, (NB, Hkv, bs, ng)).astype(np.float32)
+        hvs = rng.uniform(0.005, 0.03, (NB, Hkv, bs, ng)).astype(np.float32)
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention_decode_int8(wl.q, wl.dtype, hk, hv, hks, hvs, wl.block_tables,
+                                               wl.context_lens, wl.scale, Hkv, bs,
+                                               threads=threads)
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n_done >= 512:
+                break
+        cpu = {"value": round(kv_bytes * n_done / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"full INT8 decode of one layer pool ({B} seqs x {Hq} q-heads) repeated "
+                         f"{n_done}x in {el:.1f} s; fp64 C oracle, OpenMP",
+               "us_per_layer": round(el / n_done * 1e6, 1)}
+
+    tag = INT8_TAGS[cfg] if gs == 64 else None
+    line = {
+        "metric": "paged decode attention over INT8 KV: effective KV GB/s (codes + scales)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"i8 KV, {wl.dtype} q, fp16 products, f32 accumulate",
+        "data": "synthetic (uniform int8 codes, uniform [0.005, 0.03] scales, shuffled block pool)",
+        "config": {
+            "workload": wl.meta["description"] + f"; INT8 KV in groups of {gs}",
+            "global_batch": B, "layers_per_step": R, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": bs, "group_size": gs,
+            "sum_context_tokens": int(wl.context_lens.sum()), "partition_size": int(P),
+            "timing": "hip-graph replay" if use_graph else "eager",
+            "parallelism": "single GPU",
+        },
+        "us_per_layer": round(us_layer, 3),
+        "half_kv_decode_same_shape": half,
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": ("int8_decode_kernel (one launch per layer)" if nparts == 1 else
+                       "int8_plan_kernel + int8_decode_kernel + int8_merge_kernel (per layer)"),
+            "launches_per_layer": 1 if nparts == 1 else 3,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(tag, "int8") if tag else None,
+            "traffic_source": (f"profiles/{tag}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                               "copy-calibrated; null when the kernel changed since)" if tag
+                               else "not measured for this group size"),
+            "us_per_launch": round(us_layer, 3),
             "algorithmic_bytes_per_launch": int(alg),
         },
         "cpu_baseline": cpu,

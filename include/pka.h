@@ -353,11 +353,19 @@ pka_status pka_scatter_blocks(void *k_cache, void *v_cache, const void *packed,
  *
  * INT8 pool layout (four arrays, each 16-byte aligned, one physical block
  * of one kv head contiguous in each):
- *   k_codes   int8    [num_blocks][num_kv_heads][block_size][head_dim]
- *   v_codes   int8    [num_blocks][num_kv_heads][head_dim][block_size]
- *                     (dim-major inside a block)
+ *   k_codes, v_codes  int8 [num_blocks][num_kv_heads][block_size * head_dim]
  *   k_scales, v_scales
  *             float32 [num_blocks][num_kv_heads][block_size][head_dim / group_size]
+ * Inside a block's run of codes the tokens go in tiles of 16 (token offset
+ * = 16 * tile + row) and the codes are in the order the matrix-core
+ * products consume them (each lane of a 64-lane wave reads one contiguous
+ * run of head_dim / 4 bytes per tile):
+ *   K code of (offset, d) at ((tile * 64 + 16 * ((d % 32) / 8) + row)
+ *                             * (head_dim / 32) + d / 32) * 8 + d % 8,
+ *   V code of (offset, d) at ((tile * 64 + 16 * (row / 4) + d % 16)
+ *                             * (head_dim / 16) + d / 16) * 4 + row % 4.
+ * The scales are token-major: scale of (offset, group g) at
+ * [offset][g].
  * Slots and block tables address tokens exactly as for the other pools.
  * Supported: head_dim in {64, 128}; block_size in {16, 32}; group_size in
  * {32, 64, 128} and <= head_dim.

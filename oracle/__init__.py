@@ -411,27 +411,32 @@ def quantize_group(x, handle=None):
 
 def int8_pools(num_blocks, num_kv_heads, block_size, head_dim, group_size, fill_code=0,
                fill_scale=np.nan):
-    """Empty INT8 pools: (k_codes [NB,Hkv,bs,D], v_codes [NB,Hkv,D,bs],
-    k_scales, v_scales [NB,Hkv,bs,D/group_size]) filled with the given values."""
+    """Empty INT8 pools: (k_codes, v_codes [NB, Hkv, bs * D] int8 in the
+    documented operand order, k_scales, v_scales [NB, Hkv, bs, D /
+    group_size] float32) filled with the given values."""
     G = head_dim // group_size
-    kc = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill_code, dtype=np.int8)
-    vc = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill_code, dtype=np.int8)
+    kc = np.full((num_blocks, num_kv_heads, block_size * head_dim), fill_code, dtype=np.int8)
+    vc = np.full((num_blocks, num_kv_heads, block_size * head_dim), fill_code, dtype=np.int8)
     ks = np.full((num_blocks, num_kv_heads, block_size, G), fill_scale, dtype=np.float32)
     vs = np.full((num_blocks, num_kv_heads, block_size, G), fill_scale, dtype=np.float32)
     return kc, vc, ks, vs
 
 
 def _check_int8_pools(k_codes, v_codes, k_scales, v_scales):
-    NB, Hkv, bs, D = k_codes.shape
-    if k_codes.dtype != np.int8 or v_codes.dtype != np.int8 or v_codes.shape != (NB, Hkv, D, bs):
-        raise ValueError("k_codes int8 [NB,Hkv,bs,D] and v_codes int8 [NB,Hkv,D,bs] expected")
-    if k_scales.dtype != np.float32 or v_scales.shape != k_scales.shape or \
-            k_scales.shape[:3] != (NB, Hkv, bs) or D % k_scales.shape[3]:
+    if k_scales.dtype != np.float32 or k_scales.ndim != 4 or v_scales.shape != k_scales.shape:
         raise ValueError("k_scales / v_scales float32 [NB,Hkv,bs,D/group] expected")
+    NB, Hkv, bs, G = k_scales.shape
+    if k_codes.dtype != np.int8 or v_codes.dtype != np.int8 or k_codes.ndim != 3 or \
+            v_codes.shape != k_codes.shape or k_codes.shape[:2] != (NB, Hkv) or \
+            k_codes.shape[2] % bs:
+        raise ValueError("k_codes / v_codes int8 [NB,Hkv,bs*D] expected")
+    D = k_codes.shape[2] // bs
+    if D % G:
+        raise ValueError("group count must divide head_dim")
     for a in (k_codes, v_codes, k_scales, v_scales):
         if not a.flags["C_CONTIGUOUS"]:
             raise ValueError("INT8 pools must be C-contiguous")
-    return NB, Hkv, bs, D, D // k_scales.shape[3]
+    return NB, Hkv, bs, D, D // G
 
 
 def kv_cache_write_int8(k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales, dtype,

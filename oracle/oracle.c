@@ -757,21 +757,34 @@ void oracle_round_array(const float *src, int dtype, int64_t n, uint16_t *dst)
  * for c_i * s.  Inputs are finite (non-finite inputs leave the codes
  * unspecified).
  *
- * Layouts (one physical block of one kv head is contiguous in each array):
- *   k_codes   int8    [num_blocks][num_kv_heads][block_size][head_dim]
- *   v_codes   int8    [num_blocks][num_kv_heads][head_dim][block_size]
+ * Layouts.  The block_size * head_dim codes of one physical block and kv
+ * head form one contiguous run of each code array, [num_blocks]
+ * [num_kv_heads][block_size * head_dim] int8; inside it, tokens are taken
+ * in tiles of 16 (token offset = 16 * tile + row) and the order is
+ *   K code of (offset, d):  ((tile * 64 + 16 * jk + row) * (head_dim / 32)
+ *                            + d / 32) * 8 + d % 8,     jk = (d % 32) / 8
+ *   V code of (offset, d):  ((tile * 64 + 16 * jv + d % 16) * (head_dim / 16)
+ *                            + d / 16) * 4 + row % 4,   jv = row / 4
+ * (the order in which the matrix-core products consume them: lane
+ * 16 * j + r of a 64-lane wave reads one contiguous run per tile).  The
+ * scales are token-major:
  *   k_scales, v_scales
  *             float32 [num_blocks][num_kv_heads][block_size][head_dim/group_size]
- * V's codes are dim-major inside a block: the block_size codes of one
- * dimension are adjacent.
  * ------------------------------------------------------------------------- */
 
 static int64_t int8_code_index(const decode_args *a, int is_value, int64_t blk, int h, int off,
                                int d)
 {
     int64_t base = (blk * a->num_kv_heads + h) * (int64_t)a->block_size * a->head_dim;
-    return is_value ? base + (int64_t)d * a->block_size + off
-                    : base + (int64_t)off * a->head_dim + d;
+    int tile = off / 16, row = off % 16;
+    if (!is_value) {
+        int jk = (d % 32) / 8;
+        return base + (((int64_t)tile * 64 + 16 * jk + row) * (a->head_dim / 32) + d / 32) * 8 +
+               d % 8;
+    }
+    int jv = row / 4;
+    return base + (((int64_t)tile * 64 + 16 * jv + d % 16) * (a->head_dim / 16) + d / 16) * 4 +
+           row % 4;
 }
 
 static int64_t int8_scale_index(int32_t num_kv_heads, int32_t block_size, int32_t groups,

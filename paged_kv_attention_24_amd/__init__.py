@@ -567,37 +567,35 @@ _INT8_WORKSPACES = {}
 
 def int8_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                group_size: int, device="cuda"):
-    """Empty INT8 pools (k_codes, v_codes, k_scales, v_scales):
-    int8 [NB, Hkv, bs, D], int8 [NB, Hkv, D, bs] (dim-major inside a block),
-    float32 [NB, Hkv, bs, D / group_size] twice."""
+    """Empty INT8 pools (k_codes, v_codes, k_scales, v_scales): int8
+    [NB, Hkv, bs * D] twice (codes of one block and head in the library's
+    operand order, see include/pka.h), float32 [NB, Hkv, bs, D / group_size]
+    twice."""
     import torch
 
     if head_dim % group_size:
         raise ValueError("group_size must divide head_dim")
     ng = head_dim // group_size
-    return (torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=torch.int8,
-                        device=device),
-            torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=torch.int8,
-                        device=device),
-            torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32,
-                        device=device),
-            torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32,
-                        device=device))
+    codes = (num_blocks, num_kv_heads, block_size * head_dim)
+    scales = (num_blocks, num_kv_heads, block_size, ng)
+    return (torch.empty(codes, dtype=torch.int8, device=device),
+            torch.empty(codes, dtype=torch.int8, device=device),
+            torch.empty(scales, dtype=torch.float32, device=device),
+            torch.empty(scales, dtype=torch.float32, device=device))
 
 
 def _int8_pool_shapes(k_codes, v_codes, k_scales, v_scales):
     import torch
 
     _require_gpu(k_codes, v_codes, k_scales, v_scales)
-    if k_codes.dim() != 4 or k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
-        raise ValueError("k_codes / v_codes must be int8 [NB, Hkv, bs, D] / [NB, Hkv, D, bs]")
-    NB, Hkv, bs, D = k_codes.shape
-    if tuple(v_codes.shape) != (NB, Hkv, D, bs):
-        raise ValueError(f"v_codes must be [{NB}, {Hkv}, {D}, {bs}] (dim-major)")
-    if k_scales.dtype != torch.float32 or k_scales.dim() != 4 or \
-            tuple(k_scales.shape[:3]) != (NB, Hkv, bs) or v_scales.shape != k_scales.shape:
+    if k_scales.dtype != torch.float32 or k_scales.dim() != 4 or v_scales.shape != k_scales.shape:
         raise ValueError("k_scales / v_scales must be float32 [NB, Hkv, bs, D / group_size]")
-    ng = k_scales.shape[3]
+    NB, Hkv, bs, ng = k_scales.shape
+    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8 or k_codes.dim() != 3 or \
+            v_codes.shape != k_codes.shape or tuple(k_codes.shape[:2]) != (NB, Hkv) or \
+            k_codes.shape[2] % bs:
+        raise ValueError("k_codes / v_codes must be int8 [NB, Hkv, bs * D]")
+    D = k_codes.shape[2] // bs
     if ng <= 0 or D % ng:
         raise ValueError("the scale arrays' last dim must divide head_dim")
     for t in (k_codes, v_codes, k_scales, v_scales):

@@ -9,20 +9,24 @@
 // dims; a group keeps one float32 scale s = amax / 127 and codes
 // c = rint(x / s) in [-127, 127], and stands for c * s.
 //
-// Layouts (one physical block of one kv head is contiguous in each array):
-//   k_codes  int8 [NB][Hkv][BS][D]      token-major, like the half pools
-//   v_codes  int8 [NB][Hkv][D][BS]      dim-major inside a block
-//   k_scales, v_scales  f32 [NB][Hkv][BS][D/GS]
+// Layouts.  One physical block of one kv head is a contiguous run of each
+// array.  The BS * D codes of a block run are ordered for the matrix cores:
+// tokens in tiles of 16 (offset = 16 * tile + row), and lane L = 16 * j + r
+// of a wave owns the D / 4 bytes at (tile * 64 + L) * D / 4:
+//   K: for each 32-dim slab c, dims 32c + 8j .. +7 of token row r
+//      (the A operand of the score MFMA);
+//   V: for each 16-dim block m, tokens 4j .. 4j+3 of dim 16m + r
+//      (the A operand of the PV MFMA).
+//   k_scales, v_scales  f32 [NB][Hkv][BS][D/GS]   token-major
 //
 // Decode design (CDNA4-first):
 //  * Work unit = (sequence, partition, kv head), one wave each; the G query
 //    heads of the kv head share every code and scale read.  Four waves per
 //    workgroup run four independent units; no LDS.
-//  * The wave streams its tokens in steps of two 16-token tiles straight
-//    into registers, the next step's loads in flight while the current one
-//    is computed.  Per tile and lane: 8 K codes per 32-dim slab (one token,
-//    the MFMA A operand), 4 V codes per 16-dim block (four tokens of one dim,
-//    contiguous because V is dim-major), and the 4 tokens' scales.
+//  * The wave streams its tokens in steps of 16-token tiles straight into
+//    registers.  Per tile each lane loads its own contiguous D / 4 bytes of
+//    K codes and of V codes (the wave's loads are fully coalesced: 1 KiB or
+//    2 KiB per instruction) and the scales of its 4 tokens.
 //  * Codes become fp16 exactly (1024 + (c + 128) is an fp16 whose low byte
 //    is the offset code), so both products run as fp16 MFMAs with fp32
 //    accumulation.  bf16 queries are brought into fp16 by a per-head power
@@ -32,8 +36,10 @@
 //    its K scale.  The softmax is online in log2 units.
 //  * PV: the V scale varies per token inside the reduction, so it goes into
 //    the probability operand: P'' = p * s_v * r_g, with r_g a power of two
-//    per step and group that keeps P'' in [0, 2) for fp16; the step's MFMA
-//    result is multiplied back by 1 / r_g (exact) as it is added to O.
+//    per work unit and group (from a first pass over the unit's V scales)
+//    that keeps s_v * r_g in [0, 2) for fp16; O is divided by r_g (exactly)
+//    at the end.  The softmax reference max is lazy (p <= 2^8), so the MFMAs
+//    accumulate straight into O and a rescale is rare.
 //  * One partition per sequence: the wave writes the output.  Several: it
 //    writes (max, sum, O / sum) rows, and a merge launch combines them; a
 //    one-workgroup planning launch lists the (sequence, partition) items.
@@ -51,6 +57,15 @@ namespace pka {
 namespace {
 
 constexpr int kI8Waves = 4;             // waves (independent units) per workgroup
+#ifndef PKA_I8_TILES
+#define PKA_I8_TILES 2
+#endif
+#ifndef PKA_I8_PREFETCH
+#define PKA_I8_PREFETCH 0
+#endif
+constexpr int kI8Tiles = PKA_I8_TILES;        // 16-token tiles per step
+constexpr int kI8Step = 16 * kI8Tiles;        // tokens per step
+constexpr bool kI8Prefetch = PKA_I8_PREFETCH != 0;  // next step's loads in flight
 constexpr int kI8PlanThreads = 1024;    // planning workgroup
 
 // ---- quantising write ------------------------------------------------------
@@ -103,12 +118,12 @@ __global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
     const int64_t blk = slot / a.block_size;
     const int off = (int)(slot % a.block_size);
     const void *src = is_value ? a.v : a.k;
-    const int64_t row = i * (is_value ? a.v_token_stride : a.k_token_stride) + (int64_t)h * D;
+    const int64_t src_row = i * (is_value ? a.v_token_stride : a.k_token_stride) + (int64_t)h * D;
     float x[E];
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        x[e] = load_as_f32(T{}, src, row + lane * E + e);
+        x[e] = load_as_f32(T{}, src, src_row + lane * E + e);
         amax = fmaxf(amax, fabsf(x[e]));
     }
     amax = lanes_max<GS / E>(amax);
@@ -120,20 +135,20 @@ __global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
         q = fminf(fmaxf(q, -127.0f), 127.0f);
         c[e] = (int8_t)q;
     }
-    const int64_t tile = blk * a.num_kv_heads + h;
-    if (!is_value) {
-        int8_t *dst = a.k_codes + (tile * a.block_size + off) * D + lane * E;
+    const int64_t run = blk * a.num_kv_heads + h;  // this block's run of codes
+    int8_t *codes = (is_value ? a.v_codes : a.k_codes) + run * a.block_size * D;
+    const int tl = off / 16, row = off % 16;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            dst[e] = c[e];
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            a.v_codes[(tile * D + lane * E + e) * a.block_size + off] = c[e];
+    for (int e = 0; e < E; ++e) {
+        const int d = lane * E + e;
+        const int64_t pos =
+            is_value ? ((int64_t)(tl * 64 + 16 * (row / 4) + d % 16) * (D / 16) + d / 16) * 4 + row % 4
+                     : ((int64_t)(tl * 64 + 16 * ((d % 32) / 8) + row) * (D / 32) + d / 32) * 8 + d % 8;
+        codes[pos] = c[e];
     }
     if ((lane * E) % GS == 0) {
         float *scales = is_value ? a.v_scales : a.k_scales;
-        scales[(tile * a.block_size + off) * NG + lane * E / GS] = s;
+        scales[(run * a.block_size + off) * NG + lane * E / GS] = s;
     }
 }
 
@@ -182,10 +197,10 @@ __device__ __forceinline__ void pow2_normaliser(float sigma, float &r, float &in
 
 template <int D, int NG>
 struct StepRegs {
-    uint2 k[2][D / 32];     // per tile and slab: 8 K codes of token lane%16
-    uint32_t v[2][D / 16];  // per tile and 16-dim block: 4 V codes (tokens 4j..4j+3)
-    float4 ks[2][NG];       // per tile: K scales of tokens 4j..4j+3 ([token][group])
-    float4 vs[2][NG];
+    uint4 k[kI8Tiles][D / 64];  // per tile: the lane's D/4 bytes of K codes (8 per slab)
+    uint4 v[kI8Tiles][D / 64];  // per tile: the lane's D/4 bytes of V codes (4 per dim block)
+    float4 ks[kI8Tiles][NG];       // per tile: K scales of tokens 4j..4j+3 ([token][group])
+    float4 vs[kI8Tiles][NG];
 };
 
 template <int D, int BS, int GS>
@@ -196,32 +211,33 @@ struct I8Shape {
     static constexpr int SLABS_PER_GROUP = GS / 32;
 };
 
-// Issue the loads of the two tiles starting at token ts (only tiles that
-// start before t_end; the block of a tile is ids lane (ts - t_part0) / BS).
+// Issue the loads of the two tiles starting at token ts (the block of a
+// tile is ids lane (t0 - t_part0) / BS).  A tile past the unit's end is
+// loaded too, from a block the lanes past the partition's last id repeat
+// (in bounds; its tokens are masked when computed), so that the number of
+// loads in flight is the same on every path and the waits stay exact.
 template <int D, int BS, int GS>
 __device__ __forceinline__ void load_step(const Int8DecodeArgs &a, StepRegs<D, D / GS> &R,
                                           int ids, int t_part0, int ts, int t_end, int h,
                                           int lane)
 {
     using S = I8Shape<D, BS, GS>;
-    const int r16 = lane & 15, j = lane >> 4;
+    const int j = lane >> 4;
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
+    for (int tile = 0; tile < kI8Tiles; ++tile) {
         const int t0 = ts + 16 * tile;
-        if (t0 >= t_end)
-            break;
         const int blk = __builtin_amdgcn_readfirstlane(
             __builtin_amdgcn_readlane(ids, (t0 - t_part0) / BS));
         const int off0 = t0 % BS;
         const int64_t tile_idx = (int64_t)blk * a.num_kv_heads + h;
-        const int8_t *kp = a.k_codes + (tile_idx * BS + off0 + r16) * D + 8 * j;
+        const int64_t mine = tile_idx * BS * D + (int64_t)((off0 / 16) * 64 + lane) * (D / 4);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + mine);
+        const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + mine);
 #pragma unroll
-        for (int c = 0; c < S::SLABS; ++c)
-            R.k[tile][c] = *reinterpret_cast<const uint2 *>(kp + 32 * c);
-        const int8_t *vp = a.v_codes + (tile_idx * D + r16) * BS + off0 + 4 * j;
-#pragma unroll
-        for (int m = 0; m < S::DB; ++m)
-            R.v[tile][m] = *reinterpret_cast<const uint32_t *>(vp + 16 * m * BS);
+        for (int q = 0; q < D / 64; ++q) {
+            R.k[tile][q] = kp[q];
+            R.v[tile][q] = vp[q];
+        }
         const int64_t srow = (tile_idx * BS + off0 + 4 * j) * S::NG;
 #pragma unroll
         for (int g = 0; g < S::NG; ++g) {
@@ -229,6 +245,11 @@ __device__ __forceinline__ void load_step(const Int8DecodeArgs &a, StepRegs<D, D
             R.vs[tile][g] = reinterpret_cast<const float4 *>(a.v_scales + srow)[g];
         }
     }
+}
+
+__device__ __forceinline__ uint32_t u4(const uint4 &v, int i)
+{
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
 __device__ __forceinline__ float f4(const float4 &v, int i)
@@ -247,13 +268,15 @@ __device__ __forceinline__ float scale_of(const float4 (&rows)[NG], int i, int g
 
 template <int D, int BS, int GS>
 struct UnitState {
-    float4_t o[D / 16];  // O^T[dim 16m + 4j + i][head lane%16]
-    float m;             // running max (log2 units) of head lane%16
+    float4_t o[D / 16];  // O^T[dim 16m + 4j + i][head lane%16], times r of its group
+    float m;             // reference max (log2 units) of head lane%16
     float l;             // this lane's share of the running sum
+    float r[D / GS];     // per group: power of two that brings the unit's V scales into [0, 2)
 };
 
-// Compute one step (two tiles starting at ts) from loaded registers.
-template <int D, int BS, int GS>
+// Compute one step (kI8Tiles tiles starting at ts) from loaded registers;
+// FULL: every token of the step lies before t_end (no masking).
+template <int D, int BS, int GS, bool FULL>
 __device__ __forceinline__ void compute_step(const StepRegs<D, D / GS> &R,
                                              UnitState<D, BS, GS> &st, const uint4 (&qf)[D / 32],
                                              float qmul, int ts, int t_end, int lane)
@@ -261,89 +284,81 @@ __device__ __forceinline__ void compute_step(const StepRegs<D, D / GS> &R,
     using S = I8Shape<D, BS, GS>;
     constexpr int NG = S::NG;
     const int j = lane >> 4;
-    float s[2][4];
+    float s[kI8Tiles][4];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
+    for (int tile = 0; tile < kI8Tiles; ++tile) {
         float4_t acc[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             acc[g] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = g * S::SLABS_PER_GROUP; c < (g + 1) * S::SLABS_PER_GROUP; ++c) {
-                const uint2 lo = codes_to_f16(R.k[tile][c].x);
-                const uint2 hi = codes_to_f16(R.k[tile][c].y);
+                const uint4 &w = R.k[tile][c / 2];
+                const uint2 lo = codes_to_f16(c % 2 ? w.z : w.x);
+                const uint2 hi = codes_to_f16(c % 2 ? w.w : w.y);
                 acc[g] = mma_qk(TF16{}, make_uint4(lo.x, lo.y, hi.x, hi.y), qf[c], acc[g]);
             }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float x = 0.0f;
+            float x = acc[0][i] * scale_of<NG>(R.ks[tile], i, 0);
 #pragma unroll
-            for (int g = 0; g < NG; ++g)
+            for (int g = 1; g < NG; ++g)
                 x = fmaf(acc[g][i], scale_of<NG>(R.ks[tile], i, g), x);
-            const bool valid = ts + 16 * tile + 4 * j + i < t_end;
+            const bool valid = FULL || ts + 16 * tile + 4 * j + i < t_end;
             s[tile][i] = valid ? x * qmul : -INFINITY;
         }
     }
-    // online softmax over the step's 32 tokens
+    // Lazy online softmax: a head's reference max moves only when a logit
+    // exceeds it by more than 8 (log2 units), so p <= 2^8; sum and O always
+    // share one reference, so the result is exact.  Moves are rare after
+    // the first step, and the rescale is skipped by the whole wave then.
     float mx = s[0][0];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
+    for (int tile = 0; tile < kI8Tiles; ++tile)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             mx = fmaxf(mx, s[tile][i]);
     mx = column_max(mx);
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
-    float p[2][4];
-    float psum = 0.0f;
+    const bool move = mx > st.m + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+        const float m_new = move ? mx : st.m;
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        st.m = m_new;
+        st.l *= alpha;
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
+        for (int m = 0; m < S::DB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st.o[m][i] *= alpha;
+    }
+    uint2 pp[kI8Tiles][NG];
+#pragma unroll
+    for (int tile = 0; tile < kI8Tiles; ++tile) {
+        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[tile][i] = __builtin_amdgcn_exp2f(s[tile][i] - m_new);
-            psum += p[tile][i];
+            p[i] = __builtin_amdgcn_exp2f(s[tile][i] - st.m);
+            st.l += p[i];
         }
-    st.l = fmaf(st.l, alpha, psum);
-    // per-group power-of-two normalisers of the step's V scales
-    float r[NG], inv_r[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        float sig = 0.0f;
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool valid = ts + 16 * tile + 4 * j + i < t_end;
-                sig = fmaxf(sig, valid ? scale_of<NG>(R.vs[tile], i, g) : 0.0f);
-            }
-        pow2_normaliser(column_max(sig), r[g], inv_r[g]);
-    }
-    uint2 pp[2][NG];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             float w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool valid = ts + 16 * tile + 4 * j + i < t_end;
-                w[i] = valid ? p[tile][i] * scale_of<NG>(R.vs[tile], i, g) * r[g] : 0.0f;
+                const bool valid = FULL || ts + 16 * tile + 4 * j + i < t_end;
+                w[i] = valid ? p[i] * (scale_of<NG>(R.vs[tile], i, g) * st.r[g]) : 0.0f;
             }
             pp[tile][g] = make_uint2(pack_f16(w[0], w[1]), pack_f16(w[2], w[3]));
         }
+    }
 #pragma unroll
     for (int m = 0; m < S::DB; ++m) {
-        constexpr int dims_per_group = GS;
-        const int g = (16 * m) / dims_per_group;
-        float4_t t = float4_t{0.f, 0.f, 0.f, 0.f};
+        const int g = (16 * m) / GS;
 #pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
-            t = mma_pv(TF16{}, codes_to_f16(R.v[tile][m]), pp[tile][g], t);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st.o[m][i] = fmaf(st.o[m][i], alpha, t[i] * inv_r[g]);
+        for (int tile = 0; tile < kI8Tiles; ++tile)
+            st.o[m] = mma_pv(TF16{}, codes_to_f16(u4(R.v[tile][m / 4], m % 4)), pp[tile][g],
+                             st.o[m]);
     }
 }
 
@@ -430,22 +445,85 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
         st.o[m] = float4_t{0.f, 0.f, 0.f, 0.f};
     st.m = -INFINITY;
     st.l = 0.0f;
-
-    StepRegs<D, D / GS> A, B;
-    load_step<D, BS, GS>(a, A, ids, t_begin, t_begin, t_end, h, lane);
-    int ts = t_begin;
-    for (; ts + 32 < t_end; ts += 32) {
-        load_step<D, BS, GS>(a, B, ids, t_begin, ts + 32, t_end, h, lane);
-        compute_step<D, BS, GS>(A, st, qf, qmul, ts, t_end, lane);
-        A = B;
+    // The unit's V-scale normalisers: lane l reads the scales of the
+    // partition's block l (tokens past t_end masked), a wave max per group.
+    {
+        constexpr int NG = D / GS;
+        float sig[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            sig[g] = 0.0f;
+        if (lane < nb) {
+            const float4 *vsp = reinterpret_cast<const float4 *>(
+                a.v_scales + ((int64_t)ids * a.num_kv_heads + h) * BS * NG);
+            const int t0 = t_begin + lane * BS;
+#pragma unroll
+            for (int k4 = 0; k4 < BS * NG / 4; ++k4) {
+                const float4 v = vsp[k4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int flat = 4 * k4 + e;
+                    const bool valid = t0 + flat / NG < t_end;
+                    sig[flat % NG] = fmaxf(sig[flat % NG], valid ? f4(v, e) : 0.0f);
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            float inv_r;
+            pow2_normaliser(wave_max(sig[g]), st.r[g], inv_r);
+        }
     }
-    compute_step<D, BS, GS>(A, st, qf, qmul, ts, t_end, lane);
+
+    if constexpr (kI8Prefetch) {
+        // Two register sets take turns: the step after the one computed is
+        // always in flight.  Past the last step the prefetch repeats the
+        // last step's loads (never used), keeping the loads unconditional.
+        const int t_last = t_begin + (t_end - 1 - t_begin) / kI8Step * kI8Step;
+        StepRegs<D, D / GS> A, B;
+        load_step<D, BS, GS>(a, A, ids, t_begin, t_begin, t_end, h, lane);
+        int ts = t_begin;
+        for (;;) {
+            load_step<D, BS, GS>(a, B, ids, t_begin, min(ts + kI8Step, t_last), t_end, h, lane);
+            compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
+            ts += kI8Step;
+            if (ts > t_last)
+                break;
+            load_step<D, BS, GS>(a, A, ids, t_begin, min(ts + kI8Step, t_last), t_end, h, lane);
+            compute_step<D, BS, GS, false>(B, st, qf, qmul, ts, t_end, lane);
+            ts += kI8Step;
+            if (ts > t_last)
+                break;
+        }
+    } else {
+        // One step in flight per wave; the waves resident on a compute unit
+        // overlap each other's loads and arithmetic.
+        StepRegs<D, D / GS> A;
+        int ts = t_begin;
+        for (; ts + kI8Step <= t_end; ts += kI8Step) {
+            load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
+            compute_step<D, BS, GS, true>(A, st, qf, qmul, ts, t_end, lane);
+        }
+        if (ts < t_end) {
+            load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
+            compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
+        }
+    }
 
     const float l = column_sum(st.l);
     const int n = lane & 15, j = lane >> 4;
     if (n >= G)
         return;
     const int hq = h * G + n;
+    // O was accumulated times r of its group (a power of two): undo it
+    // exactly together with the division by the sum
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+        const float u = 1.0f / st.r[(16 * m) / GS];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.o[m][i] *= u;
+    }
     const float inv_l = 1.0f / l;
     if (a.num_partitions == 1 || L <= P) {
         const int64_t base = ((int64_t)b * a.num_q_heads + hq) * D + 4 * j;

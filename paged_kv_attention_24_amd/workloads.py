@@ -374,12 +374,43 @@ def make_prefill_config(n: int, *, seed: Optional[int] = None, poison: bool = Tr
 INT8_POISON_CODE = -128  # never produced by the quantiser (codes lie in [-127, 127])
 
 
+def int8_code_positions(block_size: int, head_dim: int, is_value: bool) -> np.ndarray:
+    """[block_size, head_dim] positions of each (token offset, dim) code
+    inside one block's run of block_size * head_dim codes, in the order the
+    library documents: tiles of 16 tokens (offset = 16 * tile + row), then
+    for K  ((tile * 64 + 16 * ((d % 32) // 8) + row) * (D / 32) + d // 32) * 8 + d % 8
+    and V  ((tile * 64 + 16 * (row // 4) + d % 16) * (D / 16) + d // 16) * 4 + row % 4."""
+    off = np.arange(block_size)[:, None]
+    d = np.arange(head_dim)[None, :]
+    tile, row = off // 16, off % 16
+    if not is_value:
+        pos = ((tile * 64 + 16 * ((d % 32) // 8) + row) * (head_dim // 32) + d // 32) * 8 + d % 8
+    else:
+        pos = ((tile * 64 + 16 * (row // 4) + d % 16) * (head_dim // 16) + d // 16) * 4 + row % 4
+    return pos.astype(np.int64)
+
+
+def int8_pack(codes: np.ndarray, is_value: bool) -> np.ndarray:
+    """Logical codes [NB, Hkv, bs, D] -> the pool array [NB, Hkv, bs * D]."""
+    NB, H, bs, D = codes.shape
+    out = np.empty((NB, H, bs * D), dtype=np.int8)
+    out[:, :, int8_code_positions(bs, D, is_value).reshape(-1)] = codes.reshape(NB, H, bs * D)
+    return out
+
+
+def int8_unpack(pool: np.ndarray, block_size: int, head_dim: int, is_value: bool) -> np.ndarray:
+    """The pool array [NB, Hkv, bs * D] -> logical codes [NB, Hkv, bs, D]."""
+    pos = int8_code_positions(block_size, head_dim, is_value)
+    return pool[:, :, pos]
+
+
 @dataclass
 class Int8Workload(Workload):
     """Decode inputs over INT8 pools.  ``dtype`` is the dtype of q (and of
-    the new tokens); k_cache / v_cache are unused (None).  Layouts:
-    k_codes int8 [NB, Hkv, bs, D]; v_codes int8 [NB, Hkv, D, bs] (dim-major
-    inside a block); k_scales, v_scales float32 [NB, Hkv, bs, D / group_size]."""
+    the new tokens); k_cache / v_cache are unused (None).  k_codes and
+    v_codes are int8 [NB, Hkv, bs * D] in the library's order (see
+    int8_code_positions); k_scales, v_scales float32 [NB, Hkv, bs, D /
+    group_size]."""
 
     group_size: int = 0
     k_codes: Optional[np.ndarray] = None
@@ -406,8 +437,9 @@ def make_int8_case(seed: int, *, q_dtype: str, context_lens: Sequence[int], num_
 
     Draw order: steps 1, 2, 5, 6 of make_case (lengths, pool permutation, q
     and the new tokens, all in q_dtype), then 7. the K codes, 8. the V codes
-    (uniform integers in [-127, 127]), 9. the K scales, 10. the V scales
-    (float32 uniform in ``scale_range``).  With ``poison`` every scale of an
+    (uniform integers in [-127, 127], drawn as [NB, Hkv, bs, D] and laid
+    out in the pool order), 9. the K scales, 10. the V scales (float32
+    uniform in ``scale_range``).  With ``poison`` every scale of an
     unused block, of the tail slots >= L_b and of the slot the write will
     fill is NaN, and the codes there are INT8_POISON_CODE."""
     if head_dim % group_size:
@@ -421,7 +453,7 @@ def make_int8_case(seed: int, *, q_dtype: str, context_lens: Sequence[int], num_
     NB, Hkv, bs, D = base.num_blocks, num_kv_heads, block_size, head_dim
     ng = D // group_size
     k_codes = rng.integers(-127, 128, size=(NB, Hkv, bs, D), dtype=np.int8)
-    v_codes = rng.integers(-127, 128, size=(NB, Hkv, D, bs), dtype=np.int8)
+    v_codes = rng.integers(-127, 128, size=(NB, Hkv, bs, D), dtype=np.int8)
     lo, hi = scale_range
     k_scales = rng.uniform(lo, hi, size=(NB, Hkv, bs, ng)).astype(np.float32)
     v_scales = rng.uniform(lo, hi, size=(NB, Hkv, bs, ng)).astype(np.float32)
@@ -445,7 +477,9 @@ def make_int8_case(seed: int, *, q_dtype: str, context_lens: Sequence[int], num_
         k_scales[blk, :, off, :] = np.nan
         v_scales[blk, :, off, :] = np.nan
         k_codes[blk, :, off, :] = INT8_POISON_CODE
-        v_codes[blk, :, :, off] = INT8_POISON_CODE
+        v_codes[blk, :, off, :] = INT8_POISON_CODE
+    k_codes = int8_pack(k_codes, False)
+    v_codes = int8_pack(v_codes, True)
     fields = {f: getattr(base, f) for f in Workload.__dataclass_fields__}
     return Int8Workload(**fields, group_size=group_size, k_codes=k_codes, v_codes=v_codes,
                         k_scales=k_scales, v_scales=v_scales)

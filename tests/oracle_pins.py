@@ -647,13 +647,14 @@ def pin_rope_identity_and_skip(h):
 
 def int8_dequantized(wl):
     """fp64 K and V pools [NB, Hkv, bs, D] from the INT8 arrays, read through
-    the documented layouts (K codes token-major, V codes dim-major, one
-    float32 scale per group of group_size consecutive dims)."""
-    gs = wl.group_size
+    the documented layouts (codes in the operand order of
+    workloads.int8_code_positions, one float32 scale per group of group_size
+    consecutive dims)."""
+    gs, bs, D = wl.group_size, wl.block_size, wl.head_dim
     ks = np.repeat(wl.k_scales.astype(np.float64), gs, axis=3)
     vs = np.repeat(wl.v_scales.astype(np.float64), gs, axis=3)
-    k = wl.k_codes.astype(np.float64) * ks
-    v = np.transpose(wl.v_codes, (0, 1, 3, 2)).astype(np.float64) * vs
+    k = W.int8_unpack(wl.k_codes, bs, D, False).astype(np.float64) * ks
+    v = W.int8_unpack(wl.v_codes, bs, D, True).astype(np.float64) * vs
     return k, v
 
 
@@ -735,7 +736,7 @@ def pin_int8_quantize_exact_grid(h):
 
 def pin_int8_write_layout(h):
     """P-q3: the quantised write stores, for each written token and head,
-    codes and scales at the documented places (K token-major, V dim-major,
+    codes and scales at the documented places (codes in the operand order,
     scales [blk, h, off, d // group]) whose product is within s / 2 of the
     input; skipped slots and every other byte keep their sentinels; the
     order of distinct slots does not matter."""
@@ -748,7 +749,9 @@ def pin_int8_write_layout(h):
         slots[2], slots[5] = -1, NB * bs + 3  # padding and out of the pool
         pools = oracle.int8_pools(NB, Hkv, bs, D, gs, fill_code=W.INT8_POISON_CODE)
         oracle.kv_cache_write_int8(k, v, slots, *pools, dtype, handle=h)
-        kc, vc, ks, vs = pools
+        kc = W.int8_unpack(pools[0], bs, D, False)
+        vc = W.int8_unpack(pools[1], bs, D, True)
+        ks, vs = pools[2], pools[3]
         written = np.zeros((NB, bs), dtype=bool)
         for i, sl in enumerate(slots):
             if not 0 <= sl < NB * bs:
@@ -756,7 +759,7 @@ def pin_int8_write_layout(h):
             blk, off = divmod(int(sl), bs)
             written[blk, off] = True
             for name, x, codes, sc in (("k", k, kc[blk, :, off, :], ks[blk, :, off, :]),
-                                       ("v", v, vc[blk, :, :, off], vs[blk, :, off, :])):
+                                       ("v", v, vc[blk, :, off, :], vs[blk, :, off, :])):
                 xv = f64(x[i], dtype)  # [Hkv, D]
                 srep = np.repeat(sc.astype(np.float64), gs, axis=1)
                 err = np.abs(codes.astype(np.float64) * srep - xv)
@@ -765,7 +768,7 @@ def pin_int8_write_layout(h):
                 assert np.allclose(sc.astype(np.float64) * 127, amax, rtol=2.0 ** -22, atol=0)
         blk, off = np.nonzero(~written)
         assert np.all(kc[blk, :, off, :] == W.INT8_POISON_CODE)
-        assert np.all(vc[blk, :, :, off] == W.INT8_POISON_CODE)
+        assert np.all(vc[blk, :, off, :] == W.INT8_POISON_CODE)
         assert np.all(np.isnan(ks[blk, :, off, :])) and np.all(np.isnan(vs[blk, :, off, :]))
         perm = rng.permutation(T)
         pools2 = oracle.int8_pools(NB, Hkv, bs, D, gs, fill_code=W.INT8_POISON_CODE)

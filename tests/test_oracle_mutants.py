@@ -90,9 +90,11 @@ MUTANTS = {
     # bf16 rounding truncates
     "bf16_round_trunc": ("double q = rint(a / ldexp(1.0, expo - 7));",
                          "double q = floor(a / ldexp(1.0, expo - 7));"),
-    # INT8: V codes stored and read token-major (the documented layout is dim-major)
-    "int8_v_token_major": ("return is_value ? base + (int64_t)d * a->block_size + off",
-                           "return is_value ? base + (int64_t)off * a->head_dim + d"),
+    # INT8: V codes stored and read in a plain token-major order
+    "int8_v_token_major": ("    int jv = row / 4;\n    return base + (",
+                           "    int jv = row / 4;\n    return base + (int64_t)off * a->head_dim + d + 0 * ("),
+    # INT8: K code lanes of one tile swapped (row and dim group transposed)
+    "int8_k_lane_order": ("16 * jk + row) * (a->head_dim / 32)", "4 * row + jk) * (a->head_dim / 32)"),
     # INT8: scale group taken modulo the group count instead of d / group_size
     "int8_scale_group": ("d / a->group_size)];", "d % (a->head_dim / a->group_size))];"),
     # INT8: K values scaled by the V scales
