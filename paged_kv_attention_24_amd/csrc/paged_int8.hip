@@ -41,8 +41,10 @@
 //    at the end.  The softmax reference max is lazy (p <= 2^8), so the MFMAs
 //    accumulate straight into O and a rescale is rare.
 //  * One partition per sequence: the wave writes the output.  Several: it
-//    writes (max, sum, O / sum) rows, and a merge launch combines them; a
-//    one-workgroup planning launch lists the (sequence, partition) items.
+//    writes (max, sum, O / sum) rows, and a merge launch combines them.  Up
+//    to 8 partitions per sequence the grid has one wave per (sequence,
+//    partition, kv head); beyond, a one-workgroup planning launch lists the
+//    (sequence, partition) items for a persistent grid.
 //  * Tokens past the unit's end are excluded by selects (scores to -inf,
 //    probabilities and scales to 0), so poisoned scales never reach O.
 #include <hip/hip_runtime.h>
@@ -67,6 +69,9 @@ constexpr int kI8Tiles = PKA_I8_TILES;        // 16-token tiles per step
 constexpr int kI8Step = 16 * kI8Tiles;        // tokens per step
 constexpr bool kI8Prefetch = PKA_I8_PREFETCH != 0;  // next step's loads in flight
 constexpr int kI8PlanThreads = 1024;    // planning workgroup
+// Up to this many partitions per sequence the decode launches one wave per
+// (sequence, partition, kv head) and no planning launch.
+constexpr int kI8DenseMaxPartitions = 8;
 
 // ---- quantising write ------------------------------------------------------
 
@@ -552,9 +557,11 @@ __device__ __forceinline__ void store_zero_rows(const Int8DecodeArgs &a, int b, 
         store_out(a.out, ((int64_t)b * a.num_q_heads + h * G) * D + e, 0.0f, a.out_kind);
 }
 
-// Dense mode (one partition covers every sequence): wave u handles unit
-// (b = u / Hkv, h = u % Hkv).  Work-list mode: the planned items (b, jp),
-// crossed with the kv heads, dealt round-robin to all waves of the grid.
+// Dense mode (at most kI8DenseMaxPartitions partitions per sequence): wave
+// u handles unit (b, jp, h), u = (b * NP + jp) * Hkv + h, and exits at once
+// when partition jp starts past the sequence's end.  Work-list mode: the
+// planned items (b, jp), crossed with the kv heads, dealt round-robin to all
+// waves of the grid.
 template <class QT, int D, int BS, int G, int GS, bool WORKLIST>
 __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8DecodeArgs a)
 {
@@ -562,15 +569,21 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t w0 = (int64_t)blockIdx.x * kI8Waves + wave;
     if constexpr (!WORKLIST) {
-        if (w0 >= (int64_t)a.num_seqs * a.num_kv_heads)
+        const int64_t per_seq = (int64_t)a.num_partitions * a.num_kv_heads;
+        if (w0 >= (int64_t)a.num_seqs * per_seq)
             return;
-        const int b = (int)(w0 / a.num_kv_heads), h = (int)(w0 % a.num_kv_heads);
+        const int b = (int)(w0 / per_seq);
+        const int jp = (int)(w0 % per_seq / a.num_kv_heads);
+        const int h = (int)(w0 % a.num_kv_heads);
         const int L = clamped_len(a, b);
         if (L == 0) {
-            store_zero_rows(a, b, h, G, D, lane);
+            if (jp == 0)
+                store_zero_rows(a, b, h, G, D, lane);
             return;
         }
-        run_unit<QT, D, BS, G, GS>(a, b, 0, h, L, lane);
+        if (jp * a.partition_size >= L)
+            return;
+        run_unit<QT, D, BS, G, GS>(a, b, jp, h, L, lane);
     } else {
         const int64_t units = (int64_t)__builtin_amdgcn_readfirstlane(a.wl_header[0]) *
                               a.num_kv_heads;
@@ -627,32 +640,68 @@ __global__ __launch_bounds__(kI8PlanThreads) void int8_plan_kernel(Int8DecodeArg
 
 // out[b][hq] from the partition rows of sequence b: exact log-sum-exp
 // merge; zero rows for L_b = 0; nothing for one partition (written by the
-// decode).  One workgroup of D threads per (b, hq).
+// decode).  One wave per (b, hq) row, kI8Waves rows per workgroup: lane k
+// takes partition k of a batch of 64 (its max, sum and weight), and every
+// lane accumulates its D / 64 dims over the batch with the weights read
+// from the lanes; batches merge with a running maximum.
 template <int D>
-__global__ __launch_bounds__(D) void int8_merge_kernel(Int8DecodeArgs a)
+__global__ __launch_bounds__(kI8Waves *kWave) void int8_merge_kernel(Int8DecodeArgs a)
 {
-    const int64_t r = blockIdx.x;
+    constexpr int E = D / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t r = (int64_t)blockIdx.x * kI8Waves + threadIdx.x / kWave;
+    if (r >= (int64_t)a.num_seqs * a.num_q_heads)
+        return;
     const int b = (int)(r / a.num_q_heads);
-    const int d = threadIdx.x;
     const int L = clamped_len(a, b);
     const int n = (L + a.partition_size - 1) / a.partition_size;
     if (L == 0) {
-        store_out(a.out, r * D + d, 0.0f, a.out_kind);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            store_out(a.out, r * D + lane * E + e, 0.0f, a.out_kind);
         return;
     }
     if (n <= 1)
         return;
     const int64_t row0 = r * a.num_partitions;
-    float M = -INFINITY;
-    for (int jp = 0; jp < n; ++jp)
-        M = fmaxf(M, a.ws_ml[2 * (row0 + jp)]);
-    float num = 0.0f, den = 0.0f;
-    for (int jp = 0; jp < n; ++jp) {
-        const float w = a.ws_ml[2 * (row0 + jp) + 1] * __builtin_amdgcn_exp2f(a.ws_ml[2 * (row0 + jp)] - M);
-        num = fmaf(w, a.ws_o[(row0 + jp) * D + d], num);
-        den += w;
+    float M = -INFINITY, den = 0.0f, acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        acc[e] = 0.0f;
+    for (int base = 0; base < n; base += kWave) {
+        const int cnt = min(kWave, n - base);
+        float2 ml = make_float2(-INFINITY, 0.0f);
+        if (lane < cnt)
+            ml = *reinterpret_cast<const float2 *>(a.ws_ml + 2 * (row0 + base + lane));
+        const float Mn = fmaxf(M, wave_max(ml.x));
+        const float alpha = __builtin_amdgcn_exp2f(M - Mn);
+        M = Mn;
+        const float w = lane < cnt ? ml.y * __builtin_amdgcn_exp2f(ml.x - M) : 0.0f;
+        float wsum = w;
+        wsum += dpp<0xB1>(wsum);
+        wsum += dpp<0x4E>(wsum);
+        wsum += dpp<0x141>(wsum);
+        wsum += dpp<0x140>(wsum);
+        wsum += swz_xor16(wsum);
+        wsum += xor32(wsum);
+        den = den * alpha + wsum;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[e] *= alpha;
+        const float *o = a.ws_o + (row0 + base) * D + lane * E;
+#pragma unroll 8
+        for (int k = 0; k < cnt; ++k) {
+            const float wk = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[e] = fmaf(wk, o[(int64_t)k * D + e], acc[e]);
+        }
     }
-    store_out(a.out, r * D + d, num / den, a.out_kind);
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        store_out(a.out, r * D + lane * E + e, acc[e] * inv, a.out_kind);
 }
 
 int compute_units()
@@ -672,33 +721,36 @@ int compute_units()
 template <class QT, int D, int BS, int G, int GS>
 hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
 {
-    if (a.num_partitions == 1) {
-        const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
+    if (a.num_partitions <= kI8DenseMaxPartitions) {
+        const int64_t waves = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
         const int64_t grid = (waves + kI8Waves - 1) / kI8Waves;
         hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, false>), dim3((unsigned)grid),
                            dim3(kI8Waves * kWave), 0, stream, a);
-        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL(int8_plan_kernel, dim3(1), dim3(kI8PlanThreads), 0, stream, a);
+        static int per_cu_cache[64];
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        int per_cu = dev >= 0 && dev < 64 ? per_cu_cache[dev] : 0;
+        if (per_cu == 0) {
+            (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, int8_decode_kernel<QT, D, BS, G, GS, true>, kI8Waves * kWave, 0);
+            per_cu = per_cu > 0 ? per_cu : 1;
+            if (dev >= 0 && dev < 64)
+                per_cu_cache[dev] = per_cu;
+        }
+        const int64_t max_units = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
+        int64_t grid = (int64_t)compute_units() * per_cu;
+        const int64_t need = (max_units + kI8Waves - 1) / kI8Waves;
+        grid = grid < need ? grid : need;
+        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, true>), dim3((unsigned)grid),
+                           dim3(kI8Waves * kWave), 0, stream, a);
     }
-    hipLaunchKernelGGL(int8_plan_kernel, dim3(1), dim3(kI8PlanThreads), 0, stream, a);
-    static int per_cu_cache[64];
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    int per_cu = dev >= 0 && dev < 64 ? per_cu_cache[dev] : 0;
-    if (per_cu == 0) {
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, int8_decode_kernel<QT, D, BS, G, GS, true>, kI8Waves * kWave, 0);
-        per_cu = per_cu > 0 ? per_cu : 1;
-        if (dev >= 0 && dev < 64)
-            per_cu_cache[dev] = per_cu;
+    if (a.num_partitions > 1) {
+        const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+        hipLaunchKernelGGL(int8_merge_kernel<D>, dim3((unsigned)((rows + kI8Waves - 1) / kI8Waves)),
+                           dim3(kI8Waves * kWave), 0, stream, a);
     }
-    const int64_t max_units = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
-    int64_t grid = (int64_t)compute_units() * per_cu;
-    const int64_t need = (max_units + kI8Waves - 1) / kI8Waves;
-    grid = grid < need ? grid : need;
-    hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, true>), dim3((unsigned)grid),
-                       dim3(kI8Waves * kWave), 0, stream, a);
-    hipLaunchKernelGGL(int8_merge_kernel<D>, dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
-                       dim3(D), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -130,9 +130,10 @@ SWEEP = [(qd, D, bs, G, gs) for qd in ("f16", "bf16") for D in (64, 128) for bs 
 
 @pytest.mark.parametrize("q_dtype,D,bs,G,gs", SWEEP)
 def test_decode_sweep(q_dtype, D, bs, G, gs):
-    """Ragged lengths (tails of every size, L = 1, an empty sequence), one
-    partition per sequence and then 32-token partitions (planning, decode
-    and merge launches)."""
+    """Ragged lengths (tails of every size, L = 1, an empty sequence): one
+    partition per sequence (a single launch), 32-token partitions (one wave
+    per unit, then the merge launch) and 16-token partitions (planned work
+    list, persistent grid, merge)."""
     Hkv = 2
     lens = (5, 37, 16, 1, 0, 33, 100, 64)
     wl = case(400 + D + bs + G + gs, q_dtype, lens, G * Hkv, Hkv, D, bs, gs)
@@ -140,6 +141,7 @@ def test_decode_sweep(q_dtype, D, bs, G, gs):
     ref = oracle_int8(wl)
     check(gpu_decode_int8(wl), ref, "one partition")
     check(gpu_decode_int8(wl, partition_size=32), ref, "32-token partitions")
+    check(gpu_decode_int8(wl, partition_size=16), ref, "16-token partitions")
 
 
 @pytest.mark.parametrize("cfg,gs", [(1, 32), (2, 32), (3, 32)])
@@ -235,10 +237,11 @@ def test_long_sequence_and_skew():
 
 
 def test_many_sequences_plan_in_chunks():
-    """2500 sequences: the planning launch scans them in chunks of 1024."""
+    """2500 sequences in 16-token partitions (up to 13 per sequence: the
+    planned work list): the planning launch scans them in chunks of 1024."""
     lens = np.random.default_rng(14).integers(0, 200, size=2500)
     wl = case(14, "bf16", lens, 4, 2, 64, 16, 64)
-    got = gpu_decode_int8(wl, partition_size=64)
+    got = gpu_decode_int8(wl, partition_size=16)
     rows = np.array([[b, h] for b in range(0, 2500, 37) for h in range(4)], dtype=np.int32)
     check(got[rows[:, 0], rows[:, 1]], oracle_int8(wl, rows=rows), "2500 sequences")
     zero = np.nonzero(wl.context_lens == 0)[0]
