@@ -130,18 +130,20 @@ SWEEP = [(qd, D, bs, G, gs) for qd in ("f16", "bf16") for D in (64, 128) for bs 
 
 @pytest.mark.parametrize("q_dtype,D,bs,G,gs", SWEEP)
 def test_decode_sweep(q_dtype, D, bs, G, gs):
-    """Ragged lengths (tails of every size, L = 1, an empty sequence): one
-    partition per sequence (a single launch), 32-token partitions (one wave
-    per unit, then the merge launch) and 16-token partitions (planned work
-    list, persistent grid, merge)."""
+    """Ragged lengths (tails of every size, L = 1, an empty sequence): the
+    library's partitions, one partition per sequence (a single launch),
+    64-token partitions (one wave per unit, then the merge launch) and
+    32-token partitions (10 for the longest: planned work list, persistent
+    grid, merge)."""
     Hkv = 2
-    lens = (5, 37, 16, 1, 0, 33, 100, 64)
+    lens = (5, 37, 16, 1, 0, 33, 100, 64, 290)
     wl = case(400 + D + bs + G + gs, q_dtype, lens, G * Hkv, Hkv, D, bs, gs)
     print(f"[int8-decode] {q_dtype} D={D} bs={bs} G={G} gs={gs}", flush=True)
     ref = oracle_int8(wl)
-    check(gpu_decode_int8(wl), ref, "one partition")
+    check(gpu_decode_int8(wl), ref, "library partitions")
+    check(gpu_decode_int8(wl, partition_size=320), ref, "one partition")
+    check(gpu_decode_int8(wl, partition_size=64), ref, "64-token partitions")
     check(gpu_decode_int8(wl, partition_size=32), ref, "32-token partitions")
-    check(gpu_decode_int8(wl, partition_size=16), ref, "16-token partitions")
 
 
 @pytest.mark.parametrize("cfg,gs", [(1, 32), (2, 32), (3, 32)])
