@@ -810,6 +810,30 @@ def run_int8(args, dev):
     nparts = -(-L // P)
     log(f"INT8 decode {us_layer:.2f} us per layer, {value:.0f} GB/s effective, P={P} "
         f"({nparts} partitions)")
+
+    # the quantising write: one new token per sequence (a decode step), and a
+    # prompt chunk of 16384 tokens (at most the pool's slots) into random
+    # slots of the first pool
+    # (16 launches per timed graph: one short launch per graph would time
+    # the graph launch)
+    kc0, vc0, ks0, vs0 = pools[0]
+    rep = 16
+    tdt = W.torch_dtype(wl.dtype)
+    wr = {}
+    for name, T in (("decode_step", B), ("prompt_chunk", min(16384, NB * bs))):
+        kn = fill_pool((T, Hkv, D), tdt, 7100 + T, dev)
+        vn = fill_pool((T, Hkv, D), tdt, 7200 + T, dev)
+        sl = torch.from_numpy(np.random.default_rng(T).permutation(NB * bs)[:T].astype(np.int64)).to(dev)
+
+        def writes():
+            for _ in range(rep):
+                pka.kv_cache_write_int8(kn, vn, sl, kc0, vc0, ks0, vs0)
+
+        ms_w = timed_calls(writes, args.steps, args.warmup, use_graph) / rep
+        moved = T * Hkv * (2 * D * wl.elt_bytes + 2 * D + 8 * ng) + 8 * T
+        wr[name] = {"tokens": T, "us_per_launch": round(ms_w * 1e3, 3),
+                    "gbps": round(moved / (ms_w * 1e-3) / 1e9, 2)}
+    log(f"INT8 write: {wr}")
     del pools
     torch.cuda.empty_cache()
 
@@ -885,6 +909,7 @@ def run_int8(args, dev):
             "parallelism": "single GPU",
         },
         "us_per_layer": round(us_layer, 3),
+        "quantising_write": wr,
         "half_kv_decode_same_shape": half,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "roofline": {
