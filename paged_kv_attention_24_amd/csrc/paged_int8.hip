@@ -43,8 +43,9 @@
 //  * One partition per sequence: the wave writes the output.  Several: it
 //    writes (max, sum, O / sum) rows, and a merge launch combines them.  Up
 //    to 8 partitions per sequence the grid has one wave per (sequence,
-//    partition, kv head); beyond, a one-workgroup planning launch lists the
-//    (sequence, partition) items for a persistent grid.
+//    partition, kv head); beyond, a persistent grid deals the (sequence,
+//    partition) items, found in a prefix each workgroup builds in LDS (up to
+//    4096 sequences) or listed by a one-workgroup planning launch.
 //  * Tokens past the unit's end are excluded by selects (scores to -inf,
 //    probabilities and scales to 0), so poisoned scales never reach O.
 #include <hip/hip_runtime.h>
@@ -72,6 +73,9 @@ constexpr int kI8PlanThreads = 1024;    // planning workgroup
 // Up to this many partitions per sequence the decode launches one wave per
 // (sequence, partition, kv head) and no planning launch.
 constexpr int kI8DenseMaxPartitions = 8;
+// Persistent grids over at most this many sequences plan their work in each
+// workgroup's LDS (a prefix of partition counts) instead of a planning launch.
+constexpr int kI8PlanInKernelSeqs = 4096;
 
 // ---- quantising write ------------------------------------------------------
 
@@ -557,18 +561,86 @@ __device__ __forceinline__ void store_zero_rows(const Int8DecodeArgs &a, int b, 
         store_out(a.out, ((int64_t)b * a.num_q_heads + h * G) * D + e, 0.0f, a.out_kind);
 }
 
-// Dense mode (at most kI8DenseMaxPartitions partitions per sequence): wave
-// u handles unit (b, jp, h), u = (b * NP + jp) * Hkv + h, and exits at once
-// when partition jp starts past the sequence's end.  Work-list mode: the
-// planned items (b, jp), crossed with the kv heads, dealt round-robin to all
-// waves of the grid.
-template <class QT, int D, int BS, int G, int GS, bool WORKLIST>
+// Exclusive prefix of the sequences' partition counts, prefix[b] = sum over
+// b' < b of ceil(L_b' / P), b = 0..B, in LDS; every thread of the workgroup
+// (NT of them) takes part.  wsum: NT / 64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ void build_prefix(const Int8DecodeArgs &a, int *prefix, int *wsum)
+{
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    int base = 0;
+    for (int b0 = 0; b0 < a.num_seqs; b0 += NT) {
+        const int b = b0 + t;
+        const int n = b < a.num_seqs ? (clamped_len(a, b) + a.partition_size - 1) / a.partition_size
+                                     : 0;
+        int x = n;  // inclusive scan within the wave, then across waves
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(x, d, kWave);
+            if (lane >= d)
+                x += y;
+        }
+        if (lane == kWave - 1)
+            wsum[wave] = x;
+        __syncthreads();
+        int before = base;
+        for (int w = 0; w < wave; ++w)
+            before += wsum[w];
+        if (b < a.num_seqs)
+            prefix[b] = before + x - n;
+        int total = base;
+        for (int w = 0; w < NT / kWave; ++w)
+            total += wsum[w];
+        __syncthreads();
+        base = total;
+    }
+    if (t == 0)
+        prefix[a.num_seqs] = base;
+    __syncthreads();
+}
+
+// One workgroup (batches of more than kI8PlanInKernelSeqs sequences): items
+// (b, jp) for jp < ceil(L_b / P), sequences in order, written to a.items;
+// their count to a.wl_header[0].
+__global__ __launch_bounds__(kI8PlanThreads) void int8_plan_kernel(Int8DecodeArgs a)
+{
+    __shared__ int wsum[kI8PlanThreads / kWave];
+    __shared__ int chunk[kI8PlanThreads + 1];
+    const int t = threadIdx.x;
+    int base = 0;
+    for (int b0 = 0; b0 < a.num_seqs; b0 += kI8PlanThreads) {
+        const int cnt = min(kI8PlanThreads, a.num_seqs - b0);
+        Int8DecodeArgs sub = a;
+        sub.num_seqs = cnt;
+        sub.context_lens = a.context_lens + b0;
+        build_prefix<kI8PlanThreads>(sub, chunk, wsum);
+        if (t < cnt) {
+            const int start = base + chunk[t];
+            const int n = chunk[t + 1] - chunk[t];
+            for (int k = 0; k < n; ++k)
+                a.items[start + k] = make_int2(b0 + t, k);
+        }
+        base += chunk[cnt];
+        __syncthreads();
+    }
+    if (t == 0)
+        a.wl_header[0] = base;
+}
+
+// MODE 0, dense (at most kI8DenseMaxPartitions partitions per sequence):
+// wave u handles unit (b, jp, h), u = (b * NP + jp) * Hkv + h, and exits at
+// once when partition jp starts past the sequence's end.  MODE 1 and 2, a
+// persistent grid: the items (b, jp), crossed with the kv heads, are dealt
+// round-robin to all waves of the grid; MODE 1 reads them from the list a
+// planning launch wrote, MODE 2 (at most kI8PlanInKernelSeqs sequences)
+// finds them in a prefix of partition counts each workgroup builds in LDS.
+template <class QT, int D, int BS, int G, int GS, int MODE>
 __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8DecodeArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t w0 = (int64_t)blockIdx.x * kI8Waves + wave;
-    if constexpr (!WORKLIST) {
+    if constexpr (MODE == 0) {
         const int64_t per_seq = (int64_t)a.num_partitions * a.num_kv_heads;
         if (w0 >= (int64_t)a.num_seqs * per_seq)
             return;
@@ -584,7 +656,7 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
         if (jp * a.partition_size >= L)
             return;
         run_unit<QT, D, BS, G, GS>(a, b, jp, h, L, lane);
-    } else {
+    } else if constexpr (MODE == 1) {
         const int64_t units = (int64_t)__builtin_amdgcn_readfirstlane(a.wl_header[0]) *
                               a.num_kv_heads;
         const int64_t stride = (int64_t)gridDim.x * kI8Waves;
@@ -595,47 +667,55 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
             const int h = (int)(u % a.num_kv_heads);
             run_unit<QT, D, BS, G, GS>(a, b, jp, h, clamped_len(a, b), lane);
         }
+    } else {
+        extern __shared__ int i8_lds[];
+        int *wsum = i8_lds;                      // [kI8Waves]
+        int *prefix = i8_lds + kI8Waves;         // [B + 1]
+        build_prefix<kI8Waves * kWave>(a, prefix, wsum);
+        const int64_t units = (int64_t)prefix[a.num_seqs] * a.num_kv_heads;
+        const int64_t stride = (int64_t)gridDim.x * kI8Waves;
+        for (int64_t u = w0; u < units; u += stride) {
+            const int item = (int)(u / a.num_kv_heads);
+            int lo = 0, hi = a.num_seqs;  // the last b with prefix[b] <= item
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (prefix[mid] <= item)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int b = __builtin_amdgcn_readfirstlane(lo);
+            const int jp = __builtin_amdgcn_readfirstlane(item - prefix[lo]);
+            const int h = (int)(u % a.num_kv_heads);
+            run_unit<QT, D, BS, G, GS>(a, b, jp, h, clamped_len(a, b), lane);
+        }
     }
 }
 
-// One workgroup: items (b, jp) for jp < ceil(L_b / P), sequences in order,
-// written to a.items; their count to a.wl_header[0].
-__global__ __launch_bounds__(kI8PlanThreads) void int8_plan_kernel(Int8DecodeArgs a)
+// acc[e] += sum_{k < cnt} w_k o[k * stride + e], w_k held by lane k: the
+// loads of all N rows are issued before the first is used (rows past cnt
+// repeat the last one and get weight 0).
+template <int N, int E>
+__device__ __forceinline__ void accumulate_rows(const float *o, int stride, int cnt, float w,
+                                                float (&acc)[E])
 {
-    __shared__ int sums[kI8PlanThreads / kWave];
-    __shared__ int base;
-    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-    if (t == 0)
-        base = 0;
-    __syncthreads();
-    for (int b0 = 0; b0 < a.num_seqs; b0 += kI8PlanThreads) {
-        const int b = b0 + t;
-        const int n = b < a.num_seqs ? (clamped_len(a, b) + a.partition_size - 1) / a.partition_size
-                                     : 0;
-        // inclusive scan within the wave, then across waves
-        int x = n;
+    float v[N][E];
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int y = __shfl_up(x, d, kWave);
-            if (lane >= d)
-                x += y;
-        }
-        if (lane == kWave - 1)
-            sums[wave] = x;
-        __syncthreads();
-        int before = base;
-        for (int w = 0; w < wave; ++w)
-            before += sums[w];
-        const int start = before + x - n;
-        for (int k = 0; k < n; ++k)
-            a.items[start + k] = make_int2(b, k);
-        __syncthreads();
-        if (t == kI8PlanThreads - 1)
-            base = start + n;
-        __syncthreads();
+    for (int k = 0; k < N; ++k) {
+        const int kk = k < cnt ? k : cnt - 1;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            v[k][e] = o[(int64_t)kk * stride + e];
     }
-    if (t == 0)
-        a.wl_header[0] = base;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const float wk = k < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                 __builtin_bit_cast(int, w), k))
+                                 : 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[e] = fmaf(wk, v[k][e], acc[e]);
+    }
 }
 
 // out[b][hq] from the partition rows of sequence b: exact log-sum-exp
@@ -689,14 +769,14 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_merge_kernel(Int8DecodeA
         for (int e = 0; e < E; ++e)
             acc[e] *= alpha;
         const float *o = a.ws_o + (row0 + base) * D + lane * E;
-#pragma unroll 8
-        for (int k = 0; k < cnt; ++k) {
-            const float wk = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                acc[e] = fmaf(wk, o[(int64_t)k * D + e], acc[e]);
-        }
+        if (cnt <= 8)
+            accumulate_rows<8, E>(o, D, cnt, w, acc);
+        else if (cnt <= 16)
+            accumulate_rows<16, E>(o, D, cnt, w, acc);
+        else if (cnt <= 32)
+            accumulate_rows<32, E>(o, D, cnt, w, acc);
+        else
+            accumulate_rows<kWave, E>(o, D, cnt, w, acc);
     }
     const float inv = 1.0f / den;
 #pragma unroll
@@ -724,27 +804,42 @@ hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
     if (a.num_partitions <= kI8DenseMaxPartitions) {
         const int64_t waves = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
         const int64_t grid = (waves + kI8Waves - 1) / kI8Waves;
-        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 0>), dim3((unsigned)grid),
                            dim3(kI8Waves * kWave), 0, stream, a);
     } else {
-        hipLaunchKernelGGL(int8_plan_kernel, dim3(1), dim3(kI8PlanThreads), 0, stream, a);
-        static int per_cu_cache[64];
+        const bool in_kernel = a.num_seqs <= kI8PlanInKernelSeqs;
+        const size_t lds = in_kernel ? (size_t)(kI8Waves + a.num_seqs + 1) * 4 : 0;
+        if (!in_kernel)
+            hipLaunchKernelGGL(int8_plan_kernel, dim3(1), dim3(kI8PlanThreads), 0, stream, a);
+        static int per_cu_cache[64][2];
         int dev = 0;
         (void)hipGetDevice(&dev);
-        int per_cu = dev >= 0 && dev < 64 ? per_cu_cache[dev] : 0;
+        const int kind = in_kernel ? 1 : 0;
+        int per_cu = dev >= 0 && dev < 64 ? per_cu_cache[dev][kind] : 0;
         if (per_cu == 0) {
-            (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, int8_decode_kernel<QT, D, BS, G, GS, true>, kI8Waves * kWave, 0);
+            // the largest in-kernel plan (kI8PlanInKernelSeqs sequences) sizes
+            // the cached figure, so it holds for every smaller batch
+            if (in_kernel)
+                (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, int8_decode_kernel<QT, D, BS, G, GS, 2>, kI8Waves * kWave,
+                    (size_t)(kI8Waves + kI8PlanInKernelSeqs + 1) * 4);
+            else
+                (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, int8_decode_kernel<QT, D, BS, G, GS, 1>, kI8Waves * kWave, 0);
             per_cu = per_cu > 0 ? per_cu : 1;
             if (dev >= 0 && dev < 64)
-                per_cu_cache[dev] = per_cu;
+                per_cu_cache[dev][kind] = per_cu;
         }
         const int64_t max_units = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
         int64_t grid = (int64_t)compute_units() * per_cu;
         const int64_t need = (max_units + kI8Waves - 1) / kI8Waves;
         grid = grid < need ? grid : need;
-        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, true>), dim3((unsigned)grid),
-                           dim3(kI8Waves * kWave), 0, stream, a);
+        if (in_kernel)
+            hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 2>), dim3((unsigned)grid),
+                               dim3(kI8Waves * kWave), lds, stream, a);
+        else
+            hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 1>), dim3((unsigned)grid),
+                               dim3(kI8Waves * kWave), 0, stream, a);
     }
     if (a.num_partitions > 1) {
         const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;

@@ -238,16 +238,18 @@ def test_long_sequence_and_skew():
     check(got[rows[:, 0], rows[:, 1]], oracle_int8(wl, rows=rows), "skewed")
 
 
-def test_many_sequences_plan_in_chunks():
-    """2500 sequences in 16-token partitions (up to 13 per sequence: the
-    planned work list): the planning launch scans them in chunks of 1024."""
-    lens = np.random.default_rng(14).integers(0, 200, size=2500)
+@pytest.mark.parametrize("nseq", [2500, 4500])
+def test_many_sequences(nseq):
+    """Many sequences in 16-token partitions (up to 13 per sequence: a
+    persistent grid).  2500 sequences: each workgroup plans its work in LDS;
+    4500: past that limit, a planning launch scans them in chunks of 1024."""
+    lens = np.random.default_rng(14).integers(0, 200, size=nseq)
     wl = case(14, "bf16", lens, 4, 2, 64, 16, 64)
     got = gpu_decode_int8(wl, partition_size=16)
-    rows = np.array([[b, h] for b in range(0, 2500, 37) for h in range(4)], dtype=np.int32)
-    check(got[rows[:, 0], rows[:, 1]], oracle_int8(wl, rows=rows), "2500 sequences")
+    rows = np.array([[b, h] for b in range(0, nseq, 37) for h in range(4)], dtype=np.int32)
+    check(got[rows[:, 0], rows[:, 1]], oracle_int8(wl, rows=rows), f"{nseq} sequences")
     zero = np.nonzero(wl.context_lens == 0)[0]
-    assert np.all(got[zero] == 0.0)
+    assert len(zero) and np.all(got[zero] == 0.0)
 
 
 def test_large_dynamic_range_of_scales():
