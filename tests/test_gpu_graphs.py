@@ -1,4 +1,4 @@
-"""GPU: the multi-token attention, the RoPE write and the block moves
+"""GPU: the multi-token attention, the RoPE write, the block moves and the INT8 write and decode
 captured in a HIP graph and replayed several times, with eager calls in
 between, give the eager results bit for bit."""
 import numpy as np
@@ -106,3 +106,35 @@ def test_block_moves_graph_replay():
         pka.scatter_blocks(kc, vc, packed, perm[160:192].to(torch.int64))
 
     replay_matches(call, [kc, vc, packed], reset=reset)
+
+
+@pytest.mark.parametrize("P", [0, 32, 16])
+def test_int8_write_and_decode_graph_replay(P):
+    """The INT8 quantising write followed by the INT8 decode, captured
+    together: one partition (a single launch), one wave per unit plus the
+    merge launch (32-token partitions), and the persistent grid that plans
+    in LDS (16-token partitions)."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+
+    # no NaN poison here: the replayed pools are compared with torch.equal
+    wl = W.make_int8_case(82, q_dtype="f16", context_lens=(5, 37, 200, 1, 64), num_q_heads=8,
+                          num_kv_heads=2, head_dim=64, block_size=16, group_size=32,
+                          poison=False)
+    d = W.int8_device_inputs(wl)
+    pools = [d["k_codes"], d["v_codes"], d["k_scales"], d["v_scales"]]
+    start = [t.clone() for t in pools]
+    out = torch.empty((wl.num_seqs, 8, 64), device="cuda")
+
+    def reset():
+        for t, s0 in zip(pools, start):
+            t.copy_(s0)
+
+    def call():
+        pka.kv_cache_write_int8(d["new_k"], d["new_v"], d["slot_mapping"], *pools)
+        pka.paged_attention_decode_int8(d["q"], *pools, d["block_tables"], d["context_lens"],
+                                        float(wl.scale), 2, 16, out=out, partition_size=P,
+                                        max_context_len=wl.max_context_len)
+
+    replay_matches(call, [out] + pools, reset=reset)
