@@ -749,9 +749,9 @@ INT8_TAGS = {2: "paged_decode_int8_llama3_1b_b16", 3: "paged_decode_int8_mix_b64
 def run_int8(args, dev):
     """Decode over group-quantised INT8 pools (codes + float32 group scales)
     for workload 2-5's shapes and lengths, over enough layer pools to exceed
-    1 GB (16 for workload 2), one call per layer (the decode launch, or the
-    planning, decode and merge launches when a sequence spans several
-    partitions); beside it, the plain fp16/bf16 decode of the same shape."""
+    1 GB (16 for workload 2), one call per layer (the decode launch, plus the
+    merge launch when a sequence spans several partitions); beside it, the
+    quantising write and the plain fp16/bf16 decode of the same shape."""
     import torch
 
     import paged_kv_attention_24_amd as pka
@@ -915,8 +915,9 @@ def run_int8(args, dev):
         "roofline": {
             "bound": "hbm",
             "kernel": ("int8_decode_kernel (one launch per layer)" if nparts == 1 else
-                       "int8_plan_kernel + int8_decode_kernel + int8_merge_kernel (per layer)"),
-            "launches_per_layer": 1 if nparts == 1 else 3,
+                       "int8_decode_kernel + int8_merge_kernel (per layer)" if nparts <= 8 or B <= 4096
+                       else "int8_plan_kernel + int8_decode_kernel + int8_merge_kernel (per layer)"),
+            "launches_per_layer": 1 if nparts == 1 else (2 if nparts <= 8 or B <= 4096 else 3),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
