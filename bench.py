@@ -758,7 +758,7 @@ def run_int8(args, dev):
     from paged_kv_attention_24_amd import workloads as W
 
     cfg, gs = args.config, args.group_size
-    wl = W.make_config(cfg, pools=False, poison=False, write=False)
+    wl = W.make_config(cfg, pools=False, poison=False, write=True)
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
     NB, ng = wl.num_blocks, D // gs
     q = W.as_torch(wl.q, wl.dtype, dev)
@@ -800,6 +800,24 @@ def run_int8(args, dev):
     use_graph = not args.eager
     ms_step = timed_calls(step, args.steps, args.warmup, use_graph)
     us_layer = ms_step * 1e3 / R
+
+    # the whole decode step in one call per layer: the new token of every
+    # sequence quantised and stored at the slot of its position L - 1, then
+    # the attention (pka_paged_attention_decode_append_int8)
+    new_k = W.as_torch(wl.new_k, wl.dtype, dev)
+    new_v = W.as_torch(wl.new_v, wl.dtype, dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+
+    def fused_step():
+        for r in range(R):
+            kc, vc, ks, vs = pools[r]
+            pka.paged_attention_decode_append_int8(q, new_k, new_v, slots, kc, vc, ks, vs, bt, cl,
+                                                   float(wl.scale), Hkv, bs, out=outs[r],
+                                                   partition_size=P, max_context_len=L,
+                                                   workspace=ws)
+
+    us_fused = timed_calls(fused_step, args.steps, args.warmup, use_graph) * 1e3 / R
+    log(f"INT8 fused write + decode step {us_fused:.2f} us per layer")
     wl8 = W.Int8Workload(**{f: getattr(wl, f) for f in W.Workload.__dataclass_fields__},
                          group_size=gs)
     kv_bytes = wl8.kv_bytes()
@@ -909,6 +927,7 @@ def run_int8(args, dev):
             "parallelism": "single GPU",
         },
         "us_per_layer": round(us_layer, 3),
+        "us_per_layer_fused_step": round(us_fused, 3),
         "quantising_write": wr,
         "half_kv_decode_same_shape": half,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

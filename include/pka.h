@@ -20,7 +20,8 @@
  *     ->  pka_copy_blocks, pka_gather_blocks, pka_scatter_blocks.
  *   - "Technical details > INT8 quantisation" (group-wise INT8 with groups
  *     of 32, 64 or 128), applied to the KV cache
- *     ->  pka_kv_cache_write_int8, pka_paged_attention_decode_int8.
+ *     ->  pka_kv_cache_write_int8, pka_paged_attention_decode_int8,
+ *     pka_paged_attention_decode_append_int8.
  *
  * Conventions (same README, "Modern C++20 architecture": explicit error
  * results instead of exceptions, zero-copy borrowed buffers):
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 5
+#define PKA_ABI_VERSION 6
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -451,6 +452,38 @@ pka_status pka_paged_attention_decode_int8(
     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/*
+ * pka_paged_attention_decode_append_int8 -- one decode step over INT8 pools
+ * in one launch (two past 8 partitions per sequence: the merge): for every
+ * sequence b with L_b >= 1, its new token's K/V rows (k_new[b], v_new[b],
+ * [num_seqs][num_kv_heads][head_dim] of q_dtype) are quantised and stored
+ * at slot_mapping[b], and the decode then attends over L_b tokens, as
+ * pka_kv_cache_write_int8 followed by pka_paged_attention_decode_int8 would
+ * (bit-identical pools and output).  slot_mapping[b] must be the slot of
+ * position L_b - 1 (a negative slot, or one past the pool, stores nothing
+ * and position L_b - 1 is read from the pool as it is); a slot that this
+ * call reads for another position races with the store.  Sequences with
+ * L_b <= 0 store nothing and yield a zero row.  The PhotonInfer README's
+ * batched write ("Technical details > Paged attention") fused with its
+ * batched decode, over the INT8 cache of "Technical details > INT8
+ * quantisation".
+ *   k_new, v_new   device, token strides k_new_token_stride /
+ *                  v_new_token_stride (elements, >= num_kv_heads * head_dim),
+ *                  heads head_dim apart, of q_dtype.
+ *   slot_mapping   device, int64 [num_seqs].
+ * Everything else as for pka_paged_attention_decode_int8 (the pools are
+ * written, so they are not const here).
+ */
+pka_status pka_paged_attention_decode_append_int8(
+    void *out, pka_dtype out_dtype, const void *q, pka_dtype q_dtype, const void *k_new,
+    const void *v_new, int64_t k_new_token_stride, int64_t v_new_token_stride,
+    const int64_t *slot_mapping, int8_t *k_codes, int8_t *v_codes, float *k_scales,
+    float *v_scales, const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
     int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
     void *stream);
 

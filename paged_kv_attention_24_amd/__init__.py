@@ -46,7 +46,7 @@ __all__ = [
     "decode_partition_size",
     "decode_workspace_bytes", "PagedKVCache", "library_path", "load_library",
     "kv_cache_write_int8", "paged_attention_decode_int8", "decode_int8_partition_size",
-    "decode_int8_workspace_bytes", "int8_pools",
+    "decode_int8_workspace_bytes", "int8_pools", "paged_attention_decode_append_int8",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -124,6 +124,10 @@ def load_library():
         P, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
         i32, ctypes.c_float, i32, i32, P, ctypes.c_size_t, P]
     lib.pka_paged_attention_decode_int8.restype = ctypes.c_int
+    lib.pka_paged_attention_decode_append_int8.argtypes = [
+        P, ctypes.c_int, P, ctypes.c_int, P, P, i64, i64, P, P, P, P, P, P, i32, P, i32, i32, i32,
+        i32, i32, i32, i32, ctypes.c_float, i32, i32, P, ctypes.c_size_t, P]
+    lib.pka_paged_attention_decode_append_int8.restype = ctypes.c_int
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_last_error.argtypes = []
@@ -644,10 +648,41 @@ def decode_int8_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
                                                               max_context_len, partition_size))
 
 
+def paged_attention_decode_append_int8(q, k_new, v_new, slot_mapping, k_codes, v_codes, k_scales,
+                                       v_scales, block_tables, context_lens, scale: float,
+                                       num_kv_heads: int, block_size: int, *, out=None,
+                                       out_dtype=None, partition_size: int = 0,
+                                       max_context_len: int = 0, workspace=None):
+    """One fused INT8 decode step: quantise and store each sequence's new
+    token (k_new[b], v_new[b], [B, Hkv, D] in q's dtype) at slot_mapping[b]
+    (int64 [B], the slot of position L_b - 1) and attend over its L_b tokens;
+    bit-identical to kv_cache_write_int8 followed by
+    paged_attention_decode_int8.  Mutates the pools; returns out."""
+    import torch
+
+    _, Hkv, _, D, _ = _int8_pool_shapes(k_codes, v_codes, k_scales, v_scales)
+    _require_gpu(k_new, v_new, slot_mapping)
+    B = q.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 3 or tuple(t.shape) != (B, Hkv, D):
+            raise ValueError(f"{name} must be [{B}, {Hkv}, {D}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} must have contiguous heads (strides [*, {D}, 1])")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [B]")
+    return paged_attention_decode_int8(
+        q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, scale, num_kv_heads,
+        block_size, out=out, out_dtype=out_dtype, partition_size=partition_size,
+        max_context_len=max_context_len, workspace=workspace,
+        _append=(k_new, v_new, slot_mapping.contiguous()))
+
+
 def paged_attention_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_tables,
                                 context_lens, scale: float, num_kv_heads: int, block_size: int,
                                 *, out=None, out_dtype=None, partition_size: int = 0,
-                                max_context_len: int = 0, workspace=None):
+                                max_context_len: int = 0, workspace=None, _append=None):
     """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache,
     K and V being code * scale of the INT8 pools.  q [B, Hq, D] float16 or
     bfloat16; returns out [B, Hq, D] (float32 unless ``out_dtype`` or ``out``
@@ -694,6 +729,15 @@ def paged_attention_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_t
                              f"bytes, {need} needed")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     lib = load_library()
+    if _append is not None:
+        kn, vn, sm = _append
+        _check(lib.pka_paged_attention_decode_append_int8(
+            out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), _dtype_code(q.dtype),
+            kn.data_ptr(), vn.data_ptr(), kn.stride(0), vn.stride(0), sm.data_ptr(),
+            k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
+            block_tables.data_ptr(), MB, context_lens.data_ptr(), B, Hq, Hkv, D, NB, bs, gs,
+            float(scale), hint, P, ws_ptr, ws_bytes, _stream_ptr(q.device)))
+        return out
     _check(lib.pka_paged_attention_decode_int8(
         out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), _dtype_code(q.dtype),
         k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),

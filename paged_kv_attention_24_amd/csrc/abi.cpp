@@ -616,14 +616,17 @@ size_t pka_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
         .total;
 }
 
-pka_status pka_paged_attention_decode_int8(
+}  // extern "C"
+
+static pka_status decode_int8_impl(
     void *out, pka_dtype out_dtype, const void *q, pka_dtype q_dtype, const int8_t *k_codes,
     const int8_t *v_codes, const float *k_scales, const float *v_scales,
     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
     int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
-    void *stream)
+    void *stream, const void *k_new, const void *v_new, int64_t k_new_stride,
+    int64_t v_new_stride, const int64_t *slot_mapping)
 {
     if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype))
         return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype");
@@ -725,10 +728,63 @@ pka_status pka_paged_attention_decode_int8(
         a.ws_ml = reinterpret_cast<float *>(base + w.ml_offset);
         a.ws_o = reinterpret_cast<float *>(base + w.o_offset);
     }
+    if (k_new || v_new || slot_mapping) {
+        if (!k_new || !v_new || !slot_mapping)
+            return fail(PKA_ERR_INVALID_ARGUMENT, "null k_new, v_new or slot_mapping");
+        const int64_t row = (int64_t)num_kv_heads * head_dim;
+        if (k_new_stride < row || v_new_stride < row)
+            return fail(PKA_ERR_INVALID_ARGUMENT,
+                        "new-token strides (%lld, %lld) must be >= num_kv_heads * head_dim = %lld",
+                        (long long)k_new_stride, (long long)v_new_stride, (long long)row);
+        if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 1u)
+            return fail(PKA_ERR_INVALID_ARGUMENT, "k_new/v_new not aligned to their element size");
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_new_stride = k_new_stride;
+        a.v_new_stride = v_new_stride;
+        a.slot_mapping = slot_mapping;
+    }
     hipError_t e = pka::launch_paged_decode_int8(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(PKA_ERR_HIP, "paged_attention_decode_int8 launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+extern "C" {
+
+pka_status pka_paged_attention_decode_int8(
+    void *out, pka_dtype out_dtype, const void *q, pka_dtype q_dtype, const int8_t *k_codes,
+    const int8_t *v_codes, const float *k_scales, const float *v_scales,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream)
+{
+    return decode_int8_impl(out, out_dtype, q, q_dtype, k_codes, v_codes, k_scales, v_scales,
+                            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, num_blocks, block_size, group_size, scale,
+                            max_context_len, partition_size, workspace, workspace_bytes, stream,
+                            nullptr, nullptr, 0, 0, nullptr);
+}
+
+pka_status pka_paged_attention_decode_append_int8(
+    void *out, pka_dtype out_dtype, const void *q, pka_dtype q_dtype, const void *k_new,
+    const void *v_new, int64_t k_new_token_stride, int64_t v_new_token_stride,
+    const int64_t *slot_mapping, int8_t *k_codes, int8_t *v_codes, float *k_scales,
+    float *v_scales, const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t group_size, float scale,
+    int32_t max_context_len, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream)
+{
+    if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "null k_new, v_new or slot_mapping");
+    return decode_int8_impl(out, out_dtype, q, q_dtype, k_codes, v_codes, k_scales, v_scales,
+                            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, num_blocks, block_size, group_size, scale,
+                            max_context_len, partition_size, workspace, workspace_bytes, stream,
+                            k_new, v_new, k_new_token_stride, v_new_token_stride, slot_mapping);
 }
 
 }  // extern "C"

@@ -46,6 +46,10 @@
 //    partition, kv head); beyond, a persistent grid deals the (sequence,
 //    partition) items, found in a prefix each workgroup builds in LDS (up to
 //    4096 sequences) or listed by a one-workgroup planning launch.
+//  * Fused append (pka_paged_attention_decode_append_int8): the unit that
+//    holds position L_b - 1 quantises and stores the new K/V rows of its kv
+//    head before it reads anything, so the result is that of the write
+//    followed by the decode.
 //  * Tokens past the unit's end are excluded by selects (scores to -inf,
 //    probabilities and scales to 0), so poisoned scales never reach O.
 #include <hip/hip_runtime.h>
@@ -105,29 +109,19 @@ __device__ __forceinline__ float load_as_f32(TBF16, const void *p, int64_t i)
     return as_f((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
 }
 
-// One wave per (new token, kv head, tensor): lane l quantises dims
-// [l*E, l*E + E), E = D / 64; a group spans GS / E lanes.
+// Quantise one token's row of one kv head (D elements of type T at
+// src[src_row ..]) and store its codes and scales at (block blk, offset off)
+// of a pool: the group's amax is a max over the GS / E lanes holding it,
+// s = amax / 127 (IEEE division), codes rint(x / s).  Lane l handles dims
+// [l*E, l*E + E), E = D / 64; it returns the scale of its group.
 template <class T, int D, int GS>
-__global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
+__device__ __forceinline__ float quantize_store_row(const void *src, int64_t src_row, bool is_value,
+                                                   int8_t *codes_pool, float *scales_pool,
+                                                   int num_kv_heads, int block_size, int64_t blk,
+                                                   int h, int off, int lane)
 {
     constexpr int E = D / kWave;
     constexpr int NG = D / GS;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;
-    if (wid >= 2 * rows)
-        return;
-    const int is_value = (int)(wid / rows);
-    const int64_t r = wid % rows;
-    const int64_t i = r / a.num_kv_heads;
-    const int h = (int)(r % a.num_kv_heads);
-    const int64_t slot = a.slot_mapping[i];
-    if (slot < 0 || slot >= (int64_t)a.num_blocks * a.block_size)
-        return;
-    const int64_t blk = slot / a.block_size;
-    const int off = (int)(slot % a.block_size);
-    const void *src = is_value ? a.v : a.k;
-    const int64_t src_row = i * (is_value ? a.v_token_stride : a.k_token_stride) + (int64_t)h * D;
     float x[E];
     float amax = 0.0f;
 #pragma unroll
@@ -144,8 +138,8 @@ __global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
         q = fminf(fmaxf(q, -127.0f), 127.0f);
         c[e] = (int8_t)q;
     }
-    const int64_t run = blk * a.num_kv_heads + h;  // this block's run of codes
-    int8_t *codes = (is_value ? a.v_codes : a.k_codes) + run * a.block_size * D;
+    const int64_t run = blk * num_kv_heads + h;  // this block's run of codes
+    int8_t *codes = codes_pool + run * block_size * D;
     const int tl = off / 16, row = off % 16;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -155,10 +149,32 @@ __global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
                      : ((int64_t)(tl * 64 + 16 * ((d % 32) / 8) + row) * (D / 32) + d / 32) * 8 + d % 8;
         codes[pos] = c[e];
     }
-    if ((lane * E) % GS == 0) {
-        float *scales = is_value ? a.v_scales : a.k_scales;
-        scales[(run * a.block_size + off) * NG + lane * E / GS] = s;
-    }
+    if ((lane * E) % GS == 0)
+        scales_pool[(run * block_size + off) * NG + lane * E / GS] = s;
+    return s;  // the scale of the lane's group
+}
+
+// One wave per (new token, kv head, tensor).
+template <class T, int D, int GS>
+__global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;
+    if (wid >= 2 * rows)
+        return;
+    const int is_value = (int)(wid / rows);
+    const int64_t r = wid % rows;
+    const int64_t i = r / a.num_kv_heads;
+    const int h = (int)(r % a.num_kv_heads);
+    const int64_t slot = a.slot_mapping[i];
+    if (slot < 0 || slot >= (int64_t)a.num_blocks * a.block_size)
+        return;
+    const void *src = is_value ? a.v : a.k;
+    const int64_t src_row = i * (is_value ? a.v_token_stride : a.k_token_stride) + (int64_t)h * D;
+    quantize_store_row<T, D, GS>(src, src_row, is_value, is_value ? a.v_codes : a.k_codes,
+                                 is_value ? a.v_scales : a.k_scales, a.num_kv_heads, a.block_size,
+                                 slot / a.block_size, h, (int)(slot % a.block_size), lane);
 }
 
 // ---- decode ----------------------------------------------------------------
@@ -438,6 +454,39 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
     const int P = a.partition_size;
     const int t_begin = jp * P;
     const int t_end = min(t_begin + P, L);
+    // Fused append: the unit that holds position L - 1 quantises the
+    // sequence's new K/V rows of this kv head and stores them at their slot
+    // first; it reads them back with the last step (after a fence there),
+    // exactly as a decode after the write would.  Its V-scale pass takes
+    // the new scales from the registers.
+    const bool appending = a.k_new != nullptr && jp == (L - 1) / P;
+    bool stored = false;
+    float new_vs = 0.0f;  // this lane's group's scale of the new V row
+    if (appending) {
+        const int64_t slot = a.slot_mapping[b];
+        if (slot >= 0 && slot < (int64_t)a.num_blocks * BS) {
+            const int64_t blk = slot / BS;
+            const int off = (int)(slot % BS);
+            quantize_store_row<QT, D, GS>(a.k_new, (int64_t)b * a.k_new_stride + (int64_t)h * D,
+                                          false, const_cast<int8_t *>(a.k_codes),
+                                          const_cast<float *>(a.k_scales), a.num_kv_heads, BS,
+                                          blk, h, off, lane);
+            new_vs = quantize_store_row<QT, D, GS>(
+                a.v_new, (int64_t)b * a.v_new_stride + (int64_t)h * D, true,
+                const_cast<int8_t *>(a.v_codes), const_cast<float *>(a.v_scales), a.num_kv_heads,
+                BS, blk, h, off, lane);
+            stored = true;
+        }
+    }
+    // before the first read of the stored rows: the stores complete, and no
+    // stale line of them stays in this compute unit's L1
+    auto publish = [&]() __attribute__((always_inline)) {
+        if (stored) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            stored = false;
+        }
+    };
     // the partition's block ids, one per lane (clamped into the table row
     // and into the pool, so every access stays in bounds)
     const int nb = (t_end - t_begin + BS - 1) / BS;
@@ -472,19 +521,26 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int flat = 4 * k4 + e;
-                    const bool valid = t0 + flat / NG < t_end;
+                    // position L - 1 of an appending unit: its new scale below
+                    const bool valid = t0 + flat / NG < (stored ? t_end - 1 : t_end);
                     sig[flat % NG] = fmaxf(sig[flat % NG], valid ? f4(v, e) : 0.0f);
                 }
             }
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
+            float m = wave_max(sig[g]);
+            if (stored)  // the lanes of group g hold its scale: lane g * GS / (D / 64)
+                m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                           __builtin_bit_cast(int, new_vs),
+                                                           g * GS / (D / kWave))));
             float inv_r;
-            pow2_normaliser(wave_max(sig[g]), st.r[g], inv_r);
+            pow2_normaliser(m, st.r[g], inv_r);
         }
     }
 
     if constexpr (kI8Prefetch) {
+        publish();
         // Two register sets take turns: the step after the one computed is
         // always in flight.  Past the last step the prefetch repeats the
         // last step's loads (never used), keeping the loads unconditional.
@@ -510,10 +566,13 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
         StepRegs<D, D / GS> A;
         int ts = t_begin;
         for (; ts + kI8Step <= t_end; ts += kI8Step) {
+            if (ts + kI8Step == t_end)
+                publish();  // the last step holds position L - 1
             load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
             compute_step<D, BS, GS, true>(A, st, qf, qmul, ts, t_end, lane);
         }
         if (ts < t_end) {
+            publish();
             load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
             compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
         }

@@ -162,6 +162,10 @@ struct Int8DecodeArgs {
     float *ws_ml;             // [B][Hq][num_partitions][2]: max (log2 units), sum
     int2 *items;              // [B * num_partitions] planned (b, partition)
     int32_t *wl_header;       // [0]: item count
+    // fused append (k_new null: plain decode): rows [B][Hkv][D] of q_dtype
+    const void *k_new = nullptr, *v_new = nullptr;
+    int64_t k_new_stride = 0, v_new_stride = 0;  // elements
+    const int64_t *slot_mapping = nullptr;
 };
 
 // Byte offsets of the INT8 decode workspace (zero total for one partition).

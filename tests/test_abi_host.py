@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strings():
     lib = pka.load_library()
-    assert lib.pka_abi_version() == 5
+    assert lib.pka_abi_version() == 6
     assert lib.pka_status_string(0) == b"ok"
     assert lib.pka_status_string(3) == b"workspace too small"
     assert lib.pka_status_string(99) == b"unknown status"
@@ -342,3 +342,18 @@ def test_int8_workspace_and_partition_helpers():
     n = lib.pka_decode_int8_workspace_bytes(4, 32, 64, 1024, 256)
     # header + items + (max, sum) rows + output rows, each 256-aligned
     assert n == 256 + 256 + 4096 + 4 * 32 * 4 * 64 * 4
+
+
+@fake_pointers
+@pytest.mark.parametrize("over,status", [
+    (dict(kn=None), 1), (dict(sm=None), 1), (dict(ks=100), 1), (dict(kn=FAKE + 1), 1),
+    (dict(qdt=0), 2), (dict(gs=48), 2),
+])
+def test_decode_append_int8_rejects(over, status):
+    a = dict(kn=FAKE, vn=FAKE, ks=512, vs=512, sm=FAKE, qdt=1, gs=32)
+    a.update(over)
+    lib = pka.load_library()
+    st = lib.pka_paged_attention_decode_append_int8(
+        FAKE, 0, FAKE, a["qdt"], a["kn"], a["vn"], a["ks"], a["vs"], a["sm"], FAKE, FAKE, FAKE,
+        FAKE, FAKE, 64, FAKE, 4, 32, 8, 64, 100, 16, a["gs"], 0.125, 1024, 0, FAKE, 1 << 30, None)
+    assert st == status, (over, st, lib.pka_last_error())

@@ -266,3 +266,38 @@ def test_large_dynamic_range_of_scales():
     assert np.all(np.isfinite(got))
     rel = np.abs(got - ref) / (np.abs(ref).max(axis=2, keepdims=True) + 1e-300)
     assert float(rel.max()) <= 2e-3
+
+
+@pytest.mark.parametrize("P", [0, 32, 16])
+@pytest.mark.parametrize("q_dtype,D,gs", [("f16", 64, 32), ("bf16", 128, 64)])
+def test_fused_append_equals_write_then_decode(P, q_dtype, D, gs):
+    """The fused step (quantise and store the new token, then attend) leaves
+    the pools and the output bit-identical to the write followed by the
+    decode, in each launch mode; a negative slot stores nothing."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+
+    wl = W.make_int8_case(90 + D + P, q_dtype=q_dtype, context_lens=(3, 70, 129, 17, 0, 300),
+                          num_q_heads=4 * 2, num_kv_heads=2, head_dim=D, block_size=16,
+                          group_size=gs, poison=False)
+    wl.slot_mapping[3] = -1  # padding: nothing stored, position L - 1 read as it is
+    d1 = W.int8_device_inputs(wl)
+    d2 = W.int8_device_inputs(wl)
+    names = ("k_codes", "v_codes", "k_scales", "v_scales")
+    pka.kv_cache_write_int8(d1["new_k"], d1["new_v"], d1["slot_mapping"], *(d1[n] for n in names))
+    ref = pka.paged_attention_decode_int8(d1["q"], *(d1[n] for n in names), d1["block_tables"],
+                                          d1["context_lens"], float(wl.scale), 2, 16,
+                                          partition_size=P)
+    got = pka.paged_attention_decode_append_int8(
+        d2["q"], d2["new_k"], d2["new_v"], d2["slot_mapping"], *(d2[n] for n in names),
+        d2["block_tables"], d2["context_lens"], float(wl.scale), 2, 16, partition_size=P)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(d1[n], d2[n]), n
+    assert torch.equal(ref, got)
+    pools = [a.copy() for a in (wl.k_codes, wl.v_codes, wl.k_scales, wl.v_scales)]
+    oracle.kv_cache_write_int8(wl.new_k, wl.new_v, wl.slot_mapping, *pools, wl.dtype)
+    want = oracle.paged_attention_decode_int8(wl.q, wl.dtype, *pools, wl.block_tables,
+                                              wl.context_lens, wl.scale, 2, 16)
+    check(got.double().cpu().numpy(), want, "fused append")
