@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--group-size", type=int, default=64,
                     help="INT8 path: quantisation group (32, 64 or 128 dims)")
     ap.add_argument("--no-compare", action="store_true",
-                    help="INT8 path: skip timing the fp16/bf16 decode of the same shape")
+                    help="INT8 path: skip timing the fp16/bf16 decode of the same shape "
+                         "and the fused write + decode step")
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
                     help="workload (decode: 2 = Llama-3.2-1B batch 16, the headline; "
                          "prefill: 2 = chunked prefill, 3 = drafted-token check)")
@@ -804,20 +805,24 @@ def run_int8(args, dev):
     # the whole decode step in one call per layer: the new token of every
     # sequence quantised and stored at the slot of its position L - 1, then
     # the attention (pka_paged_attention_decode_append_int8)
-    new_k = W.as_torch(wl.new_k, wl.dtype, dev)
-    new_v = W.as_torch(wl.new_v, wl.dtype, dev)
-    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    # (skipped with --no-compare, so that a profile's decode-kernel average
+    # covers the plain decode launches alone)
+    us_fused = None
+    if not args.no_compare:
+        new_k = W.as_torch(wl.new_k, wl.dtype, dev)
+        new_v = W.as_torch(wl.new_v, wl.dtype, dev)
+        slots = torch.from_numpy(wl.slot_mapping).to(dev)
 
-    def fused_step():
-        for r in range(R):
-            kc, vc, ks, vs = pools[r]
-            pka.paged_attention_decode_append_int8(q, new_k, new_v, slots, kc, vc, ks, vs, bt, cl,
-                                                   float(wl.scale), Hkv, bs, out=outs[r],
-                                                   partition_size=P, max_context_len=L,
-                                                   workspace=ws)
+        def fused_step():
+            for r in range(R):
+                kc, vc, ks, vs = pools[r]
+                pka.paged_attention_decode_append_int8(q, new_k, new_v, slots, kc, vc, ks, vs, bt,
+                                                       cl, float(wl.scale), Hkv, bs, out=outs[r],
+                                                       partition_size=P, max_context_len=L,
+                                                       workspace=ws)
 
-    us_fused = timed_calls(fused_step, args.steps, args.warmup, use_graph) * 1e3 / R
-    log(f"INT8 fused write + decode step {us_fused:.2f} us per layer")
+        us_fused = timed_calls(fused_step, args.steps, args.warmup, use_graph) * 1e3 / R
+        log(f"INT8 fused write + decode step {us_fused:.2f} us per layer")
     wl8 = W.Int8Workload(**{f: getattr(wl, f) for f in W.Workload.__dataclass_fields__},
                          group_size=gs)
     kv_bytes = wl8.kv_bytes()
@@ -927,7 +932,7 @@ def run_int8(args, dev):
             "parallelism": "single GPU",
         },
         "us_per_layer": round(us_layer, 3),
-        "us_per_layer_fused_step": round(us_fused, 3),
+        "us_per_layer_fused_step": None if us_fused is None else round(us_fused, 3),
         "quantising_write": wr,
         "half_kv_decode_same_shape": half,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

@@ -446,8 +446,9 @@ __device__ __forceinline__ int clamped_len(const Int8DecodeArgs &a, int b)
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// Tokens [jp * P, min((jp+1) * P, L)) of sequence b, kv head h.
-template <class QT, int D, int BS, int G, int GS>
+// Tokens [jp * P, min((jp+1) * P, L)) of sequence b, kv head h; APPEND:
+// the new token's row is stored first (a plain decode compiles without it).
+template <class QT, int D, int BS, int G, int GS, bool APPEND>
 __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp, int h, int L,
                                          int lane)
 {
@@ -459,7 +460,7 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
     // first; it reads them back with the last step (after a fence there),
     // exactly as a decode after the write would.  Its V-scale pass takes
     // the new scales from the registers.
-    const bool appending = a.k_new != nullptr && jp == (L - 1) / P;
+    const bool appending = APPEND && jp == (L - 1) / P;
     bool stored = false;
     float new_vs = 0.0f;  // this lane's group's scale of the new V row
     if (appending) {
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(kI8PlanThreads) void int8_plan_kernel(Int8DecodeArg
 // round-robin to all waves of the grid; MODE 1 reads them from the list a
 // planning launch wrote, MODE 2 (at most kI8PlanInKernelSeqs sequences)
 // finds them in a prefix of partition counts each workgroup builds in LDS.
-template <class QT, int D, int BS, int G, int GS, int MODE>
+template <class QT, int D, int BS, int G, int GS, int MODE, bool APPEND>
 __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8DecodeArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
         }
         if (jp * a.partition_size >= L)
             return;
-        run_unit<QT, D, BS, G, GS>(a, b, jp, h, L, lane);
+        run_unit<QT, D, BS, G, GS, APPEND>(a, b, jp, h, L, lane);
     } else if constexpr (MODE == 1) {
         const int64_t units = (int64_t)__builtin_amdgcn_readfirstlane(a.wl_header[0]) *
                               a.num_kv_heads;
@@ -724,7 +725,7 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
             const int b = __builtin_amdgcn_readfirstlane(it.x);
             const int jp = __builtin_amdgcn_readfirstlane(it.y);
             const int h = (int)(u % a.num_kv_heads);
-            run_unit<QT, D, BS, G, GS>(a, b, jp, h, clamped_len(a, b), lane);
+            run_unit<QT, D, BS, G, GS, APPEND>(a, b, jp, h, clamped_len(a, b), lane);
         }
     } else {
         extern __shared__ int i8_lds[];
@@ -746,7 +747,7 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
             const int b = __builtin_amdgcn_readfirstlane(lo);
             const int jp = __builtin_amdgcn_readfirstlane(item - prefix[lo]);
             const int h = (int)(u % a.num_kv_heads);
-            run_unit<QT, D, BS, G, GS>(a, b, jp, h, clamped_len(a, b), lane);
+            run_unit<QT, D, BS, G, GS, APPEND>(a, b, jp, h, clamped_len(a, b), lane);
         }
     }
 }
@@ -857,20 +858,20 @@ int compute_units()
     return cached[dev];
 }
 
-template <class QT, int D, int BS, int G, int GS>
+template <class QT, int D, int BS, int G, int GS, bool APPEND>
 hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
 {
     if (a.num_partitions <= kI8DenseMaxPartitions) {
         const int64_t waves = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
         const int64_t grid = (waves + kI8Waves - 1) / kI8Waves;
-        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 0>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 0, APPEND>), dim3((unsigned)grid),
                            dim3(kI8Waves * kWave), 0, stream, a);
     } else {
         const bool in_kernel = a.num_seqs <= kI8PlanInKernelSeqs;
         const size_t lds = in_kernel ? (size_t)(kI8Waves + a.num_seqs + 1) * 4 : 0;
         if (!in_kernel)
             hipLaunchKernelGGL(int8_plan_kernel, dim3(1), dim3(kI8PlanThreads), 0, stream, a);
-        static int per_cu_cache[64][2];
+        static int per_cu_cache[64][2];  // per device and plan kind, per instantiation
         int dev = 0;
         (void)hipGetDevice(&dev);
         const int kind = in_kernel ? 1 : 0;
@@ -880,11 +881,11 @@ hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
             // the cached figure, so it holds for every smaller batch
             if (in_kernel)
                 (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, int8_decode_kernel<QT, D, BS, G, GS, 2>, kI8Waves * kWave,
+                    &per_cu, int8_decode_kernel<QT, D, BS, G, GS, 2, APPEND>, kI8Waves * kWave,
                     (size_t)(kI8Waves + kI8PlanInKernelSeqs + 1) * 4);
             else
                 (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, int8_decode_kernel<QT, D, BS, G, GS, 1>, kI8Waves * kWave, 0);
+                    &per_cu, int8_decode_kernel<QT, D, BS, G, GS, 1, APPEND>, kI8Waves * kWave, 0);
             per_cu = per_cu > 0 ? per_cu : 1;
             if (dev >= 0 && dev < 64)
                 per_cu_cache[dev][kind] = per_cu;
@@ -894,10 +895,10 @@ hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
         const int64_t need = (max_units + kI8Waves - 1) / kI8Waves;
         grid = grid < need ? grid : need;
         if (in_kernel)
-            hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 2>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 2, APPEND>), dim3((unsigned)grid),
                                dim3(kI8Waves * kWave), lds, stream, a);
         else
-            hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 1>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 1, APPEND>), dim3((unsigned)grid),
                                dim3(kI8Waves * kWave), 0, stream, a);
     }
     if (a.num_partitions > 1) {
@@ -912,11 +913,16 @@ template <class QT, int D, int BS, int G>
 hipError_t dispatch_gs(const Int8DecodeArgs &a, hipStream_t s)
 {
     switch (a.group_size) {
-    case 32: return launch_decode_t<QT, D, BS, G, 32>(a, s);
-    case 64: return launch_decode_t<QT, D, BS, G, 64>(a, s);
+    case 32:
+        return a.k_new ? launch_decode_t<QT, D, BS, G, 32, true>(a, s)
+                       : launch_decode_t<QT, D, BS, G, 32, false>(a, s);
+    case 64:
+        return a.k_new ? launch_decode_t<QT, D, BS, G, 64, true>(a, s)
+                       : launch_decode_t<QT, D, BS, G, 64, false>(a, s);
     case 128:
         if constexpr (D >= 128)
-            return launch_decode_t<QT, D, BS, G, 128>(a, s);
+            return a.k_new ? launch_decode_t<QT, D, BS, G, 128, true>(a, s)
+                           : launch_decode_t<QT, D, BS, G, 128, false>(a, s);
         break;
     }
     return hipErrorInvalidValue;
