@@ -939,9 +939,11 @@ def run_int8(args, dev):
         "roofline": {
             "bound": "hbm",
             "kernel": ("int8_decode_kernel (one launch per layer)" if nparts == 1 else
-                       "int8_decode_kernel + int8_merge_kernel (per layer)" if nparts <= 8 or B <= 4096
+                       "int8_decode_kernel, partitions merged in the workgroup (one launch per layer)"
+                       if nparts <= 8 else
+                       "int8_decode_kernel + int8_merge_kernel (per layer)" if B <= 4096
                        else "int8_plan_kernel + int8_decode_kernel + int8_merge_kernel (per layer)"),
-            "launches_per_layer": 1 if nparts == 1 else (2 if nparts <= 8 or B <= 4096 else 3),
+            "launches_per_layer": 1 if nparts <= 8 else (2 if B <= 4096 else 3),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

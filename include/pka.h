@@ -424,11 +424,12 @@ size_t pka_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  * a power of two per head so that they are exact in fp16 too; the
  * probabilities times the V scales enter the second product rounded to fp16).
  * L_b <= 0 yields a zero row.  Long sequences are cut into partitions that
- * separate waves process; with more than one, a merge launch on `stream`
- * combines them exactly (log-sum-exp).  Past 8 partitions per sequence a
+ * separate waves process, and their rows are combined exactly (log-sum-exp):
+ * up to 8 partitions per sequence, the waves of one workgroup per (sequence,
+ * kv head) take one partition each and merge in that workgroup; past 8 a
  * persistent grid takes the (sequence, partition) items, planned in each
  * workgroup's LDS up to 4096 sequences and by a one-workgroup planning
- * launch beyond.
+ * launch beyond, and a merge launch on `stream` combines the rows.
  *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (F32,
  *                 or q_dtype rounded to nearest even), 16-byte aligned.
  *   q             device [num_seqs][num_q_heads][head_dim] of q_dtype (F16 or

@@ -77,6 +77,13 @@ constexpr int kI8PlanThreads = 1024;    // planning workgroup
 // Up to this many partitions per sequence the decode launches one wave per
 // (sequence, partition, kv head) and no planning launch.
 constexpr int kI8DenseMaxPartitions = 8;
+#ifndef PKA_I8_GROUP_MERGE
+#define PKA_I8_GROUP_MERGE 1
+#endif
+// With 2..kI8DenseMaxPartitions partitions, one workgroup per (sequence, kv
+// head) whose wave w takes partition w merges the partitions' rows in LDS
+// (no merge launch, no partial rows in HBM).
+constexpr bool kI8GroupMerge = PKA_I8_GROUP_MERGE != 0;
 // Persistent grids over at most this many sequences plan their work in each
 // workgroup's LDS (a prefix of partition counts) instead of a planning launch.
 constexpr int kI8PlanInKernelSeqs = 4096;
@@ -448,9 +455,12 @@ __device__ __forceinline__ int clamped_len(const Int8DecodeArgs &a, int b)
 
 // Tokens [jp * P, min((jp+1) * P, L)) of sequence b, kv head h; APPEND:
 // the new token's row is stored first (a plain decode compiles without it).
+// A partial result (L > P) goes to the workspace rows, or with lds_o set to
+// LDS: o / l at lds_o[n * D + d] and (max, sum) at lds_ml[n] for head n < G.
 template <class QT, int D, int BS, int G, int GS, bool APPEND>
 __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp, int h, int L,
-                                         int lane)
+                                         int lane, float *lds_o = nullptr,
+                                         float2 *lds_ml = nullptr)
 {
     const int P = a.partition_size;
     const int t_begin = jp * P;
@@ -594,7 +604,16 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
             st.o[m][i] *= u;
     }
     const float inv_l = 1.0f / l;
-    if (a.num_partitions == 1 || L <= P) {
+    if (lds_o != nullptr && L > P) {
+        float *o = lds_o + n * D + 4 * j;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m)
+            *reinterpret_cast<float4 *>(o + 16 * m) =
+                make_float4(st.o[m][0] * inv_l, st.o[m][1] * inv_l, st.o[m][2] * inv_l,
+                            st.o[m][3] * inv_l);
+        if (j == 0)
+            lds_ml[n] = make_float2(st.m, l);
+    } else if (a.num_partitions == 1 || L <= P) {
         const int64_t base = ((int64_t)b * a.num_q_heads + hq) * D + 4 * j;
 #pragma unroll
         for (int m = 0; m < D / 16; ++m)
@@ -694,8 +713,12 @@ __global__ __launch_bounds__(kI8PlanThreads) void int8_plan_kernel(Int8DecodeArg
 // round-robin to all waves of the grid; MODE 1 reads them from the list a
 // planning launch wrote, MODE 2 (at most kI8PlanInKernelSeqs sequences)
 // finds them in a prefix of partition counts each workgroup builds in LDS.
+// MODE 3 (2..kI8DenseMaxPartitions partitions): workgroup (b, h) of
+// num_partitions waves, wave w on partition w; the workgroup merges the
+// partitions' rows in LDS with the exact log-sum-exp weights.
 template <class QT, int D, int BS, int G, int GS, int MODE, bool APPEND>
-__global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8DecodeArgs a)
+__global__ __launch_bounds__(MODE == 3 ? kI8DenseMaxPartitions * kWave : kI8Waves * kWave)
+void int8_decode_kernel(Int8DecodeArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -716,6 +739,42 @@ __global__ __launch_bounds__(kI8Waves *kWave) void int8_decode_kernel(Int8Decode
         if (jp * a.partition_size >= L)
             return;
         run_unit<QT, D, BS, G, GS, APPEND>(a, b, jp, h, L, lane);
+    } else if constexpr (MODE == 3) {
+        extern __shared__ int i8_lds[];
+        const int nw = a.num_partitions;  // waves of the workgroup
+        const int b = (int)(blockIdx.x / a.num_kv_heads);
+        const int h = (int)(blockIdx.x % a.num_kv_heads);
+        const int L = clamped_len(a, b);
+        if (L == 0) {  // the whole workgroup leaves
+            if (wave == 0)
+                store_zero_rows(a, b, h, G, D, lane);
+            return;
+        }
+        float *lo = reinterpret_cast<float *>(i8_lds);               // [nw][G][D]
+        float2 *lml = reinterpret_cast<float2 *>(lo + nw * G * D);  // [nw][G]
+        const int P = a.partition_size;
+        if (wave * P < L)
+            run_unit<QT, D, BS, G, GS, APPEND>(a, b, wave, h, L, lane, lo + wave * G * D,
+                                               lml + wave * G);
+        const int np = (L + P - 1) / P;
+        if (np <= 1)  // written by wave 0; the same for every wave
+            return;
+        __syncthreads();
+        for (int e = threadIdx.x; e < G * D; e += nw * kWave) {
+            const int n = e / D, d = e % D;
+            float M = -INFINITY;
+            for (int w = 0; w < np; ++w)
+                M = fmaxf(M, lml[w * G + n].x);
+            float acc = 0.0f, den = 0.0f;
+            for (int w = 0; w < np; ++w) {
+                const float2 ml = lml[w * G + n];
+                const float wk = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+                acc = fmaf(wk, lo[(w * G + n) * D + d], acc);
+                den += wk;
+            }
+            store_out(a.out, ((int64_t)b * a.num_q_heads + h * G + n) * D + d,
+                      acc * (1.0f / den), a.out_kind);
+        }
     } else if constexpr (MODE == 1) {
         const int64_t units = (int64_t)__builtin_amdgcn_readfirstlane(a.wl_header[0]) *
                               a.num_kv_heads;
@@ -861,6 +920,15 @@ int compute_units()
 template <class QT, int D, int BS, int G, int GS, bool APPEND>
 hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
 {
+    if (kI8GroupMerge && a.num_partitions > 1 && a.num_partitions <= kI8DenseMaxPartitions) {
+        const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads;
+        if (groups > 0x7fffffff)
+            return hipErrorInvalidValue;
+        const size_t lds = (size_t)a.num_partitions * G * (D * 4 + 8);
+        hipLaunchKernelGGL((int8_decode_kernel<QT, D, BS, G, GS, 3, APPEND>),
+                           dim3((unsigned)groups), dim3(a.num_partitions * kWave), lds, stream, a);
+        return hipGetLastError();  // merged in the launch
+    }
     if (a.num_partitions <= kI8DenseMaxPartitions) {
         const int64_t waves = (int64_t)a.num_seqs * a.num_partitions * a.num_kv_heads;
         const int64_t grid = (waves + kI8Waves - 1) / kI8Waves;

@@ -132,7 +132,8 @@ SWEEP = [(qd, D, bs, G, gs) for qd in ("f16", "bf16") for D in (64, 128) for bs 
 def test_decode_sweep(q_dtype, D, bs, G, gs):
     """Ragged lengths (tails of every size, L = 1, an empty sequence): the
     library's partitions, one partition per sequence (a single launch),
-    64-token partitions (one wave per unit, then the merge launch) and
+    64-token partitions (one workgroup per (sequence, kv head), its waves'
+    partitions merged in LDS) and
     32-token partitions (10 for the longest: planned work list, persistent
     grid, merge)."""
     Hkv = 2
@@ -268,7 +269,7 @@ def test_large_dynamic_range_of_scales():
     assert float(rel.max()) <= 2e-3
 
 
-@pytest.mark.parametrize("P", [0, 32, 16])
+@pytest.mark.parametrize("P", [0, 320, 32, 16])
 @pytest.mark.parametrize("q_dtype,D,gs", [("f16", 64, 32), ("bf16", 128, 64)])
 def test_fused_append_equals_write_then_decode(P, q_dtype, D, gs):
     """The fused step (quantise and store the new token, then attend) leaves
