@@ -116,35 +116,48 @@ __device__ __forceinline__ float load_as_f32(TBF16, const void *p, int64_t i)
     return as_f((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
 }
 
-// Quantise one token's row of one kv head (D elements of type T at
-// src[src_row ..]) and store its codes and scales at (block blk, offset off)
-// of a pool: the group's amax is a max over the GS / E lanes holding it,
-// s = amax / 127 (IEEE division), codes rint(x / s).  Lane l handles dims
-// [l*E, l*E + E), E = D / 64; it returns the scale of its group.
-template <class T, int D, int GS>
-__device__ __forceinline__ float quantize_store_row(const void *src, int64_t src_row, bool is_value,
-                                                   int8_t *codes_pool, float *scales_pool,
-                                                   int num_kv_heads, int block_size, int64_t blk,
-                                                   int h, int off, int lane)
+// One token's row of one kv head, quantised by one wave: lane l holds dims
+// [l*E, l*E + E), E = D / 64.  load_row reads the D elements of type T at
+// src[src_row ..]; quantise_row takes the group's amax over the GS / E
+// lanes holding it, s = amax / 127 (IEEE division), codes rint(x / s), and
+// returns the lane's group scale; store_row stores codes and scale at
+// (block blk, offset off) of a pool in its layout.
+template <class T, int D>
+__device__ __forceinline__ void load_row(const void *src, int64_t src_row, int lane,
+                                         float (&x)[D / kWave])
+{
+#pragma unroll
+    for (int e = 0; e < D / kWave; ++e)
+        x[e] = load_as_f32(T{}, src, src_row + lane * (D / kWave) + e);
+}
+
+template <int D, int GS>
+__device__ __forceinline__ float quantise_row(const float (&x)[D / kWave], int8_t (&c)[D / kWave])
 {
     constexpr int E = D / kWave;
-    constexpr int NG = D / GS;
-    float x[E];
     float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        x[e] = load_as_f32(T{}, src, src_row + lane * E + e);
+    for (int e = 0; e < E; ++e)
         amax = fmaxf(amax, fabsf(x[e]));
-    }
     amax = lanes_max<GS / E>(amax);
     const float s = amax / 127.0f;  // IEEE division (correctly rounded)
-    int8_t c[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         float q = s > 0.0f ? rintf(x[e] / s) : 0.0f;
         q = fminf(fmaxf(q, -127.0f), 127.0f);
         c[e] = (int8_t)q;
     }
+    return s;
+}
+
+template <int D, int GS>
+__device__ __forceinline__ void store_row(const int8_t (&c)[D / kWave], float s, bool is_value,
+                                          int8_t *codes_pool, float *scales_pool,
+                                          int num_kv_heads, int block_size, int64_t blk, int h,
+                                          int off, int lane)
+{
+    constexpr int E = D / kWave;
+    constexpr int NG = D / GS;
     const int64_t run = blk * num_kv_heads + h;  // this block's run of codes
     int8_t *codes = codes_pool + run * block_size * D;
     const int tl = off / 16, row = off % 16;
@@ -158,7 +171,31 @@ __device__ __forceinline__ float quantize_store_row(const void *src, int64_t src
     }
     if ((lane * E) % GS == 0)
         scales_pool[(run * block_size + off) * NG + lane * E / GS] = s;
-    return s;  // the scale of the lane's group
+}
+
+// The lane's codes in one dword (byte e: dim l*E + e).
+template <int E>
+__device__ __forceinline__ uint32_t pack_codes(const int8_t (&c)[E])
+{
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        w |= (uint32_t)(uint8_t)c[e] << (8 * e);
+    return w;
+}
+
+template <class T, int D, int GS>
+__device__ __forceinline__ void quantize_store_row(const void *src, int64_t src_row, bool is_value,
+                                                   int8_t *codes_pool, float *scales_pool,
+                                                   int num_kv_heads, int block_size, int64_t blk,
+                                                   int h, int off, int lane)
+{
+    float x[D / kWave];
+    int8_t c[D / kWave];
+    load_row<T, D>(src, src_row, lane, x);
+    const float s = quantise_row<D, GS>(x, c);
+    store_row<D, GS>(c, s, is_value, codes_pool, scales_pool, num_kv_heads, block_size, blk, h,
+                     off, lane);
 }
 
 // One wave per (new token, kv head, tensor).
@@ -287,6 +324,30 @@ __device__ __forceinline__ uint32_t u4(const uint4 &v, int i)
 __device__ __forceinline__ float f4(const float4 &v, int i)
 {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ void set_u4(uint4 &v, int i, uint32_t x)
+{
+    if (i == 0)
+        v.x = x;
+    else if (i == 1)
+        v.y = x;
+    else if (i == 2)
+        v.z = x;
+    else
+        v.w = x;
+}
+
+__device__ __forceinline__ void set_f4(float4 &v, int i, float x)
+{
+    if (i == 0)
+        v.x = x;
+    else if (i == 1)
+        v.y = x;
+    else if (i == 2)
+        v.z = x;
+    else
+        v.w = x;
 }
 
 // Scale of token 4j+i of a tile, group g, from the [token][group] rows a
@@ -453,8 +514,75 @@ __device__ __forceinline__ int clamped_len(const Int8DecodeArgs &a, int b)
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// Put a token's codes and scales, as quantise_store_row produced them
+// (k_pk / v_pk: each lane's packed codes, k_s / v_s: its group's scales),
+// into a loaded step's registers at step position rel, where the loads may
+// have found the pool before or after that row's store.  The layouts are
+// the operand orders of load_step: K byte 8s + i of lane 16p + row holds
+// dim 32s + 8p + i; V byte 4m + row % 4 of lane 16 (row / 4) + c holds dim
+// c + 16m; scales of tokens 4j..4j+3 sit in the lanes 16j..16j+15.
+template <int D, int GS>
+__device__ __forceinline__ void patch_new_token(StepRegs<D, D / GS> &R, int rel, uint32_t k_pk,
+                                                uint32_t v_pk, float k_s, float v_s, int lane)
+{
+    constexpr int E = D / kWave;
+    constexpr int NG = D / GS;
+    const int tile_of = rel / 16, row = rel % 16;
+    // dword of dims 4c..4c+3 in the lane holding dim 4c
+    uint32_t w;
+    if constexpr (E == 1)
+        w = k_pk | (__shfl_down(k_pk, 1) << 8) | (__shfl_down(k_pk, 2) << 16) |
+            (__shfl_down(k_pk, 3) << 24);
+    else
+        w = k_pk | (__shfl_down(k_pk, 2 / E) << 16);
+    const bool k_lane = (lane & 15) == row;
+    const bool q_lane = (lane >> 4) == row / 4;  // V codes and the scales
+    const int p = lane >> 4, c = lane & 15, sh = 8 * (row % 4);
+    uint32_t kd[D / 16], vd[D / 16];  // the lane's new dwords, in load order
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            kd[2 * s + hh] = __shfl(w, (32 * s + 8 * p + 4 * hh) / E);
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m)
+        vd[m] = (__shfl(v_pk, (c + 16 * m) / E) >> (8 * (c % E))) & 0xffu;
+    float ksn[NG], vsn[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        ksn[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k_s),
+                                                                      g * GS / E));
+        vsn[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v_s),
+                                                                      g * GS / E));
+    }
+#pragma unroll
+    for (int t = 0; t < kI8Tiles; ++t) {
+        if (t != tile_of)
+            continue;
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t kv = u4(R.k[t][q], e), vv = u4(R.v[t][q], e);
+                set_u4(R.k[t][q], e, k_lane ? kd[4 * q + e] : kv);
+                set_u4(R.v[t][q], e,
+                       q_lane ? ((vv & ~(0xffu << sh)) | (vd[4 * q + e] << sh)) : vv);
+            }
+#pragma unroll
+        for (int f = 0; f < NG; ++f)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int flat = 4 * f + e;  // token flat / NG of the quad, group flat % NG
+                const bool hit = q_lane && flat / NG == row % 4;
+                set_f4(R.ks[t][f], e, hit ? ksn[flat % NG] : f4(R.ks[t][f], e));
+                set_f4(R.vs[t][f], e, hit ? vsn[flat % NG] : f4(R.vs[t][f], e));
+            }
+    }
+}
+
 // Tokens [jp * P, min((jp+1) * P, L)) of sequence b, kv head h; APPEND:
-// the new token's row is stored first (a plain decode compiles without it).
+// the new token's row is quantised and stored (a plain decode compiles
+// without it).
 // A partial result (L > P) goes to the workspace rows, or with lds_o set to
 // LDS: o / l at lds_o[n * D + d] and (max, sum) at lds_ml[n] for head n < G.
 template <class QT, int D, int BS, int G, int GS, bool APPEND>
@@ -466,38 +594,23 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
     const int t_begin = jp * P;
     const int t_end = min(t_begin + P, L);
     // Fused append: the unit that holds position L - 1 quantises the
-    // sequence's new K/V rows of this kv head and stores them at their slot
-    // first; it reads them back with the last step (after a fence there),
-    // exactly as a decode after the write would.  Its V-scale pass takes
-    // the new scales from the registers.
+    // sequence's new K/V rows of this kv head and stores them at their slot.
+    // Its V-scale pass and its last step take the new codes and scales from
+    // the registers, the values a decode after the write would read, so
+    // nothing waits for the stores.  The rows are loaded together with the
+    // unit's other first loads.
+    constexpr int E = D / kWave;
     const bool appending = APPEND && jp == (L - 1) / P;
-    bool stored = false;
-    float new_vs = 0.0f;  // this lane's group's scale of the new V row
+    int64_t slot = -1;
+    float xk[E], xv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        xk[e] = xv[e] = 0.0f;
     if (appending) {
-        const int64_t slot = a.slot_mapping[b];
-        if (slot >= 0 && slot < (int64_t)a.num_blocks * BS) {
-            const int64_t blk = slot / BS;
-            const int off = (int)(slot % BS);
-            quantize_store_row<QT, D, GS>(a.k_new, (int64_t)b * a.k_new_stride + (int64_t)h * D,
-                                          false, const_cast<int8_t *>(a.k_codes),
-                                          const_cast<float *>(a.k_scales), a.num_kv_heads, BS,
-                                          blk, h, off, lane);
-            new_vs = quantize_store_row<QT, D, GS>(
-                a.v_new, (int64_t)b * a.v_new_stride + (int64_t)h * D, true,
-                const_cast<int8_t *>(a.v_codes), const_cast<float *>(a.v_scales), a.num_kv_heads,
-                BS, blk, h, off, lane);
-            stored = true;
-        }
+        slot = a.slot_mapping[b];
+        load_row<QT, D>(a.k_new, (int64_t)b * a.k_new_stride + (int64_t)h * D, lane, xk);
+        load_row<QT, D>(a.v_new, (int64_t)b * a.v_new_stride + (int64_t)h * D, lane, xv);
     }
-    // before the first read of the stored rows: the stores complete, and no
-    // stale line of them stays in this compute unit's L1
-    auto publish = [&]() __attribute__((always_inline)) {
-        if (stored) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            stored = false;
-        }
-    };
     // the partition's block ids, one per lane (clamped into the table row
     // and into the pool, so every access stays in bounds)
     const int nb = (t_end - t_begin + BS - 1) / BS;
@@ -514,6 +627,13 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
         st.o[m] = float4_t{0.f, 0.f, 0.f, 0.f};
     st.m = -INFINITY;
     st.l = 0.0f;
+    const bool stored = appending && slot >= 0 && slot < (int64_t)a.num_blocks * BS;
+    int8_t ck[E], cv[E];
+    float new_ks = 0.0f, new_vs = 0.0f;  // this lane's group's scales of the new rows
+    if (stored) {
+        new_ks = quantise_row<D, GS>(xk, ck);
+        new_vs = quantise_row<D, GS>(xv, cv);
+    }
     // The unit's V-scale normalisers: lane l reads the scales of the
     // partition's block l (tokens past t_end masked), a wave max per group.
     {
@@ -549,9 +669,25 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
             pow2_normaliser(m, st.r[g], inv_r);
         }
     }
+    uint32_t new_kc = 0, new_vc = 0;  // this lane's codes of the new rows
+    if (stored) {
+        const int64_t blk = slot / BS;
+        const int off = (int)(slot % BS);
+        store_row<D, GS>(ck, new_ks, false, const_cast<int8_t *>(a.k_codes),
+                         const_cast<float *>(a.k_scales), a.num_kv_heads, BS, blk, h, off, lane);
+        store_row<D, GS>(cv, new_vs, true, const_cast<int8_t *>(a.v_codes),
+                         const_cast<float *>(a.v_scales), a.num_kv_heads, BS, blk, h, off, lane);
+        new_kc = pack_codes<E>(ck);
+        new_vc = pack_codes<E>(cv);
+    }
 
+    // the step starting at ts holds position L - 1: its registers get the
+    // new token
+    auto patch = [&](StepRegs<D, D / GS> &R, int ts) __attribute__((always_inline)) {
+        if (stored && ts <= L - 1 && L - 1 < ts + kI8Step)
+            patch_new_token<D, GS>(R, L - 1 - ts, new_kc, new_vc, new_ks, new_vs, lane);
+    };
     if constexpr (kI8Prefetch) {
-        publish();
         // Two register sets take turns: the step after the one computed is
         // always in flight.  Past the last step the prefetch repeats the
         // last step's loads (never used), keeping the loads unconditional.
@@ -561,11 +697,13 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
         int ts = t_begin;
         for (;;) {
             load_step<D, BS, GS>(a, B, ids, t_begin, min(ts + kI8Step, t_last), t_end, h, lane);
+            patch(A, ts);
             compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
             ts += kI8Step;
             if (ts > t_last)
                 break;
             load_step<D, BS, GS>(a, A, ids, t_begin, min(ts + kI8Step, t_last), t_end, h, lane);
+            patch(B, ts);
             compute_step<D, BS, GS, false>(B, st, qf, qmul, ts, t_end, lane);
             ts += kI8Step;
             if (ts > t_last)
@@ -577,14 +715,13 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
         StepRegs<D, D / GS> A;
         int ts = t_begin;
         for (; ts + kI8Step <= t_end; ts += kI8Step) {
-            if (ts + kI8Step == t_end)
-                publish();  // the last step holds position L - 1
             load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
+            patch(A, ts);
             compute_step<D, BS, GS, true>(A, st, qf, qmul, ts, t_end, lane);
         }
         if (ts < t_end) {
-            publish();
             load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
+            patch(A, ts);
             compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
         }
     }
