@@ -40,16 +40,18 @@
 //    that keeps s_v * r_g in [0, 2) for fp16; O is divided by r_g (exactly)
 //    at the end.  The softmax reference max is lazy (p <= 2^8), so the MFMAs
 //    accumulate straight into O and a rescale is rare.
-//  * One partition per sequence: the wave writes the output.  Several: it
-//    writes (max, sum, O / sum) rows, and a merge launch combines them.  Up
-//    to 8 partitions per sequence the grid has one wave per (sequence,
-//    partition, kv head); beyond, a persistent grid deals the (sequence,
-//    partition) items, found in a prefix each workgroup builds in LDS (up to
-//    4096 sequences) or listed by a one-workgroup planning launch.
+//  * One partition per sequence: the wave writes the output.  2 to 8: one
+//    workgroup per (sequence, kv head), wave w on partition w, and the
+//    workgroup merges the waves' (max, sum, O / sum) rows in LDS.  More: a
+//    persistent grid deals the (sequence, partition) items, found in a
+//    prefix each workgroup builds in LDS (up to 4096 sequences) or listed by
+//    a one-workgroup planning launch; the units write their rows to the
+//    workspace and a merge launch combines them.
 //  * Fused append (pka_paged_attention_decode_append_int8): the unit that
-//    holds position L_b - 1 quantises and stores the new K/V rows of its kv
-//    head before it reads anything, so the result is that of the write
-//    followed by the decode.
+//    holds position L_b - 1 quantises the new K/V rows of its kv head,
+//    stores them, and takes their codes and scales from its registers where
+//    it would read them back, so the result is that of the write followed
+//    by the decode and nothing waits for the stores.
 //  * Tokens past the unit's end are excluded by selects (scores to -inf,
 //    probabilities and scales to 0), so poisoned scales never reach O.
 #include <hip/hip_runtime.h>
