@@ -147,6 +147,20 @@ def test_decode_sweep(q_dtype, D, bs, G, gs):
     check(gpu_decode_int8(wl, partition_size=32), ref, "32-token partitions")
 
 
+@pytest.mark.parametrize("q_dtype,D,bs,G,gs", [("bf16", 128, 16, 8, 32), ("f16", 64, 32, 1, 64),
+                                                ("f16", 128, 32, 4, 128)])
+def test_workgroup_merge_boundaries(q_dtype, D, bs, G, gs):
+    """Partition counts from 1 to 8 (the largest workgroup of the in-LDS
+    merge), lengths on and just past partition boundaries, and the largest
+    LDS footprint (D = 128 with G = 8) among the shapes."""
+    P = 2 * bs
+    lens = (8 * P, 8 * P - 1, 7 * P + 1, P, P + 1, 1, 0, 3 * P)
+    Hkv = 2
+    wl = case(700 + D + bs + G + gs, q_dtype, lens, G * Hkv, Hkv, D, bs, gs)
+    print(f"[int8-wg-merge] {q_dtype} D={D} bs={bs} G={G} gs={gs} P={P}", flush=True)
+    check(gpu_decode_int8(wl, partition_size=P), oracle_int8(wl), f"P={P}")
+
+
 @pytest.mark.parametrize("cfg,gs", [(1, 32), (2, 32), (3, 32)])
 def test_named_workload_full(cfg, gs):
     """Workloads 1-3 with INT8 pools (q in the workload's dtype; workload 1
