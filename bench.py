@@ -110,8 +110,6 @@ def measured_traffic(tag, path_kind="decode"):
     return int(fields["traffic_bytes_per_launch"])
 
 
-DENSE_MAX_PARTITIONS = 8  # the library's switch to its persistent work-list grid
-
 PROFILE_TAGS = {2: "paged_decode_llama3_1b_b16", 3: "paged_decode_mix_b64",
                 4: "paged_decode_qwen3_b128", 5: "paged_decode_skewed_b256"}
 
@@ -184,7 +182,7 @@ def main():
             vcs.append(fill_pool(shape, tdt, 1001 + 2 * r, dev))
     P = args.partition_size or wl.partition_size or \
         pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
-    ws_bytes = pka.decode_workspace_bytes(B, Hq, D, wl.max_context_len, P)
+    ws_bytes = pka.decode_workspace_bytes(B, Hq, Hkv, D)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # counters start at 0
     outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
     torch.cuda.synchronize()
@@ -262,11 +260,7 @@ def main():
     nblk = int(np.sum((wl.context_lens.astype(np.int64) + bs - 1) // bs))
     new_rows = B * Hkv * D * wl.elt_bytes * 2
     alg_bytes = kv_bytes + B * Hq * D * (wl.elt_bytes + 4) + nblk * 4 + B * 4 + 2 * new_rows + 8 * B
-    # A layer is one decode launch, or (more than DENSE_MAX_PARTITIONS
-    # partitions per sequence: persistent grid) the decode launch plus a
-    # small launch that merges partitions; the per-layer time covers both.
-    nparts = -(-wl.max_context_len // P)
-    launches = 1 if nparts <= DENSE_MAX_PARTITIONS else 2
+    launches = 1  # one decode launch per layer (it combines its partial results itself)
     us_launch = us_per_layer
     achieved = alg_bytes / (us_launch * 1e-6) / 1e9
 
@@ -325,10 +319,7 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("partition_kernel (one launch per layer: new-token store + decode)"
-                       if launches == 1 else
-                       "partition_kernel + merge_kernel (per layer: new-token store + decode, "
-                       "then the partition merge)"),
+            "kernel": "decode_kernel (one launch per layer: new-token store + decode + merge)",
             "launches_per_layer": launches,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -868,7 +859,7 @@ def run_int8(args, dev):
         hp = [(fill_pool((NB, Hkv, bs, D), tdt, 8000 + 2 * r, dev),
                fill_pool((NB, Hkv, bs, D), tdt, 8001 + 2 * r, dev)) for r in range(Rh)]
         Ph = pka.decode_partition_size(B, Hkv, bs, L) if cfg != 5 else 512
-        wsh = torch.zeros(max(pka.decode_workspace_bytes(B, Hq, D, L, Ph), 256),
+        wsh = torch.zeros(max(pka.decode_workspace_bytes(B, Hq, Hkv, D), 256),
                           dtype=torch.uint8, device=dev)
         oh = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 6
+#define PKA_ABI_VERSION 7
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -135,21 +135,24 @@ pka_status pka_kv_cache_write_rope(const void *k, const void *v, int64_t k_token
                                    pka_dtype dtype, void *stream);
 
 /*
- * pka_decode_partition_size -- the partition length (tokens, a multiple of
- * block_size) pka_paged_attention_decode uses when its partition_size
- * argument is 0.  Pure host function of the shapes.
+ * pka_decode_partition_size -- the default of pka_paged_attention_decode's
+ * partition_size argument: the fewest tokens (summed over the (sequence, kv
+ * head) pairs it touches) that one wave of the decode takes.  Pure host
+ * function of the shapes.
  */
 int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                   int32_t max_context_len);
 
 /*
- * pka_decode_workspace_bytes -- bytes of device scratch the decode needs for
- * these shapes and this partition length (already resolved, > 0).  0 when
- * every sequence fits one partition (max_context_len <= partition_size);
- * then the workspace pointer may be NULL.
+ * pka_decode_workspace_bytes -- bytes of device scratch
+ * pka_paged_attention_decode (and _append) needs for these shapes on the
+ * current device: 1 MiB of report counters, then two partial-result slots
+ * of (num_q_heads / num_kv_heads) * (head_dim + 2) floats per wave of the
+ * decode grid.  It does not depend on the context lengths.  0 when
+ * num_seqs <= 0.
  */
-size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_context_len, int32_t partition_size);
+size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim);
 
 /*
  * pka_paged_attention_decode -- one query token per sequence attends over
@@ -162,15 +165,15 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * Softmax is computed stably (running max subtracted, fp32 throughout);
  * products and sums accumulate in fp32.  L_b <= 0 yields a zero row.
  *
- * Long sequences are split into partitions of partition_size tokens that
- * are processed independently; each writes its running max, sum and
- * normalised partial output to the workspace, and the last partition of a
- * (sequence, kv head) to finish merges them exactly (log-sum-exp) in the
- * same launch.  The result does not depend on the partition length beyond
- * fp32 rounding.  When the longest sequence spans more than 8 partitions,
- * a one-workgroup planning kernel first lists the (sequence, partition)
- * items on the device and a persistent grid processes them, so that short
- * sequences in a skewed batch launch no empty workgroups.
+ * How the work is split (split-context partitions): the tokens of all
+ * (sequence, kv head) pairs form one flat sequence of chunks, and every wave
+ * of the grid takes an equal contiguous share of it, so long sequences are
+ * cut into partitions wherever the shares end.  A wave that holds only part
+ * of a pair leaves its running max, sum and unnormalised output in the
+ * workspace; the last wave to finish with that pair combines the parts
+ * exactly (log-sum-exp) in the same launch.  The result does not depend on
+ * the split beyond fp32 rounding.  Batches of more than 2040 sequences run as
+ * several launches on `stream`.
  *
  *   out             device, [num_seqs][num_q_heads][head_dim], contiguous,
  *                   of out_dtype (PKA_F32, or the KV dtype: rounded to
@@ -179,32 +182,29 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                   of the KV dtype.
  *   k_cache,v_cache device pools (layout above), of kv_dtype.
  *   block_tables    device, int32 [num_seqs][max_blocks_per_seq].  Entries
- *                   at index >= ceil(L_b / block_size) may be read but are
- *                   never used; any value there is harmless.  A used entry
- *                   outside [0, num_blocks) is clamped into range (the row's
- *                   result is then meaningless, but no access leaves the
- *                   pools).
+ *                   at index >= ceil(L_b / block_size) are never used.  A
+ *                   used entry outside [0, num_blocks) is clamped into range
+ *                   (the row's result is then meaningless, but no access
+ *                   leaves the pools).
  *   context_lens    device, int32 [num_seqs].  Lengths are clamped on the
- *                   device to [0, min(max_blocks_per_seq * block_size,
- *                   max_context_len rounded up to whole partitions)].
+ *                   device to [0, max_blocks_per_seq * block_size].
  *   scale           multiplier of the dot products (typically 1/sqrt(D)).
- *   max_context_len host hint: no sequence is longer.  <= 0 means
- *                   max_blocks_per_seq * block_size.  It sizes the launch
- *                   without a device-to-host copy.
+ *   max_context_len accepted for interface compatibility and not used: the
+ *                   launch is sized from the device, so no hint can cut a
+ *                   sequence short.
  *   partition_size  0: pka_decode_partition_size(); else a positive
- *                   multiple of block_size.
+ *                   multiple of block_size: the fewest tokens one wave
+ *                   takes (fewer, longer shares leave fewer parts to
+ *                   combine).
  *   workspace       device scratch of workspace_bytes >=
- *                   pka_decode_workspace_bytes(...), 256-byte aligned; may
- *                   be NULL when that size is 0.  Its first 1 MiB holds
- *                   completion and scheduling counters (one int32 per
- *                   (sequence, kv head); num_seqs * num_kv_heads <= 262128)
- *                   that must be zero
- *                   before the first call using this workspace: zero-fill a
- *                   new workspace once.  Every call leaves the counters
- *                   zero again, so a workspace can be reused by later calls
- *                   of any shape on the same stream (or in a captured graph);
- *                   calls that share one workspace on different streams
- *                   race.  The rest is overwritten by each call.
+ *                   pka_decode_workspace_bytes(...), 256-byte aligned.  Its
+ *                   leading report counters must be zero before the first
+ *                   call using this workspace: zero-fill a new workspace
+ *                   once.  Every call leaves them zero again, so a workspace
+ *                   can be reused by later calls of any shape on the same
+ *                   stream (or in a captured graph); calls that share one
+ *                   workspace on different streams race.  The rest is
+ *                   overwritten by each call.
  * Supported: kv_dtype in {F32, F16, BF16}; head_dim in {64, 128};
  * block_size in {16, 32}; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  */

@@ -90,7 +90,7 @@ def load_library():
     lib.pka_kv_cache_write.restype = ctypes.c_int
     lib.pka_decode_partition_size.argtypes = [i32, i32, i32, i32]
     lib.pka_decode_partition_size.restype = i32
-    lib.pka_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pka_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.pka_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pka_paged_attention_decode.argtypes = [
         P, ctypes.c_int, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
@@ -210,10 +210,13 @@ def decode_partition_size(num_seqs: int, num_kv_heads: int, block_size: int,
                                                         max_context_len))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                           max_context_len: int, partition_size: int) -> int:
-    return int(load_library().pka_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                         max_context_len, partition_size))
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int) -> int:
+    """Bytes of scratch the decode needs on the current device (report
+    counters plus two partial-result slots per wave of the decode grid); it
+    does not depend on the context lengths."""
+    return int(load_library().pka_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                         head_dim))
 
 
 def _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, block_size,
@@ -250,18 +253,16 @@ def _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
             raise ValueError("out must be a contiguous [B, Hq, D] tensor on q's device")
     hint = max_context_len if max_context_len > 0 else MB * bs
     hint = min(hint, MB * bs)
-    P = 0
+    P = int(partition_size)  # 0: the library default; the C ABI rejects bad values
     ws_ptr, ws_bytes = None, 0
     if B > 0:
-        P = partition_size if partition_size > 0 else decode_partition_size(B, Hkv, bs, hint)
-        need = decode_workspace_bytes(B, Hq, D, hint, P)
-        if need > 0:
-            if workspace is None:
-                workspace = _cached_workspace(q.device, need)
-            elif workspace.numel() * workspace.element_size() < need:
-                raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
-                                 f"bytes, {need} needed")
-            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        need = decode_workspace_bytes(B, Hq, Hkv, D)
+        if workspace is None:
+            workspace = _cached_workspace(q.device, need)
+        elif workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {need} needed")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return dict(q=q, block_tables=block_tables, context_lens=context_lens, out=out, B=B, Hq=Hq,
                 Hkv=Hkv, D=D, NB=NB, bs=bs, MB=MB, hint=hint, P=P, ws_ptr=ws_ptr,
                 ws_bytes=ws_bytes)
@@ -515,18 +516,20 @@ _WORKSPACES = {}
 
 
 def _cached_workspace(device, nbytes: int):
-    """A zero-filled workspace per device, grown on demand.
+    """A zero-filled workspace per (device, current stream), grown on demand.
 
-    Its leading completion counters start at zero and every decode leaves
-    them zero, so the buffer is reusable by later calls; calls that run
-    concurrently on different streams must pass workspaces of their own.
+    Its leading report counters start at zero and every decode leaves them
+    zero, so the buffer is reusable by later calls on the same stream.  Each
+    stream gets its own buffer, so decodes issued on different streams never
+    share counters or partial results.
     """
     import torch
 
-    ws = _WORKSPACES.get(device)
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 2 << 20), dtype=torch.uint8, device=device)
-        _WORKSPACES[device] = ws
+        _WORKSPACES[key] = ws
     return ws
 
 

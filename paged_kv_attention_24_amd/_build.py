@@ -1,11 +1,10 @@
 """Build libpka.so (HIP kernels for gfx950 + the C ABI) in the package dir.
 
-    python -m paged_kv_attention_24_amd._build [-v] [--variant vector_alu]
+    python -m paged_kv_attention_24_amd._build [-v] [--only a.hip,b.cpp]
 
-``--variant vector_alu`` builds libpka_vector_alu.so instead: the same
-library with fp16/bf16 KV on the vector ALUs rather than the matrix cores,
-the build the matrix-core path is measured against (load it by setting
-PKA_LIBRARY=libpka_vector_alu.so before importing the package).
+``--only`` recompiles just the named sources and relinks with the objects
+already in _build/ (a quick rebuild after editing one file; ``build()``
+always compiles everything).
 
 Every HIP translation unit is compiled with packed FP32 instructions
 disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host
@@ -29,7 +28,7 @@ ARCH = "gfx950"
 SOURCES = ["paged_decode.hip", "paged_prefill.hip", "kv_cache_write.hip", "block_ops.hip",
            "paged_int8.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-VARIANTS = {"vector_alu": ["-DPKA_MATRIX_CORES=0"]}
+VARIANTS = {}
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -42,7 +41,8 @@ def _compile_cmd(src: str, obj: str, extra=()):
     return [HIPCC, *lang, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
 
 
-def build(verbose: bool = False, extra_flags=(), variant: str | None = None) -> str:
+def build(verbose: bool = False, extra_flags=(), variant: str | None = None,
+          only=None) -> str:
     build_dir, lib_path = BUILD_DIR, LIB_PATH
     if variant is not None:
         extra_flags = [*extra_flags, *VARIANTS[variant]]
@@ -54,6 +54,8 @@ def build(verbose: bool = False, extra_flags=(), variant: str | None = None) -> 
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
+        if only is not None and src not in only and os.path.exists(obj):
+            continue
         cmd = _compile_cmd(src, obj, extra_flags)
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -85,4 +87,5 @@ def clean():
 
 if __name__ == "__main__":
     var = sys.argv[sys.argv.index("--variant") + 1] if "--variant" in sys.argv else None
-    print(build(verbose="-v" in sys.argv, variant=var))
+    only = sys.argv[sys.argv.index("--only") + 1].split(",") if "--only" in sys.argv else None
+    print(build(verbose="-v" in sys.argv, variant=var, only=only))

@@ -38,30 +38,36 @@ pka::DType to_internal(pka_dtype d) { return static_cast<pka::DType>(static_cast
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int64_t kDefaultPartition = 512;
-constexpr int64_t kComputeUnits = 256;  // MI355X
-
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+constexpr int64_t kDefaultPartition = 512;
+
+// Compute units of the current device (256 on MI355X; fewer on a partitioned
+// GPU), so that host heuristics match what the kernels see.
+int64_t compute_units()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}
 
 }  // namespace
 
 pka::WorkspaceLayout pka::decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads,
-                                                  int64_t head_dim, int64_t num_partitions)
+                                                  int64_t num_kv_heads, int64_t head_dim,
+                                                  int64_t max_waves)
 {
-    WorkspaceLayout w{0, 0, 0, 0, 0, 0, false};
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_partitions <= 1)
+    WorkspaceLayout w{0, 0, 0};
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_waves <= 0)
         return w;
-    const int64_t rows = num_seqs * num_q_heads * num_partitions;
+    const int64_t group = num_q_heads / num_kv_heads;
+    // a fixed counter region, so that one workspace serves calls of any shape
     w.counter_offset = 0;
-    w.o_offset = (size_t)kCounterBytes;
-    w.ml_offset = w.o_offset + (size_t)round256(rows * head_dim * 4);
-    w.total = w.ml_offset + (size_t)round256(rows * 2 * 4);
-    if (num_partitions > kDenseMaxPartitions) {
-        w.worklist = true;
-        w.header_offset = w.total;
-        w.items_offset = w.header_offset + 256;
-        w.total = w.items_offset + (size_t)round256(num_seqs * num_partitions * 8);
-    }
+    w.parts_offset = (size_t)kCounterBytes;
+    w.total = w.parts_offset + (size_t)round256(2 * max_waves * decode_part_floats(group, head_dim) * 4);
     return w;
 }
 
@@ -177,37 +183,25 @@ pka_status pka_kv_cache_write_rope(const void *k, const void *v, int64_t k_token
 int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                   int32_t max_context_len)
 {
-    // 512 tokens unless that leaves fewer (sequence, kv head, partition)
-    // work items than compute units; then halve, down to 64 tokens.  Longer
-    // partitions amortise each work item's fixed cost (block-id fetch, the
-    // cross-wave merge, one partial row per query head); measured best for
-    // batches 16-256 on MI355X.
-    // When the (sequence, kv head) pairs alone fill at least half of the
-    // compute units and no sequence exceeds 1024 tokens, one partition per
-    // sequence: no partial rows and no merge (Llama-3.2-1B at batch 16:
-    // 9.6 us per layer against 9.9 with 512).
+    // The decode spreads the flat (sequence, kv head, chunk) space evenly
+    // over the GPU's waves; partition_size only sets how short a wave's
+    // range may get.  64 tokens by default: a shorter range spends more of
+    // its time on its first request and on the partial result it leaves.
+    (void)num_seqs;
+    (void)num_kv_heads;
+    (void)max_context_len;
     if (block_size <= 0)
         return 0;
-    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-    const int64_t lmax = max_context_len > 0 ? max_context_len : 1;
-    if (lmax > kDefaultPartition && lmax <= 2 * kDefaultPartition && 2 * pairs >= kComputeUnits &&
-        pairs <= kComputeUnits)
-        return (int32_t)(ceil_div(lmax, block_size) * block_size);
-    int64_t P = kDefaultPartition;
-    while (P > 64 && pairs * ceil_div(lmax, P) < kComputeUnits)
-        P /= 2;
-    if (P < block_size)
-        P = block_size;
-    return (int32_t)(ceil_div(P, block_size) * block_size);
+    return (int32_t)(ceil_div(pka::kDefaultRangeTokens, block_size) * block_size);
 }
 
-size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_context_len, int32_t partition_size)
+size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim)
 {
-    if (partition_size <= 0 || max_context_len <= partition_size)
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
         return 0;
-    return pka::decode_workspace_layout(num_seqs, num_q_heads, head_dim,
-                                        ceil_div(max_context_len, partition_size))
+    return pka::decode_workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        pka::decode_max_waves())
         .total;
 }
 
@@ -249,19 +243,17 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
         return fail(PKA_ERR_INVALID_ARGUMENT,
                     "partition_size %d must be 0 or a positive multiple of block_size %d",
                     partition_size, block_size);
-    if (partition_size > pka::kMaxPartition)
-        return fail(PKA_ERR_UNSUPPORTED, "partition_size %d exceeds %d", partition_size,
-                    pka::kMaxPartition);
+    (void)max_context_len;  // the launch is sized from the device, not from a hint
     if (num_seqs == 0)
         return ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
         return fail(PKA_ERR_INVALID_ARGUMENT, "null pointer argument");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKA_ERR_INVALID_ARGUMENT, "out, q and the caches must be 16-byte aligned");
+    const int elt = pka::dtype_bytes(to_internal(kv_dtype));
     if (k_new || v_new || slot_mapping) {
         if (!k_new || !v_new || !slot_mapping)
             return fail(PKA_ERR_INVALID_ARGUMENT, "null k_new, v_new or slot_mapping");
-        const int elt = pka::dtype_bytes(to_internal(kv_dtype));
         const int64_t row = (int64_t)num_kv_heads * head_dim;
         if (k_new_token_stride < row || v_new_token_stride < row)
             return fail(PKA_ERR_INVALID_ARGUMENT,
@@ -272,73 +264,69 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
             (v_new_token_stride * elt) % 16)
             return fail(PKA_ERR_INVALID_ARGUMENT, "k_new/v_new rows must be 16-byte aligned");
     }
+    // One launch plans its sequences in LDS and counts chunks of 16 tokens
+    // or more in int32: cut the batch into launches that respect both.
     const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
-    int64_t lmax = max_context_len > 0 ? max_context_len : table_cap;
-    if (lmax > table_cap)
-        lmax = table_cap;
-    if (lmax > INT32_MAX)
-        return fail(PKA_ERR_UNSUPPORTED, "context length beyond int32");
-    if (partition_size == 0)
-        partition_size = pka_decode_partition_size(num_seqs, num_kv_heads, block_size, (int32_t)lmax);
-    const int64_t parts = lmax > 0 ? ceil_div(lmax, partition_size) : 1;
-    if (parts > 0x7fffffff)
-        return fail(PKA_ERR_UNSUPPORTED, "too many partitions");
-    const size_t need = pka_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                   (int32_t)lmax, partition_size);
-    if (need > 0 && (int64_t)num_seqs * num_kv_heads > pka::kMaxCompletionCounters)
-        return fail(PKA_ERR_UNSUPPORTED,
-                    "num_seqs * num_kv_heads = %lld exceeds the %lld completion counters of a "
-                    "multi-partition workspace",
-                    (long long)num_seqs * num_kv_heads, (long long)pka::kMaxCompletionCounters);
-    if (need > 0) {
-        if (!workspace)
-            return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);
-        if (workspace_bytes < need)
-            return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got %zu",
-                        need, workspace_bytes);
-        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-            return fail(PKA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    }
-    pka::DecodeArgs a{};
-    a.out = out;
-    a.out_dtype = to_internal(out_dtype);
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_tables = block_tables;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.context_lens = context_lens;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.head_dim = head_dim;
-    a.num_blocks = num_blocks;
-    a.block_size = block_size;
-    a.scale = scale;
-    a.kv_dtype = to_internal(kv_dtype);
-    a.max_context_len = (int32_t)lmax;
-    a.partition_size = partition_size;
-    a.num_partitions = (int32_t)parts;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.k_new_token_stride = k_new_token_stride;
-    a.v_new_token_stride = v_new_token_stride;
-    a.slot_mapping = slot_mapping;
-    if (need > 0) {
-        const pka::WorkspaceLayout w =
-            pka::decode_workspace_layout(num_seqs, num_q_heads, head_dim, parts);
-        char *base = static_cast<char *>(workspace);
-        a.counters = reinterpret_cast<int32_t *>(base + w.counter_offset);
-        a.ws_o = reinterpret_cast<float *>(base + w.o_offset);
-        a.ws_ml = reinterpret_cast<float *>(base + w.ml_offset);
-        if (w.worklist) {
-            a.wl_header = reinterpret_cast<int32_t *>(base + w.header_offset);
-            a.items = reinterpret_cast<int2 *>(base + w.items_offset);
+    const int64_t chunks_per_seq = ceil_div(table_cap, 16) * num_kv_heads;
+    if (chunks_per_seq >= INT32_MAX)
+        return fail(PKA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size too large");
+    int64_t per_launch = pka::kMaxSeqsPerLaunch;
+    if (per_launch * chunks_per_seq >= INT32_MAX)
+        per_launch = (INT32_MAX - 1) / chunks_per_seq;
+    if (per_launch * num_kv_heads > pka::kMaxCounters)
+        per_launch = pka::kMaxCounters / num_kv_heads;
+    if (per_launch < 1)
+        return fail(PKA_ERR_UNSUPPORTED, "num_kv_heads %d exceeds the report counters",
+                    num_kv_heads);
+    const int64_t max_waves = pka::decode_max_waves();
+    const size_t need = pka::decode_workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                     max_waves)
+                            .total;
+    if (!workspace)
+        return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);
+    if (workspace_bytes < need)
+        return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got %zu", need,
+                    workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PKA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const pka::WorkspaceLayout wl =
+        pka::decode_workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_waves);
+    char *base = static_cast<char *>(workspace);
+    const int out_elt = pka::dtype_bytes(to_internal(out_dtype));
+    for (int64_t b0 = 0; b0 < num_seqs; b0 += per_launch) {
+        const int64_t nb = num_seqs - b0 < per_launch ? num_seqs - b0 : per_launch;
+        pka::DecodeArgs a{};
+        a.out = static_cast<char *>(out) + b0 * num_q_heads * head_dim * out_elt;
+        a.out_dtype = to_internal(out_dtype);
+        a.q = static_cast<const char *>(q) + b0 * num_q_heads * head_dim * elt;
+        a.k_cache = k_cache;
+        a.v_cache = v_cache;
+        a.block_tables = block_tables + b0 * max_blocks_per_seq;
+        a.max_blocks_per_seq = max_blocks_per_seq;
+        a.context_lens = context_lens + b0;
+        a.num_seqs = (int32_t)nb;
+        a.num_q_heads = num_q_heads;
+        a.num_kv_heads = num_kv_heads;
+        a.head_dim = head_dim;
+        a.num_blocks = num_blocks;
+        a.block_size = block_size;
+        a.scale = scale;
+        a.kv_dtype = to_internal(kv_dtype);
+        a.partition_size = partition_size;
+        a.counters = reinterpret_cast<int32_t *>(base + wl.counter_offset);
+        a.parts = reinterpret_cast<float *>(base + wl.parts_offset);
+        a.max_waves = max_waves;
+        if (k_new) {
+            a.k_new = static_cast<const char *>(k_new) + b0 * k_new_token_stride * elt;
+            a.v_new = static_cast<const char *>(v_new) + b0 * v_new_token_stride * elt;
+            a.k_new_token_stride = k_new_token_stride;
+            a.v_new_token_stride = v_new_token_stride;
+            a.slot_mapping = slot_mapping + b0;
         }
+        hipError_t e = pka::launch_paged_decode(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess)
+            return fail(PKA_ERR_HIP, "paged_attention_decode launch: %s", hipGetErrorString(e));
     }
-    hipError_t e = pka::launch_paged_decode(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(PKA_ERR_HIP, "paged_attention_decode launch: %s", hipGetErrorString(e));
     return ok();
 }
 
@@ -601,7 +589,7 @@ int32_t pka_decode_int8_partition_size(int32_t num_seqs, int32_t num_kv_heads,
     if (lmax <= 256)
         return (int32_t)(ceil_div(lmax, block_size) * block_size);
     int64_t P = kDefaultPartition;
-    while (P > 128 && pairs * ceil_div(lmax, P) < 32 * kComputeUnits)
+    while (P > 128 && pairs * ceil_div(lmax, P) < 32 * compute_units())
         P /= 2;
     return (int32_t)(ceil_div(P, block_size) * block_size);
 }

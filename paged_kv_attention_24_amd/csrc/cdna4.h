@@ -130,6 +130,39 @@ __device__ __forceinline__ float4_t mma_pv(TBF16, const uint2 &v, const uint2 &p
                                                      __builtin_bit_cast(short4_t, pr), acc, 0, 0, 0);
 }
 
+// fp32 KV: the same two tile products on v_mfma_f32_16x16x4f32, four
+// products per 16-byte operand.  Score step: lane l supplies 4 consecutive
+// dims of K[token l%16] and of q[head l%16] (one 16-byte unit); product j
+// takes dim j of the unit as its k = l/16.  PV: lane l supplies V[token
+// 4(l/16)+j][dim l%16] and P[same token][head l%16] in element j; product j
+// takes k = l/16 <-> token 4(l/16)+j.
+__device__ __forceinline__ float4_t mma_qk(TF32, const uint4 &k, const uint4 &q, float4_t acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(k.x), as_f(q.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(k.y), as_f(q.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(k.z), as_f(q.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(k.w), as_f(q.w), acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ float4_t mma_pv(TF32, const uint4 &v, const uint4 &pr, float4_t acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(v.x), as_f(pr.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(v.y), as_f(pr.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(v.z), as_f(pr.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(v.w), as_f(pr.w), acc, 0, 0, 0);
+    return acc;
+}
+
+// A wave-uniform int32 read through the scalar data cache (the address must
+// be wave-uniform and the memory unchanged for the whole kernel).  Scalar
+// loads count on lgkmcnt, so waiting for one never waits for the vector
+// loads in flight.
+__device__ __forceinline__ int32_t scalar_load(const int32_t *base, int64_t i)
+{
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    return ((const const_i32 *)(uintptr_t)base)[i];
+}
+
 // 16 bytes per lane straight from global memory into LDS at byte address
 // lds_base + 16*lane (lds_base is wave-uniform: it goes to M0).
 __device__ __forceinline__ void load_to_lds(const char *g, uint32_t lds_base)
@@ -224,6 +257,19 @@ __device__ __forceinline__ float token_group_sum(float x)
     return x;
 }
 
+// Sum over the whole wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    x += swz_xor16(x);
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    return lo + hi;
+}
+
 // Max over the whole wave, returned as a wave-uniform value.
 __device__ __forceinline__ float wave_max(float x)
 {
@@ -256,6 +302,24 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float x, int o
         static_cast<uint16_t *>(out)[idx] = f32_to_bf16_rne(x);
 }
 
+// Four consecutive output elements out[idx .. idx+3] (idx a multiple of 4)
+// in one vector store.
+__device__ __forceinline__ void store_out4(void *out, int64_t idx, float4_t x, int out_kind)
+{
+    if (out_kind == 0) {
+        *reinterpret_cast<float4_t *>(static_cast<float *>(out) + idx) = x;
+    } else if (out_kind == 1) {
+        const half2_t a = {(_Float16)x[0], (_Float16)x[1]};
+        const half2_t b = {(_Float16)x[2], (_Float16)x[3]};
+        *reinterpret_cast<uint2 *>(static_cast<_Float16 *>(out) + idx) =
+            make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+    } else {
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + idx) =
+            make_uint2(f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16),
+                       f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16));
+    }
+}
+
 // Agent-scope relaxed accesses: plain loads/stores with the coherence bit,
 // so partial rows written on one XCD are read correctly on another without
 // flushing or invalidating any L2.
@@ -267,6 +331,12 @@ __device__ __forceinline__ float coherent_load(const float *p)
 {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes (16-byte aligned) with the same coherence as coherent_store: one
+// write of four consecutive floats instead of four scattered dword writes.
+__device__ __forceinline__ void coherent_store16(float *p, float4_t v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every vector memory
 // access of this wave has completed (loads landed, stores acknowledged).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -276,18 +346,64 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left free
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
 // Every vector memory access of this wave except the n most recent has
-// completed (n is wave-uniform; counts above 15 wait for everything).
+// completed (n is wave-uniform, 0..63; vector memory accesses complete in
+// issue order for this count).
 __device__ __forceinline__ void wait_vmem_keep(int n)
 {
     switch (n) {
 #define PKA_KEEP(k) \
     case k: __builtin_amdgcn_s_waitcnt(vmcnt_imm(k)); break;
+#define PKA_KEEP8(k) PKA_KEEP(k) PKA_KEEP(k + 1) PKA_KEEP(k + 2) PKA_KEEP(k + 3) \
+    PKA_KEEP(k + 4) PKA_KEEP(k + 5) PKA_KEEP(k + 6) PKA_KEEP(k + 7)
     PKA_KEEP(1) PKA_KEEP(2) PKA_KEEP(3) PKA_KEEP(4) PKA_KEEP(5) PKA_KEEP(6) PKA_KEEP(7)
-    PKA_KEEP(8) PKA_KEEP(9) PKA_KEEP(10) PKA_KEEP(11) PKA_KEEP(12) PKA_KEEP(13) PKA_KEEP(14)
-    PKA_KEEP(15)
+    PKA_KEEP8(8) PKA_KEEP8(16) PKA_KEEP8(24) PKA_KEEP8(32) PKA_KEEP8(40) PKA_KEEP8(48)
+    PKA_KEEP8(56)
+#undef PKA_KEEP8
 #undef PKA_KEEP
     default: wait_vmem();
     }
+}
+
+// ---- LDS accesses the compiler does not see ------------------------------
+// Staged chunks arrive by LDS DMA, which the compiler tracks only as "some
+// LDS write pending": before any LDS access it would wait for every vector
+// memory access in flight, stores included.  The operand reads and the few
+// staging writes of the attention loop are therefore written here in
+// assembly, each block complete (its own lgkmcnt(0)) before it ends, and the
+// loop waits for exactly the DMA it needs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Four 16-byte reads and eight transposing 8-byte reads (one chunk's K and
+// V operands of the fp16/bf16 tiles) at LDS byte addresses ka[], va[].
+__device__ __forceinline__ void lds_read_chunk(u32x4 (&k)[4], u32x2 (&v)[8], const uint32_t (&ka)[4],
+                                               const uint32_t (&va)[8])
+{
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b64_tr_b16 %4, %16\n\t"
+        "ds_read_b64_tr_b16 %5, %17\n\t"
+        "ds_read_b64_tr_b16 %6, %18\n\t"
+        "ds_read_b64_tr_b16 %7, %19\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %21\n\t"
+        "ds_read_b64_tr_b16 %10, %22\n\t"
+        "ds_read_b64_tr_b16 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
+          "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+          "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+        : "memory");
+}
+// One 16-byte LDS write, complete before the block ends.
+__device__ __forceinline__ void lds_write16(uint32_t addr, const uint4 &x)
+{
+    const u32x4 d = {x.x, x.y, x.z, x.w};
+    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(d) : "memory");
 }
 
 }  // namespace pka

@@ -40,56 +40,58 @@ struct DecodeArgs {
     int32_t num_blocks, block_size;
     float scale;
     DType kv_dtype;
-    int32_t max_context_len;  // resolved (> 0 unless num_seqs == 0)
-    int32_t partition_size;   // resolved, multiple of block_size
-    int32_t num_partitions;   // ceil(max_context_len / partition_size), >= 1
-    float *ws_o;              // [B][Hq][num_partitions][D]    (if num_partitions > 1)
-    float *ws_ml;             // [B][Hq][num_partitions][2]    (max in log2 units, sum)
-    int2 *items;              // work list {b, j}, [B * num_partitions]; null: dense grid
-    int32_t *wl_header;       // [2]: dynamic-item counter, item count (work-list mode)
-    int32_t *counters;        // [B][Hkv] completion counters; zero before and after a call
+    int32_t partition_size;   // smallest number of tokens one wave takes; 0: library default
+    float *parts;             // [2 * max_waves] partial results of decode_part_floats(G, D)
+    int32_t *counters;        // [num_seqs][num_kv_heads] report counters, zero before and after
+    int64_t max_waves;        // waves the partial-result slots cover
     // optional appended token per sequence (k_new null: plain decode)
     const void *k_new, *v_new;
     int64_t k_new_token_stride, v_new_token_stride;  // elements
     const int64_t *slot_mapping;
 };
 
-// The workspace of a multi-partition decode starts with this many bytes of
-// completion counters (one int32 per (sequence, kv head)).  They must be
-// zero before the first call that uses the workspace; every call leaves
-// them zero.  A fixed size keeps them in place whatever the shapes.
+// The decode plans its work in the kernel from a prefix of chunk counts per
+// sequence kept in LDS, so one launch takes at most this many sequences;
+// the C ABI cuts longer batches into launches of this size.
+constexpr int kMaxSeqsPerLaunch = 2040;
+// Decode workgroups resident per compute unit (LDS staging of 4 waves x
+// 16 KiB, plus the prefix) and the waves the partial-result slots cover.
+constexpr int kMaxWorkgroupsPerCU = 2;
+// Smallest number of tokens (of any mix of pairs) one decode wave takes by
+// default: fewer, longer ranges mean fewer partial results to combine.
+constexpr int kDefaultRangeTokens = 64;
+
+// Floats of one decode partial result: the unnormalised output [G][D], then
+// the running maxima [G] and sums [G], padded to 16 bytes so that every
+// partial result and output row starts 16-byte aligned.
+constexpr int64_t decode_part_floats(int64_t group, int64_t head_dim)
+{
+    return group * head_dim + (2 * group + 3) / 4 * 4;
+}
+
+// Waves of the decode grid on the current device (2 slots of partial
+// results each).
+int decode_max_waves();
+
+// The decode workspace starts with this many bytes of report counters (one
+// int32 per (sequence, kv head) of a launch), zero before and after every
+// call; a fixed size keeps them in place whatever the shapes, so one
+// workspace serves calls of any shape.  Partial results follow.
 constexpr int64_t kCounterBytes = 1 << 20;
-// The persistent grid's scheduler keeps two counters (next work unit,
-// finished workgroups) in the last 64 bytes of that region, so
-// num_seqs * num_kv_heads completion counters fit in kCounterBytes - 64.
-constexpr int64_t kSchedBytes = 64;
-constexpr int64_t kMaxCompletionCounters = (kCounterBytes - kSchedBytes) / 4;
-// Work lists of at most this many sequences are planned inside the decode
-// kernel (a prefix of partition counts in LDS); longer batches get a
-// separate planning launch that writes the list to the workspace.
-constexpr int kPlanInKernelSeqs = 2048;
+constexpr int64_t kMaxCounters = kCounterBytes / 4;
 
-// Above this many partitions per sequence the decode builds a work list on
-// the device instead of launching a dense (partition, head, sequence) grid
-// whose workgroups past a short sequence's end would exit empty.
-#ifndef PKA_DENSE_MAX_PARTITIONS
-#define PKA_DENSE_MAX_PARTITIONS 8
-#endif
-constexpr int kDenseMaxPartitions = PKA_DENSE_MAX_PARTITIONS;
-
-// Byte offsets of the decode workspace's two regions (256-aligned starts)
-// and its total size; zero when one partition covers every sequence.
+// Byte offsets of the decode workspace: report counters, then partial
+// results (256-byte aligned starts).
 struct WorkspaceLayout {
-    size_t counter_offset, o_offset, ml_offset, header_offset, items_offset, total;
-    bool worklist;
+    size_t counter_offset, parts_offset, total;
 };
-WorkspaceLayout decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                                        int64_t num_partitions);
+WorkspaceLayout decode_workspace_layout(int64_t num_seqs, int64_t num_q_heads,
+                                        int64_t num_kv_heads, int64_t head_dim, int64_t max_waves);
 
 // Whether (dtype, head_dim, block_size, group) has a compiled kernel.
 bool decode_supported(DType kv, int head_dim, int block_size, int group);
 
-// Largest partition the kernels accept (bounds their LDS use).
+// Largest partition the INT8 kernels accept (bounds their LDS use).
 constexpr int kMaxPartition = 1024;
 
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);

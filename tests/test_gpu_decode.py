@@ -118,15 +118,21 @@ def test_block_relabel_is_bit_exact():
     assert np.array_equal(base, again)
 
 
-def test_batch_permutation_is_bit_exact():
+def test_batch_permutation():
+    """Permuting the batch permutes the outputs.  The work is split evenly
+    over the waves in batch order, so a sequence's parts (and the fp32
+    rounding of their merge) depend on its place in the batch: the outputs
+    agree to rounding, and each matches the oracle."""
     wl = case(8, "bf16", [40, 513, 1000, 7, 64], 16, 8, 128, 16, write=False)
     base = gpu_decode(wl, partition_size=256)
+    ref = oracle_full(wl)
     p = np.array([4, 2, 0, 3, 1])
     wl.q = np.ascontiguousarray(wl.q[p])
     wl.block_tables = np.ascontiguousarray(wl.block_tables[p])
     wl.context_lens = np.ascontiguousarray(wl.context_lens[p])
     again = gpu_decode(wl, partition_size=256)
-    assert np.array_equal(again, base[p])
+    assert np.max(np.abs(again - base[p])) <= 1e-5
+    check_close(again, ref[p], "bf16")
 
 
 def test_run_to_run_determinism():
@@ -171,8 +177,8 @@ def test_long_single_sequence_many_partitions():
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_skewed_work_list(dtype):
-    """Many partitions per sequence (device-built work list, persistent
-    grid): one long sequence among short and empty ones."""
+    """One long sequence among short and empty ones, with the smallest
+    shares: the long one is split over many waves."""
     lens = [0, 5000, 1, 33, 0, 700, 16, 17] + [100] * 40
     wl = case(13, dtype, lens, 16, 4, 64, 16)
     got = gpu_decode(wl, partition_size=64)  # 79 partitions for the longest
@@ -182,7 +188,7 @@ def test_skewed_work_list(dtype):
 
 def test_workspace_reuse_across_shapes():
     """One explicit workspace, zero-filled once, serves calls of different
-    shapes back to back (its completion counters stay at a fixed place and
+    shapes back to back (its report counters stay at a fixed place and
     every call leaves them zero)."""
     import torch
 
@@ -205,7 +211,7 @@ def test_workspace_reuse_across_shapes():
             torch.cuda.synchronize()
             check_close(out.double().cpu().numpy(), oracle_full(wl), wl.dtype,
                         f"round {rnd} case {i}")
-    assert int(ws[: 1 << 20].count_nonzero()) == 0  # counters left at zero
+    assert int(ws[: 1 << 20].count_nonzero()) == 0  # report counters left at zero
 
 
 def test_graph_replay_matches_eager():
@@ -258,15 +264,17 @@ def test_bad_partition_size_is_rejected():
     with pytest.raises(pka.PkaError):
         gpu_decode(wl, partition_size=24)
     with pytest.raises(pka.PkaError):
-        gpu_decode(wl, partition_size=4096)
+        gpu_decode(wl, partition_size=-16)
+    # any positive multiple of the block size is a valid smallest share
+    check_close(gpu_decode(wl, partition_size=4096), oracle_full(wl), "f16")
 
 
 @pytest.mark.parametrize("dtype,B", [("f16", 2048), ("bf16", 2049), ("f32", 2049)])
 def test_large_batch_work_list(dtype, B):
-    """Batches at and past the size the kernel plans in its own LDS: beyond
-    it the work list is planned by a separate launch into the workspace.
-    Several partitions per sequence, empty sequences mixed in; rows of the
-    longest sequence and of the last sequences are always compared."""
+    """Batches past the 2040 sequences one launch plans in its LDS run as
+    several launches that share the workspace.  Sequences split over several
+    waves, empty sequences mixed in; rows of the longest sequence and of the
+    last sequences are always compared."""
     rng = np.random.default_rng(31)
     lens = rng.integers(1, 700, size=B)
     lens[::97] = 0
