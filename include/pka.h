@@ -147,8 +147,9 @@ int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_
  * pka_decode_workspace_bytes -- bytes of device scratch
  * pka_paged_attention_decode (and _append) needs for these shapes on the
  * current device: 1 MiB of report counters, then two partial-result slots
- * of (num_q_heads / num_kv_heads) * (head_dim + 2) floats per wave of the
- * decode grid.  It does not depend on the context lengths.  0 when
+ * per wave of the decode grid, each of G * head_dim output floats and 2 G
+ * (max, sum) floats padded to a multiple of 4 (G = num_q_heads /
+ * num_kv_heads).  It does not depend on the context lengths.  0 when
  * num_seqs <= 0.
  */
 size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
