@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKA_ABI_VERSION 7
+#define PKA_ABI_VERSION 8
 
 typedef enum pka_status {
     PKA_OK = 0,
@@ -218,6 +218,33 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
                                       pka_dtype kv_dtype, int32_t max_context_len,
                                       int32_t partition_size, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * pka_paged_attention_decode_noalloc -- pka_paged_attention_decode without
+ * a workspace argument and without any device allocation, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * The report counters and partial results live in a static device array of
+ * PKA_DECODE_STATIC_SCRATCH_BYTES bytes that the library holds on every GPU
+ * it runs on until the process ends.  The first call on a device takes that
+ * array's address and clears its counters (a fill kernel on `stream`); each
+ * call leaves them zero again.  All calls on one GPU share the array: calls
+ * that overlap on one GPU (different streams, or threads without ordering)
+ * race and give unspecified results.  Arguments and results are those of
+ * pka_paged_attention_decode (same kernels, bit-identical output).
+ * Returns PKA_ERR_WORKSPACE_TOO_SMALL when the shapes need more scratch than
+ * the array holds (pka_decode_workspace_bytes() above the limit: not the
+ * case for any supported shape on a GPU of up to 256 compute units), and
+ * PKA_ERR_HIP when the array's address cannot be obtained.
+ */
+#define PKA_DECODE_STATIC_SCRATCH_BYTES (18u << 20)
+pka_status pka_paged_attention_decode_noalloc(
+    void *out, pka_dtype out_dtype, const void *q, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, float scale, pka_dtype kv_dtype,
+    int32_t max_context_len, int32_t partition_size, void *stream);
 
 /*
  * pka_paged_attention_decode_append -- one decode step of a batch in a

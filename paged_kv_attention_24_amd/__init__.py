@@ -41,6 +41,7 @@ from typing import Optional
 
 __all__ = [
     "PkaError", "kv_cache_write", "paged_attention_decode", "paged_attention_decode_append",
+    "paged_attention_decode_noalloc",
     "paged_attention_prefill", "kv_cache_write_rope", "copy_blocks", "gather_blocks", "scatter_blocks", "swap_out",
     "swap_in",
     "decode_partition_size",
@@ -96,6 +97,10 @@ def load_library():
         P, ctypes.c_int, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
         ctypes.c_int, i32, i32, P, ctypes.c_size_t, P]
     lib.pka_paged_attention_decode.restype = ctypes.c_int
+    lib.pka_paged_attention_decode_noalloc.argtypes = [
+        P, ctypes.c_int, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+        ctypes.c_int, i32, i32, P]
+    lib.pka_paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.pka_paged_attention_decode_append.argtypes = [
         P, ctypes.c_int, P, P, P, i64, i64, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
         ctypes.c_float, ctypes.c_int, i32, i32, P, ctypes.c_size_t, P]
@@ -220,7 +225,8 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
 
 
 def _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, block_size,
-                  out, out_dtype, partition_size, max_context_len, workspace):
+                  out, out_dtype, partition_size, max_context_len, workspace,
+                  use_workspace: bool = True):
     import torch
 
     _require_gpu(q, k_cache, v_cache, block_tables, context_lens)
@@ -255,7 +261,7 @@ def _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
     hint = min(hint, MB * bs)
     P = int(partition_size)  # 0: the library default; the C ABI rejects bad values
     ws_ptr, ws_bytes = None, 0
-    if B > 0:
+    if B > 0 and use_workspace:
         need = decode_workspace_bytes(B, Hq, Hkv, D)
         if workspace is None:
             workspace = _cached_workspace(q.device, need)
@@ -293,6 +299,29 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         a["B"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], float(scale),
         _dtype_code(k_cache.dtype), a["hint"], a["P"], a["ws_ptr"], a["ws_bytes"],
         _stream_ptr(q.device)))
+    return a["out"]
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens,
+                                   scale: float, num_kv_heads: int, block_size: int, *, out,
+                                   partition_size: int = 0, max_context_len: int = 0):
+    """paged_attention_decode into ``out`` with the library's static device
+    scratch instead of a workspace: the call allocates no device memory when
+    its inputs are already contiguous.  Calls that overlap on one GPU race
+    (they share that scratch)."""
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    a = _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                      block_size, out, None, partition_size, max_context_len, None,
+                      use_workspace=False)
+    if a["B"] == 0:
+        return a["out"]
+    lib = load_library()
+    _check(lib.pka_paged_attention_decode_noalloc(
+        a["out"].data_ptr(), _dtype_code(a["out"].dtype), a["q"].data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), a["block_tables"].data_ptr(), a["MB"], a["context_lens"].data_ptr(),
+        a["B"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], float(scale),
+        _dtype_code(k_cache.dtype), a["hint"], a["P"], _stream_ptr(q.device)))
     return a["out"]
 
 

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "pka_internal.h"
 
@@ -207,6 +208,59 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
 
 }  // extern "C"
 
+// Workspace of pka_paged_attention_decode_noalloc: report counters, then
+// partial results, as in a caller's decode workspace.  Each device holds its
+// own copy; host code uses only the per-device address from
+// hipGetSymbolAddress, never this name.
+static_assert(PKA_DECODE_STATIC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) char scratch[PKA_DECODE_STATIC_SCRATCH_BYTES];
+
+__global__ void zero_words(int32_t *p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, set up (address taken, counters
+// cleared on `stream`) by the first call on that device.
+pka_status static_scratch(void **ptr, hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(PKA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKA_ERR_UNSUPPORTED, "device %d beyond the %d the static scratch serves", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(PKA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        // the counters must read zero before the first decode (a kernel
+        // rather than a memset, so that a captured first call stays valid)
+        constexpr int64_t n = pka::kCounterBytes / 4;
+        hipLaunchKernelGGL(zero_words, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<int32_t *>(p), n);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(PKA_ERR_HIP, "clearing the static scratch: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PKA_OK;
+}
+
+}  // namespace
+
 static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *context_lens,
@@ -216,7 +270,7 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
                               int32_t partition_size, void *workspace, size_t workspace_bytes,
                               void *stream, const void *k_new, const void *v_new,
                               int64_t k_new_token_stride, int64_t v_new_token_stride,
-                              const int64_t *slot_mapping)
+                              const int64_t *slot_mapping, bool static_workspace = false)
 {
     if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype))
         return fail(PKA_ERR_INVALID_ARGUMENT, "unknown dtype");
@@ -282,6 +336,16 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
     const size_t need = pka::decode_workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                      max_waves)
                             .total;
+    if (static_workspace) {
+        if (need > sizeof(scratch))
+            return fail(PKA_ERR_WORKSPACE_TOO_SMALL,
+                        "decode needs %zu bytes of scratch; the static scratch holds %zu", need,
+                        sizeof(scratch));
+        const pka_status s = static_scratch(&workspace, static_cast<hipStream_t>(stream));
+        if (s != PKA_OK)
+            return s;
+        workspace_bytes = sizeof(scratch);
+    }
     if (!workspace)
         return fail(PKA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes required, got NULL", need);
     if (workspace_bytes < need)
@@ -347,6 +411,19 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
                        block_size, scale, kv_dtype, max_context_len, partition_size, workspace,
                        workspace_bytes, stream, nullptr, nullptr, 0, 0, nullptr);
+}
+
+pka_status pka_paged_attention_decode_noalloc(
+    void *out, pka_dtype out_dtype, const void *q, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, float scale, pka_dtype kv_dtype,
+    int32_t max_context_len, int32_t partition_size, void *stream)
+{
+    return decode_impl(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                       block_size, scale, kv_dtype, max_context_len, partition_size, nullptr, 0,
+                       stream, nullptr, nullptr, 0, 0, nullptr, /*static_workspace=*/true);
 }
 
 pka_status pka_paged_attention_decode_append(

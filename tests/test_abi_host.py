@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strings():
     lib = pka.load_library()
-    assert lib.pka_abi_version() == 7
+    assert lib.pka_abi_version() == 8
     assert lib.pka_status_string(0) == b"ok"
     assert lib.pka_status_string(3) == b"workspace too small"
     assert lib.pka_status_string(99) == b"unknown status"
@@ -105,6 +105,48 @@ def test_decode_rejects(over, status):
     st, msg = decode(**over)
     assert st == status, (over, st, msg)
     assert msg
+
+
+def decode_noalloc(**over):
+    a = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=128, cl=FAKE, B=16, Hq=32,
+             Hkv=8, D=64, NB=1000, bs=16, scale=0.125, kdt=1, maxl=2048, P=0)
+    a.update(over)
+    lib = pka.load_library()
+    st = lib.pka_paged_attention_decode_noalloc(
+        a["out"], a["odt"], a["q"], a["kc"], a["vc"], a["bt"], a["MB"], a["cl"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["NB"], a["bs"], a["scale"], a["kdt"], a["maxl"], a["P"], None)
+    return st, lib.pka_last_error().decode()
+
+
+@fake_pointers
+@pytest.mark.parametrize("over,status", [
+    (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(NB=0), 1),
+    (dict(MB=0), 1), (dict(B=-1), 1), (dict(D=80), 2), (dict(bs=64), 2), (dict(Hq=24), 2),
+    (dict(scale=float("nan")), 1), (dict(P=24), 1), (dict(q=None), 1), (dict(out=FAKE + 2), 1),
+    (dict(B=70000), 2), (dict(cl=None), 1),
+])
+def test_decode_noalloc_rejects(over, status):
+    # the arguments are checked before the static scratch is touched
+    st, msg = decode_noalloc(**over)
+    assert st == status, (over, st, msg)
+    assert msg
+
+
+@fake_pointers
+def test_decode_noalloc_empty_batch_is_ok_without_launch():
+    st, _ = decode_noalloc(B=0, out=None, q=None)
+    assert st == 0
+
+
+def test_static_scratch_covers_every_supported_shape():
+    # the no-allocation decode's scratch holds the largest workspace of any
+    # supported shape on a GPU of 256 compute units
+    if not _no_gpu_visible():
+        pytest.skip("the grid depends on the visible GPU")
+    limit = 18 << 20
+    for D in (64, 128):
+        for G in (1, 2, 4, 8):
+            assert pka.decode_workspace_bytes(4096, 8 * G, 8, D) <= limit, (D, G)
 
 
 @fake_pointers
