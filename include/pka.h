@@ -146,7 +146,8 @@ int32_t pka_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_
 /*
  * pka_decode_workspace_bytes -- bytes of device scratch
  * pka_paged_attention_decode (and _append) needs for these shapes on the
- * current device: 1 MiB of report counters, then two partial-result slots
+ * current device: 4 MiB of report counters (one per 128-byte line), then
+ * two partial-result slots
  * per wave of the decode grid, each of G * head_dim output floats and 2 G
  * (max, sum) floats padded to a multiple of 4 (G = num_q_heads /
  * num_kv_heads).  It does not depend on the context lengths.  0 when
@@ -238,7 +239,7 @@ pka_status pka_paged_attention_decode(void *out, pka_dtype out_dtype, const void
  * case for any supported shape on a GPU of up to 256 compute units), and
  * PKA_ERR_HIP when the array's address cannot be obtained.
  */
-#define PKA_DECODE_STATIC_SCRATCH_BYTES (18u << 20)
+#define PKA_DECODE_STATIC_SCRATCH_BYTES (22u << 20)
 pka_status pka_paged_attention_decode_noalloc(
     void *out, pka_dtype out_dtype, const void *q, const void *k_cache, const void *v_cache,
     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,

@@ -102,6 +102,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // S^T tile += K rows (16 tokens x 32 dims) * q^T (32 dims x 16 heads).
 // Lane l supplies K[token l%16][dims 8(l/16)..+7] and q[head l%16][same dims];
@@ -270,6 +271,54 @@ __device__ __forceinline__ float wave_sum(float x)
     return lo + hi;
 }
 
+// Sums / maxima over the whole wave of N values at once, returned
+// wave-uniform: the stages of the N reductions are interleaved, so their
+// latencies overlap instead of adding up.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&x)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0xB1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0x4E>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0x141>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp<0x140>(x[i]);
+    float t[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) t[i] = swz_xor16(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        x[i] += t[i];
+        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[i]), 0));
+        const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[i]), 32));
+        x[i] = lo + hi;
+    }
+}
+template <int N>
+__device__ __forceinline__ void wave_max_n(float (&x)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = fmaxf(x[i], dpp<0xB1>(x[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = fmaxf(x[i], dpp<0x4E>(x[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = fmaxf(x[i], dpp<0x141>(x[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = fmaxf(x[i], dpp<0x140>(x[i]));
+    float t[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) t[i] = swz_xor16(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        x[i] = fmaxf(x[i], t[i]);
+        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[i]), 0));
+        const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[i]), 32));
+        x[i] = fmaxf(lo, hi);
+    }
+}
+
 // Max over the whole wave, returned as a wave-uniform value.
 __device__ __forceinline__ float wave_max(float x)
 {
@@ -331,11 +380,27 @@ __device__ __forceinline__ float coherent_load(const float *p)
 {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16 bytes (16-byte aligned) with the same coherence as coherent_store: one
-// write of four consecutive floats instead of four scattered dword writes.
-__device__ __forceinline__ void coherent_store16(float *p, float4_t v)
+// Raw buffer view of `bytes` bytes at `base` (wave-uniform), for the 16-byte
+// coherent accesses below; accesses past `bytes` read zero / write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(void *base, uint32_t bytes)
 {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+// Cache policy of the buffer accesses: sc1, the coherence bit that the
+// agent-scope relaxed accesses above carry.
+constexpr int kCoherentPolicy = 16;
+// 16 bytes at a 16-byte aligned byte offset, with the coherence of
+// coherent_store / coherent_load: one access for four consecutive floats.
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset,
+                                                 float4_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_offset, 0,
+                                           kCoherentPolicy);
+}
+__device__ __forceinline__ float4_t coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset)
+{
+    return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0,
+                                                                              kCoherentPolicy));
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every vector memory
 // access of this wave has completed (loads landed, stores acknowledged).
@@ -371,7 +436,6 @@ __device__ __forceinline__ void wait_vmem_keep(int n)
 // staging writes of the attention loop are therefore written here in
 // assembly, each block complete (its own lgkmcnt(0)) before it ends, and the
 // loop waits for exactly the DMA it needs.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Four 16-byte reads and eight transposing 8-byte reads (one chunk's K and
@@ -400,6 +464,14 @@ __device__ __forceinline__ void lds_read_chunk(u32x4 (&k)[4], u32x2 (&v)[8], con
         : "memory");
 }
 // One 16-byte LDS write, complete before the block ends.
+// 16 bytes from LDS byte address addr, waited for in the same block (the
+// compiler does not track it, so it never waits for LDS DMA on its behalf).
+__device__ __forceinline__ uint4 lds_read16(uint32_t addr)
+{
+    u32x4 d;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d) : "v"(addr) : "memory");
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
 __device__ __forceinline__ void lds_write16(uint32_t addr, const uint4 &x)
 {
     const u32x4 d = {x.x, x.y, x.z, x.w};

@@ -65,8 +65,8 @@ struct DecodeParams {
     float scale_log2;     // scale * log2(e)
     int32_t len_cap;      // lengths are clamped to [0, len_cap]
     int32_t min_chunks;   // an active wave takes at least this many chunks
-    float *parts;         // [2 * grid waves][G][D + 2] partial results
-    int32_t *counters;    // [num_seqs][num_kv_heads] reports per split pair; zero between calls
+    float *parts;         // [2 * grid waves] partial results of decode_part_floats(G, D)
+    int32_t *counters;    // [num_seqs][num_kv_heads] reports per split pair, kCounterStride apart; zero between calls
     // appended token per sequence (k_new null: plain decode)
     const char *k_new, *v_new;
     int64_t k_new_stride, v_new_stride;  // bytes between sequences
@@ -86,7 +86,9 @@ struct Shape {
     static constexpr int CT = NL * TPL;            // tokens per chunk
     static constexpr int TPC = CT / 16;            // 16-token tiles per chunk
     static constexpr int CHUNK = NL * 1024;        // bytes of one tensor's chunk
-    static constexpr int STAGE = 2 * 2 * CHUNK;    // LDS per wave: 2 buffers of K and V
+    static constexpr int QROWS = G * R;            // bytes of a pair's G query rows
+    static constexpr int QA = (QROWS + 2 * R + 1023) / 1024 * 1024;  // q rows, new K row, new V row
+    static constexpr int STAGE = 2 * 2 * CHUNK + QA;  // LDS per wave: 2 buffers of K and V, then QA
     static constexpr int TILE = BS * R;            // bytes of one (block, head) tile
     static constexpr int KS = D * ELT / 64;        // 16-byte steps of the score product
     static constexpr int MT = D / 16;              // 16-dim tiles of the output
@@ -372,26 +374,42 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     // the segment's first chunk into buffer buf, its q^T operand (head n,
     // 16-byte unit quad + 4 st) and, when it holds position L - 1 of an
     // appending call, the new K/V row (lanes < LPR, unit cl)
-    auto prime = [&](const Segment &s, uint4 (&qop)[KS], uint4 &knew, uint4 &vnew, int buf,
-                     const Ids &ids) __attribute__((always_inline)) {
-        stage_chunk(s, s.k0, buf, ids);
-        const int nn = head_ok ? n : G - 1;
-        const char *qrow = p.q + ((int64_t)s.b * p.num_q_heads + s.h * G + nn) * R;
+    // The pair's q rows (and, when the segment holds position L - 1 of an
+    // appending call, the new K and V rows) go to this wave's QA area by
+    // DMA ahead of the chunk, so the wait for the chunk covers them and no
+    // register load is in flight across the loop (which would make the
+    // compiler wait for every access, stores included, before using it).
+    const uint32_t qa_lds = stage_lds + 4 * CHUNK;
+    auto prime = [&](const Segment &s, int64_t &pool_slot, int buf, const Ids &ids)
+                     __attribute__((always_inline)) {
+        const char *qsrc = p.q + ((int64_t)s.b * p.num_q_heads + s.h * G) * R;
 #pragma unroll
-        for (int st = 0; st < KS; ++st)
-            qop[st] = *reinterpret_cast<const uint4 *>(qrow + 16 * (quad + 4 * st));
+        for (int i = 0; i < (S::QROWS + 1023) / 1024; ++i)
+            if (i * 1024 + lane * 16 < S::QROWS)
+                load_to_lds(qsrc + i * 1024 + lane * 16, qa_lds + i * 1024);
         if (p.k_new != nullptr && s.k1 == s.nch) {
-            const int64_t hoff = (int64_t)s.h * R + cl * 16;
-            knew = *reinterpret_cast<const uint4 *>(p.k_new + s.b * p.k_new_stride + hoff);
-            vnew = *reinterpret_cast<const uint4 *>(p.v_new + s.b * p.v_new_stride + hoff);
+            if (lane < LPR) {
+                const int64_t hoff = (int64_t)s.h * R + lane * 16;
+                load_to_lds(p.k_new + s.b * p.k_new_stride + hoff, qa_lds + S::QROWS);
+                load_to_lds(p.v_new + s.b * p.v_new_stride + hoff, qa_lds + S::QROWS + R);
+            }
+            const int32_t *slot_words = reinterpret_cast<const int32_t *>(p.slots);
+            const uint32_t lo = (uint32_t)scalar_load(slot_words, 2 * (int64_t)s.b);
+            const uint32_t hi = (uint32_t)scalar_load(slot_words, 2 * (int64_t)s.b + 1);
+            pool_slot = (int64_t)(((uint64_t)hi << 32) | lo);
         }
+        stage_chunk(s, s.k0, buf, ids);
     };
 
-    // where this lane's partial results of a segment go
-    auto part_base = [&](int64_t slot) { return p.parts + slot * S::PART; };
+    // partial results: slot s holds S::PART floats at byte s * 4 * S::PART
+    // (two slots per launched wave)
+    const __amdgpu_buffer_rsrc_t parts_view =
+        buffer_view(p.parts, (uint32_t)(2u * gridDim.x * kWaves * S::PART * 4u));
+    auto part_byte = [&](int64_t slot) { return (uint32_t)(slot * (S::PART * 4)); };
 
-    uint4 qop[KS], knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
-    prime(cur, qop, knew, vnew, 0, load_ids(cur, cur.k0));
+    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+    int64_t pool_slot = -1;
+    prime(cur, pool_slot, 0, load_ids(cur, cur.k0));
     int par = 0;  // chunk buffer of the current segment's first chunk
     // split segments of this range (at most the first and the last), reported
     // once the whole range is done: {b, h, first flat chunk of the pair}
@@ -429,13 +447,14 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         } else if (head_ok) {
             // partial: (unnormalised O, max in log2 units, sum) with stores
             // that another XCD reads back
-            float *pb = part_base(pend.part_slot);
+            const uint32_t pb = part_byte(pend.part_slot);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                coherent_store16(pb + n * D + 16 * mt + 4 * quad, pend.O[mt]);
+                coherent_store16(parts_view, pb + 4 * (n * D + 16 * mt + 4 * quad), pend.O[mt]);
             if (quad == 0) {
-                coherent_store(pb + G * D + n, pend.m);
-                coherent_store(pb + G * D + G + n, pend.l);
+                float *pf = p.parts + pend.part_slot * S::PART;
+                coherent_store(pf + G * D + n, pend.m);
+                coherent_store(pf + G * D + G + n, pend.l);
             }
         }
         if (pend.app && lane < LPR) {
@@ -472,7 +491,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         Segment nxt2;
         bool has_next2 = false;
         Ids ids_carry{};
-        uint4 qopn[KS], knewn = make_uint4(0, 0, 0, 0), vnewn = make_uint4(0, 0, 0, 0);
+        int64_t pool_slotn = -1;
         auto ids_after = [&](int k) __attribute__((always_inline)) {
             Ids r{};
             if (k < cur.k1)
@@ -485,20 +504,22 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         const int k_app = cur.nch - 1;                 // chunk of position L - 1
         const int row_app = cur.L - 1 - k_app * CT;    // its row in that chunk
 
-        // q (requested with the first chunk; the compiler waits for exactly
-        // those loads): sign of the scale, zero padding heads
-        if constexpr (S::F32)
-            wait_vmem();
+        // q^T operand (head n, 16-byte unit quad + 4 st) from QA, read once
+        // the segment's first chunk (DMA'd after it) has landed: sign of the
+        // scale applied, padding heads zero
         uint4 qs[KS];
+        auto read_q = [&]() __attribute__((always_inline)) {
+            const int nn = head_ok ? n : G - 1;
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-            uint4 v = qop[st];
-            v.x ^= qflip;
-            v.y ^= qflip;
-            v.z ^= qflip;
-            v.w ^= qflip;
-            qs[st] = select4(head_ok, v, make_uint4(0, 0, 0, 0));
-        }
+            for (int st = 0; st < KS; ++st) {
+                uint4 v = lds_read16(qa_lds + nn * R + 16 * (quad + 4 * st));
+                v.x ^= qflip;
+                v.y ^= qflip;
+                v.z ^= qflip;
+                v.w ^= qflip;
+                qs[st] = select4(head_ok, v, make_uint4(0, 0, 0, 0));
+            }
+        };
         float4_t O[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -535,8 +556,12 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
                             lds_write16(vdl + i * 1024 + lane * 16, make_uint4(0, 0, 0, 0));
                     }
             }
+            if (kk == 0)
+                read_q();
             if (app && k == k_app && lane < LPR) {
-                // position L-1 takes the new K/V, not the pool
+                // position L-1 takes the new K/V (from QA), not the pool
+                knew = lds_read16(qa_lds + S::QROWS + 16 * lane);
+                vnew = lds_read16(qa_lds + S::QROWS + R + 16 * lane);
                 const uint32_t ko = row_app * R + 16 * (lane ^ swk(row_app));
                 const uint32_t vo = row_app * R + 16 * (lane ^ swv(row_app));
                 if constexpr (S::F32) {
@@ -600,7 +625,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
                 stage_chunk(cur, k + 1, nbuf, ids_a);
                 ids_a = ids_after(k + 2);
             } else if (has_next) {
-                prime(nxt, qopn, knewn, vnewn, nbuf, ids_a);
+                prime(nxt, pool_slotn, nbuf, ids_a);
                 has_next2 = advance(nxt, nxt2);
                 ids_carry = ids_following(nxt, has_next2, nxt2);
             }
@@ -699,7 +724,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         pend.knew = knew;
         pend.vnew = vnew;
         pend.part_slot = 2 * a + (cur.first ? 0 : 1);
-        pend.pool_slot = app ? p.slots[cur.b] : -1;
+        pend.pool_slot = app ? pool_slot : -1;
         if (!pend.whole) {
             if (cur.first) {
                 sp_b[0] = cur.b;
@@ -718,11 +743,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         nxt = nxt2;
         has_next = has_next2;
         ids_a = ids_carry;
-#pragma unroll
-        for (int st = 0; st < KS; ++st)
-            qop[st] = qopn[st];
-        knew = knewn;
-        vnew = vnewn;
+        pool_slot = pool_slotn;
     }
 
     flush();  // the last segment's stores
@@ -744,31 +765,67 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     int old = -1;
     const int rb = lane == 0 ? sp_b[0] : sp_b[1], rh = lane == 0 ? sp_h[0] : sp_h[1];
     if (lane < 2 && rb >= 0)
-        old = __hip_atomic_fetch_add(p.counters + (int64_t)rb * Hkv + rh, 1, __ATOMIC_RELAXED,
+        old = __hip_atomic_fetch_add(p.counters + ((int64_t)rb * Hkv + rh) * kCounterStride, 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     const bool last0 = __builtin_amdgcn_readlane(old, 0) == nseg_[0] - 1 && sp_b[0] >= 0;
     const bool last1 = __builtin_amdgcn_readlane(old, 1) == nseg_[1] - 1 && sp_b[1] >= 0;
+    // out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over a pair's
+    // parts, 64 parts at a time with a running maximum.  Lane j of a batch
+    // reads part j's (max, sum) block (2G floats, 16-byte loads); each lane
+    // accumulates its output elements e = lane + 64 i (head (64 i) / D, the
+    // same in all lanes) over the parts, BJ parts' rows at a time.  When this
+    // wave combines both of its split pairs, the first batch of loads of both
+    // is requested before either is combined.
+    constexpr int E = G * D / kWave;          // output elements per lane
+    constexpr int BJ = E >= 16 ? 4 : 64 / E;  // parts per batch of row loads
+    constexpr int MLV = (2 * G + 3) / 4;      // 16-byte loads of one (max, sum) block
+    struct Merge {
+        int64_t wf, slot_wf;  // first contributing wave, its slot
+        int nseg;
+        float4_t ml[MLV];     // the first batch: part `lane`'s (max, sum)
+        float o[BJ][E];       // the first batch: rows of parts 0 .. BJ-1
+    };
+    Merge mg[2];
+    const bool lastv[2] = {last0, last1};
+    // part of wave ww: the first contributing wave holds it in its second
+    // slot when the pair starts inside that wave's range; every later wave's
+    // range starts inside the pair, so there it is the first slot
+    auto slot_of = [&](const Merge &m, int64_t ww) { return ww == m.wf ? m.slot_wf : 2 * ww; };
+    auto load_ml = [&](const Merge &m, int j0, float4_t (&ml)[MLV]) __attribute__((always_inline)) {
+        const int nb = m.nseg - j0 < kWave ? m.nseg - j0 : kWave;
+        const uint32_t pb = part_byte(slot_of(m, m.wf + j0 + (lane < nb ? lane : nb - 1)));
+#pragma unroll
+        for (int v = 0; v < MLV; ++v)
+            ml[v] = coherent_load16(parts_view, pb + 4 * (G * D + 4 * v));
+    };
+    auto load_rows = [&](const Merge &m, int j0, int jj, float (&o)[BJ][E]) __attribute__((always_inline)) {
+        const int nb = m.nseg - j0 < kWave ? m.nseg - j0 : kWave;
+#pragma unroll
+        for (int u = 0; u < BJ; ++u) {
+            const int j = jj + u < nb ? jj + u : nb - 1;
+            const float *pr = p.parts + slot_of(m, m.wf + j0 + j) * S::PART;
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                o[u][i] = coherent_load(pr + kWave * i + lane);
+        }
+    };
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
-        if (!(si == 0 ? last0 : last1))
+        if (!lastv[si])
             continue;
+        Merge &m = mg[si];
+        m.wf = wf_[si];
+        m.nseg = nseg_[si];
+        m.slot_wf = 2 * m.wf + (sp_pc0[si] > range_start(m.wf, C, N) ? 1 : 0);
+        load_ml(m, 0, m.ml);
+        load_rows(m, 0, 0, m.o);
+    }
+#pragma unroll
+    for (int si = 0; si < 2; ++si) {
+        if (!lastv[si])
+            continue;
+        Merge &m = mg[si];
         const int bb = sp_b[si], hh = sp_h[si];
-        const int64_t ps = sp_pc0[si], wf = wf_[si];
-        const int nseg = nseg_[si];
-        int32_t *counter = p.counters + (int64_t)bb * Hkv + hh;
-        // out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over the parts,
-        // 64 parts at a time with a running maximum.  Lane j of a batch reads
-        // part j's (max, sum) of every head; each lane accumulates its output
-        // elements e = lane + 64 i (head (64 i) / D, the same in all lanes)
-        // over the parts, BJ parts' rows at a time; the first rows are
-        // requested together with the (max, sum) pairs.
-        constexpr int E = G * D / kWave;            // output elements per lane
-        constexpr int BJ = E >= 16 ? 4 : 64 / E;    // parts per batch of row loads
-        // part of wave ww: the first contributing wave holds it in its second
-        // slot when the pair starts inside that wave's range; every later
-        // wave's range starts inside the pair, so there it is the first slot
-        const int64_t slot_wf = 2 * wf + (ps > range_start(wf, C, N) ? 1 : 0);
-        auto slot_of = [&](int64_t ww) { return ww == wf ? slot_wf : 2 * ww; };
         float Mrun[G], den[G], acc[E];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -778,70 +835,91 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
 #pragma unroll
         for (int i = 0; i < E; ++i)
             acc[i] = 0.0f;
-        for (int j0 = 0; j0 < nseg; j0 += kWave) {
-            const int nb = nseg - j0 < kWave ? nseg - j0 : kWave;
+        for (int j0 = 0; j0 < m.nseg; j0 += kWave) {
+            const int nb = m.nseg - j0 < kWave ? m.nseg - j0 : kWave;
             const bool mine = lane < nb;
-            const float *pl = part_base(slot_of(wf + j0 + (mine ? lane : nb - 1)));
-            float mj[G], lj[G], wj[G];
+            float4_t ml[MLV];
+            float o[BJ][E];
+            if (j0 == 0) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                mj[g] = coherent_load(pl + G * D + g);
-                lj[g] = coherent_load(pl + G * D + G + g);
-            }
-            auto row_loads = [&](int jj, float (&o)[BJ][E]) __attribute__((always_inline)) {
+                for (int v = 0; v < MLV; ++v)
+                    ml[v] = m.ml[v];
 #pragma unroll
-                for (int u = 0; u < BJ; ++u) {
-                    const int j = jj + u < nb ? jj + u : nb - 1;
-                    const float *pr = part_base(slot_of(wf + j0 + j));
+                for (int u = 0; u < BJ; ++u)
 #pragma unroll
                     for (int i = 0; i < E; ++i)
-                        o[u][i] = coherent_load(pr + kWave * i + lane);
-                }
-            };
-            float o[BJ][E];
-            row_loads(0, o);
+                        o[u][i] = m.o[u][i];
+            } else {
+                load_ml(m, j0, ml);
+                load_rows(m, j0, 0, o);
+            }
+            // the G heads' weights (lanes past the last part weigh 0)
+            float mj[G], lj[G], mx[G], wj[G], sw[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                if (!mine) {
-                    mj[g] = -INFINITY;
-                    lj[g] = 0.0f;
-                }
-                const float Mb = fmaxf(Mrun[g], wave_max(mj[g]));
+                mj[g] = mine ? ml[g / 4][g % 4] : -INFINITY;
+                lj[g] = mine ? ml[(G + g) / 4][(G + g) % 4] : 0.0f;
+                mx[g] = mj[g];
+            }
+            wave_max_n(mx);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float Mb = fmaxf(Mrun[g], mx[g]);
                 const float rs = Mrun[g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mrun[g] - Mb);
                 wj[g] = mj[g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj[g] - Mb);
-                den[g] = den[g] * rs + wave_sum(wj[g] * lj[g]);
+                sw[g] = wj[g] * lj[g];
+                den[g] *= rs;
 #pragma unroll
                 for (int i = 0; i < E; ++i)
                     if ((kWave * i) / D == g)
                         acc[i] *= rs;
                 Mrun[g] = Mb;
             }
+            wave_sum_n(sw);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                den[g] += sw[g];
             for (int jj = 0; jj < nb; jj += BJ) {
                 if (jj > 0)
-                    row_loads(jj, o);
+                    load_rows(m, j0, jj, o);
+                float wgt[BJ][G];
 #pragma unroll
-                for (int u = 0; u < BJ; ++u) {
-                    const int j = jj + u;
+                for (int u = 0; u < BJ; ++u)
 #pragma unroll
-                    for (int i = 0; i < E; ++i) {
-                        const int g = (kWave * i) / D;
-                        const float wgt = j < nb ? __builtin_bit_cast(
-                                                       float, __builtin_amdgcn_readlane(
-                                                                  __builtin_bit_cast(int, wj[g]), j))
-                                                 : 0.0f;
-                        acc[i] = fmaf(wgt, o[u][i], acc[i]);
-                    }
-                }
+                    for (int g = 0; g < G; ++g)
+                        wgt[u][g] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj[g]), jj + u));
+#pragma unroll
+                for (int u = 0; u < BJ; ++u)
+#pragma unroll
+                    for (int i = 0; i < E; ++i)
+                        acc[i] = fmaf(wgt[u][(kWave * i) / D], o[u][i], acc[i]);
             }
         }
+        float res[E];
+        int64_t idx[E];
 #pragma unroll
         for (int i = 0; i < E; ++i) {
             const int g = (kWave * i) / D, d = kWave * i + lane - g * D;
-            store_out(p.out, ((int64_t)bb * p.num_q_heads + hh * G + g) * D + d,
-                      den[g] > 0.0f ? acc[i] / den[g] : 0.0f, p.out_kind);
+            res[i] = den[g] > 0.0f ? acc[i] / den[g] : 0.0f;
+            idx[i] = ((int64_t)bb * p.num_q_heads + hh * G + g) * D + d;
+        }
+        if (p.out_kind == 0) {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                store_out(p.out, idx[i], res[i], 0);
+        } else if (p.out_kind == 1) {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                store_out(p.out, idx[i], res[i], 1);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                store_out(p.out, idx[i], res[i], 2);
         }
         if (lane == 0)
-            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.counters + ((int64_t)bb * Hkv + hh) * kCounterStride, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -42,7 +42,7 @@ struct DecodeArgs {
     DType kv_dtype;
     int32_t partition_size;   // smallest number of tokens one wave takes; 0: library default
     float *parts;             // [2 * max_waves] partial results of decode_part_floats(G, D)
-    int32_t *counters;        // [num_seqs][num_kv_heads] report counters, zero before and after
+    int32_t *counters;        // [num_seqs][num_kv_heads] report counters (kCounterStride apart), zero before and after
     int64_t max_waves;        // waves the partial-result slots cover
     // optional appended token per sequence (k_new null: plain decode)
     const void *k_new, *v_new;
@@ -76,9 +76,12 @@ int decode_max_waves();
 // The decode workspace starts with this many bytes of report counters (one
 // int32 per (sequence, kv head) of a launch), zero before and after every
 // call; a fixed size keeps them in place whatever the shapes, so one
-// workspace serves calls of any shape.  Partial results follow.
-constexpr int64_t kCounterBytes = 1 << 20;
-constexpr int64_t kMaxCounters = kCounterBytes / 4;
+// workspace serves calls of any shape.  Partial results follow.  Each
+// counter has a 128-byte line to itself: atomics on one line are served one
+// after another, so counters sharing a line would queue behind each other.
+constexpr int64_t kCounterBytes = 4 << 20;
+constexpr int64_t kCounterStride = 32;  // int32s between counters (128 bytes)
+constexpr int64_t kMaxCounters = kCounterBytes / 4 / kCounterStride;
 
 // Byte offsets of the decode workspace: report counters, then partial
 // results (256-byte aligned starts).

@@ -211,7 +211,7 @@ def test_workspace_reuse_across_shapes():
             torch.cuda.synchronize()
             check_close(out.double().cpu().numpy(), oracle_full(wl), wl.dtype,
                         f"round {rnd} case {i}")
-    assert int(ws[: 1 << 20].count_nonzero()) == 0  # report counters left at zero
+    assert int(ws[: 4 << 20].count_nonzero()) == 0  # report counters left at zero
 
 
 def test_graph_replay_matches_eager():
