@@ -60,18 +60,25 @@ extern "C" {
 
 #define PKA_ABI_VERSION 8
 
+/* Both enums are 32-bit codes.  The *_RANGE_* members are not values to
+ * pass: they make every int32 a value of the type, so that a code the
+ * library does not know (reported as such) is still a defined value. */
 typedef enum pka_status {
     PKA_OK = 0,
     PKA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, shape or alignment */
     PKA_ERR_UNSUPPORTED = 2,        /* valid but outside the compiled set */
     PKA_ERR_WORKSPACE_TOO_SMALL = 3,
-    PKA_ERR_HIP = 4                 /* the HIP runtime reported an error */
+    PKA_ERR_HIP = 4,                /* the HIP runtime reported an error */
+    PKA_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+    PKA_STATUS_RANGE_MAX_ = 0x7fffffff
 } pka_status;
 
 typedef enum pka_dtype {
     PKA_F32 = 0,
     PKA_F16 = 1,   /* IEEE binary16 */
-    PKA_BF16 = 2   /* bfloat16 */
+    PKA_BF16 = 2,  /* bfloat16 */
+    PKA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+    PKA_DTYPE_RANGE_MAX_ = 0x7fffffff
 } pka_dtype;
 
 /*
@@ -437,7 +444,9 @@ int32_t pka_decode_int8_partition_size(int32_t num_seqs, int32_t num_kv_heads,
  * pka_decode_int8_workspace_bytes -- device scratch of the INT8 decode for
  * these shapes and this (resolved) partition length; 0 when every sequence
  * fits one partition.  The workspace needs no initialisation: each call
- * writes everything it reads.
+ * writes everything it reads.  Its first 4 MiB are left untouched, so one
+ * buffer (zero-filled once) can also serve as the workspace of
+ * pka_paged_attention_decode, whose report counters live there.
  */
 size_t pka_decode_int8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                        int32_t max_context_len, int32_t partition_size);

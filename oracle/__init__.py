@@ -41,16 +41,25 @@ class OracleError(RuntimeError):
     pass
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so next to it (gcc, -O2, OpenMP)."""
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall",
+# gcc flags of the sanitizer build: AddressSanitizer and UndefinedBehavior-
+# Sanitizer, every finding fatal (the process must load libasan first).
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(force: bool = True, path: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, -O2, OpenMP), or
+    into ``path``; ``sanitize`` builds with SANITIZE_FLAGS instead of -O2."""
+    out = path or _LIB_PATH
+    if not force and os.path.exists(out):
+        return out
+    tmp = out + ".tmp"
+    opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall",
            "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -61,6 +70,9 @@ def lib(path: Optional[str] = None):
     global _lib
     if path is not None:
         return _declare(ctypes.CDLL(path))
+    if _lib is None and os.environ.get("ORACLE_LIBRARY"):
+        # another build of oracle.c (the sanitizer build of the tests)
+        _lib = _declare(ctypes.CDLL(os.environ["ORACLE_LIBRARY"]))
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()

@@ -151,6 +151,75 @@ def _check(status: int):
         raise PkaError(status, f"pka: {name}: {detail}")
 
 
+PKA_ERR_INVALID_ARGUMENT = 1
+
+
+def _invalid(msg: str):
+    raise PkaError(PKA_ERR_INVALID_ARGUMENT, f"pka: invalid argument (validate=True): {msg}")
+
+
+def _first(mask) -> tuple:
+    import torch
+
+    return tuple(int(x) for x in torch.nonzero(mask)[0])
+
+
+def _validate_tables(block_tables, context_lens, num_blocks: int, block_size: int, hint: int = 0):
+    """The device-data checks behind ``validate=True`` (they synchronise the
+    stream): every length within the block table (and within the host hint
+    when one is given), and every block-table entry a length uses inside
+    [0, num_blocks).  The kernels clamp such inputs instead of failing."""
+    import torch
+
+    L = context_lens.to(torch.int64)
+    if L.numel() == 0:
+        return
+    MB = block_tables.shape[1]
+    cap = MB * block_size
+    if bool((L > cap).any()):
+        (b,) = _first(L > cap)
+        _invalid(f"context_lens[{b}] = {int(L[b])} exceeds the table ({MB} blocks of {block_size})")
+    if hint > 0 and bool((L > hint).any()):
+        (b,) = _first(L > hint)
+        _invalid(f"context_lens[{b}] = {int(L[b])} exceeds max_context_len = {hint}")
+    used = (L.clamp(min=0) + block_size - 1) // block_size
+    col = torch.arange(MB, device=L.device)
+    bad = (col[None, :] < used[:, None]) & ((block_tables < 0) | (block_tables >= num_blocks))
+    if bool(bad.any()):
+        b, j = _first(bad)
+        _invalid(f"block_tables[{b}, {j}] = {int(block_tables[b, j])} is outside [0, {num_blocks})")
+
+
+def _validate_slots(slot_mapping, num_slots: int, block_tables=None, context_lens=None,
+                    block_size: int = 0):
+    """Stored slots (those inside the pool) must be distinct; with a block
+    table, a slot stored for the last position of a sequence must not be
+    one the same call reads for another position of any sequence."""
+    import torch
+
+    s = slot_mapping.to(torch.int64)
+    store = (s >= 0) & (s < num_slots)
+    if context_lens is not None:
+        store &= context_lens.to(torch.int64) > 0
+    st = s[store]
+    if st.numel() != torch.unique(st).numel():
+        _invalid("slot_mapping stores two tokens in one slot")
+    if block_tables is None or st.numel() == 0:
+        return
+    L = context_lens.to(torch.int64).clamp(min=0)
+    n_read = (L - 1).clamp(min=0)
+    total = int(n_read.sum())
+    if total == 0:
+        return
+    dev = L.device
+    bi = torch.repeat_interleave(torch.arange(L.numel(), device=dev), n_read)
+    start = torch.cumsum(n_read, 0) - n_read
+    t = torch.arange(total, device=dev) - start[bi]
+    read = block_tables[bi, t // block_size].to(torch.int64) * block_size + t % block_size
+    if bool(torch.isin(st, read).any()):
+        _invalid("a slot in slot_mapping is also read for another position")
+
+
 def _dtype_code(dt) -> int:
     import torch
 
@@ -176,11 +245,13 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be on the same device")
 
 
-def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
+def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, *, validate: bool = False) -> None:
     """Store k, v [T, Hkv, D] into the pools at slot_mapping (int64 [T]).
 
     Slot s addresses block s // block_size, offset s % block_size; negative
     slots are skipped.  Bit-exact copy; mutates k_cache and v_cache.
+    ``validate=True`` first checks on the device (synchronising) that the
+    stored slots are distinct, and raises PkaError otherwise.
     """
     import torch
 
@@ -202,6 +273,8 @@ def kv_cache_write(k, v, slot_mapping, k_cache, v_cache) -> None:
         raise ValueError("slot_mapping must be int64 [T] with T = k.shape[0] = v.shape[0]")
     slot_mapping = slot_mapping.contiguous()
     T = k.shape[0]
+    if validate:
+        _validate_slots(slot_mapping, NB * bs)
     lib = load_library()
     _check(lib.pka_kv_cache_write(
         k.data_ptr(), v.data_ptr(), k.stride(0) if T else Hkv * D, v.stride(0) if T else Hkv * D,
@@ -277,7 +350,7 @@ def _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                            num_kv_heads: int, block_size: int, *, out=None, out_dtype=None,
                            partition_size: int = 0, max_context_len: int = 0,
-                           workspace=None):
+                           workspace=None, validate: bool = False):
     """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache.
 
     q [B, Hq, D] (the KV dtype); pools [NB, Hkv, bs, D]; block_tables int32
@@ -286,12 +359,16 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     is an optional host hint (no device sync); ``partition_size`` 0 lets the
     library choose.  ``workspace`` (uint8 device tensor, zero-filled before
     its first use; each call leaves it reusable) defaults to a cached one per
-    device.
+    device.  ``validate=True`` first checks the device data (synchronising):
+    every length within the block table and within ``max_context_len`` when
+    given, every block id a length uses inside the pool; PkaError otherwise.
     """
     a = _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                       block_size, out, out_dtype, partition_size, max_context_len, workspace)
     if a["B"] == 0:
         return a["out"]
+    if validate:
+        _validate_tables(a["block_tables"], a["context_lens"], a["NB"], a["bs"], max_context_len)
     lib = load_library()
     _check(lib.pka_paged_attention_decode(
         a["out"].data_ptr(), _dtype_code(a["out"].dtype), a["q"].data_ptr(), k_cache.data_ptr(),
@@ -329,12 +406,14 @@ def paged_attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cach
                                   context_lens, scale: float, num_kv_heads: int,
                                   block_size: int, *, out=None, out_dtype=None,
                                   partition_size: int = 0, max_context_len: int = 0,
-                                  workspace=None):
+                                  workspace=None, validate: bool = False):
     """One fused decode step: store each sequence's new token (k_new[b],
     v_new[b], [B, Hkv, D]) at slot_mapping[b] (int64 [B]) and attend over
     its L_b tokens, the last of which is that new token.  Equal, bit for bit,
     to kv_cache_write followed by paged_attention_decode when slot_mapping[b]
-    is the slot of position L_b - 1.  Mutates the pools; returns out."""
+    is the slot of position L_b - 1.  Mutates the pools; returns out.
+    ``validate=True``: the checks of paged_attention_decode, plus distinct
+    stored slots, none of them read for another position by this call."""
     import torch
 
     a = _decode_setup(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
@@ -353,6 +432,10 @@ def paged_attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cach
     slot_mapping = slot_mapping.contiguous()
     if B == 0:
         return a["out"]
+    if validate:
+        _validate_tables(a["block_tables"], a["context_lens"], a["NB"], a["bs"], max_context_len)
+        _validate_slots(slot_mapping, a["NB"] * a["bs"], a["block_tables"], a["context_lens"],
+                        a["bs"])
     lib = load_library()
     _check(lib.pka_paged_attention_decode_append(
         a["out"].data_ptr(), _dtype_code(a["out"].dtype), a["q"].data_ptr(), k_new.data_ptr(),
@@ -366,14 +449,17 @@ def paged_attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cach
 
 def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start,
                             scale: float, num_kv_heads: int, block_size: int, *, out=None,
-                            out_dtype=None, max_query_len: int = 0):
+                            out_dtype=None, max_query_len: int = 0, validate: bool = False):
     """Multi-token causal attention: q [N, Hq, D] holds the new tokens of all
     sequences, sequence b owning rows query_start[b] .. query_start[b+1] - 1
     (int32 [B + 1]); their K/V are already in the pools and context_lens[b]
     counts them, so new token i of sequence b sits at position
     context_lens[b] - T_b + i and attends to positions 0 .. that one.
     max_query_len, an upper bound of T_b, sizes the grid (0: N).  Returns
-    out [N, Hq, D]."""
+    out [N, Hq, D].  ``validate=True`` first checks the device data
+    (synchronising): query_start non-decreasing from 0 to N, T_b <= L_b,
+    T_b <= max_query_len when given, and the decode's table checks;
+    PkaError otherwise."""
     import torch
 
     _require_gpu(q, k_cache, v_cache, block_tables, context_lens, query_start)
@@ -408,6 +494,19 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
         raise ValueError("out must be a contiguous [N, Hq, D] tensor on q's device")
     if B == 0 or N == 0:
         return out
+    if validate:
+        qs = query_start.to(torch.int64)
+        if int(qs[0]) != 0 or int(qs[-1]) != N or bool((qs[1:] < qs[:-1]).any()):
+            _invalid(f"query_start must run non-decreasing from 0 to {N}")
+        T = qs[1:] - qs[:-1]
+        L = context_lens.to(torch.int64)
+        if bool((T > L).any()):
+            (b,) = _first(T > L)
+            _invalid(f"sequence {b} has {int(T[b])} new tokens but context_lens {int(L[b])}")
+        if max_query_len > 0 and bool((T > max_query_len).any()):
+            (b,) = _first(T > max_query_len)
+            _invalid(f"sequence {b} has {int(T[b])} new tokens, max_query_len = {max_query_len}")
+        _validate_tables(block_tables, context_lens, NB, bs)
     lib = load_library()
     _check(lib.pka_paged_attention_prefill(
         out.data_ptr(), _dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
@@ -684,7 +783,8 @@ def paged_attention_decode_append_int8(q, k_new, v_new, slot_mapping, k_codes, v
                                        v_scales, block_tables, context_lens, scale: float,
                                        num_kv_heads: int, block_size: int, *, out=None,
                                        out_dtype=None, partition_size: int = 0,
-                                       max_context_len: int = 0, workspace=None):
+                                       max_context_len: int = 0, workspace=None,
+                                       validate: bool = False):
     """One fused INT8 decode step: quantise and store each sequence's new
     token (k_new[b], v_new[b], [B, Hkv, D] in q's dtype) at slot_mapping[b]
     (int64 [B], the slot of position L_b - 1) and attend over its L_b tokens;
@@ -707,18 +807,21 @@ def paged_attention_decode_append_int8(q, k_new, v_new, slot_mapping, k_codes, v
     return paged_attention_decode_int8(
         q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, scale, num_kv_heads,
         block_size, out=out, out_dtype=out_dtype, partition_size=partition_size,
-        max_context_len=max_context_len, workspace=workspace,
+        max_context_len=max_context_len, workspace=workspace, validate=validate,
         _append=(k_new, v_new, slot_mapping.contiguous()))
 
 
 def paged_attention_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_tables,
                                 context_lens, scale: float, num_kv_heads: int, block_size: int,
                                 *, out=None, out_dtype=None, partition_size: int = 0,
-                                max_context_len: int = 0, workspace=None, _append=None):
+                                max_context_len: int = 0, workspace=None, validate: bool = False,
+                                _append=None):
     """out[b, hq] = softmax(scale * q[b, hq] . K^T) V over sequence b's cache,
     K and V being code * scale of the INT8 pools.  q [B, Hq, D] float16 or
     bfloat16; returns out [B, Hq, D] (float32 unless ``out_dtype`` or ``out``
-    says q's dtype).  Other arguments as for paged_attention_decode; the
+    says q's dtype).  Other arguments, ``validate`` included, as for
+    paged_attention_decode (lengths beyond ``max_context_len`` are cut short
+    by this kernel, so there validation catches an undersized hint); the
     workspace needs no initialisation."""
     import torch
 
@@ -745,6 +848,10 @@ def paged_attention_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_t
         raise ValueError("out must be a contiguous [B, Hq, D] tensor on q's device")
     if B == 0:
         return out
+    if validate:
+        _validate_tables(block_tables, context_lens, NB, bs, max_context_len)
+        if _append is not None:
+            _validate_slots(_append[2], NB * bs, block_tables, context_lens, bs)
     hint = max_context_len if max_context_len > 0 else MB * bs
     hint = min(hint, MB * bs)
     P = partition_size if partition_size > 0 else decode_int8_partition_size(B, Hkv, bs, hint)

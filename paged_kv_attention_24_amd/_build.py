@@ -81,6 +81,49 @@ def build(verbose: bool = False, extra_flags=(), variant: str | None = None,
     return lib_path
 
 
+# Host-side sanitizers for the C ABI layer: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host pass only (the device code is built
+# as usual), every finding fatal.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                 "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(PKG, "libpka_sanitized.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libpka_sanitized.so: abi.cpp (argument checks, sizing, dispatch) with
+    host sanitizers, linked with the kernel objects of the regular build
+    (built first if missing).  Load it with PKA_LIBRARY=libpka_sanitized.so
+    and clang's ASan runtime preloaded."""
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    san_dir = os.path.join(BUILD_DIR, "sanitized")
+    os.makedirs(san_dir, exist_ok=True)
+    abi_obj = os.path.join(san_dir, "abi.o")
+    cmd = [HIPCC, "-x", "hip", *[f for f in COMMON if f != "-O3"], "-O1", "-g", *SANITIZE_HOST,
+           "-c", os.path.join(CSRC, "abi.cpp"), "-o", abi_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host",
+            "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", abi_obj,
+            *[o for o in objs if not o.endswith("abi.o")], "-o", SANITIZED_LIB + ".tmp"]
+    subprocess.run(link, check=True, capture_output=not verbose)
+    os.replace(SANITIZED_LIB + ".tmp", SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
+def asan_runtime() -> str:
+    """clang's ASan runtime that a process loading the sanitized library
+    must preload (empty when absent)."""
+    import glob
+
+    root = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+    hits = sorted(glob.glob(os.path.join(root, "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else ""
+
+
 def clean():
     shutil.rmtree(BUILD_DIR, ignore_errors=True)
 

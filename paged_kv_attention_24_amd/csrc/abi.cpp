@@ -82,6 +82,7 @@ const char *pka_status_string(pka_status s)
     case PKA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PKA_ERR_HIP: return "HIP runtime error";
+    default: break;
     }
     return "unknown status";
 }
@@ -583,8 +584,10 @@ pka::Int8WorkspaceLayout pka::int8_workspace_layout(int64_t num_seqs, int64_t nu
     if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_partitions <= 1)
         return w;
     const int64_t rows = num_seqs * num_q_heads * num_partitions;
-    w.header_offset = 0;
-    w.items_offset = 256;
+    // the first kCounterBytes stay untouched: there the fp16/bf16/fp32 decode
+    // keeps counters that must read zero, so one buffer can serve both decodes
+    w.header_offset = (size_t)kCounterBytes;
+    w.items_offset = w.header_offset + 256;
     w.ml_offset = w.items_offset + (size_t)round256(num_seqs * num_partitions * 8);
     w.o_offset = w.ml_offset + (size_t)round256(rows * 2 * 4);
     w.total = w.o_offset + (size_t)round256(rows * head_dim * 4);

@@ -66,26 +66,15 @@ namespace pka {
 namespace {
 
 constexpr int kI8Waves = 4;             // waves (independent units) per workgroup
-#ifndef PKA_I8_TILES
-#define PKA_I8_TILES 2
-#endif
-#ifndef PKA_I8_PREFETCH
-#define PKA_I8_PREFETCH 0
-#endif
-constexpr int kI8Tiles = PKA_I8_TILES;        // 16-token tiles per step
+constexpr int kI8Tiles = 2;                   // 16-token tiles per step
 constexpr int kI8Step = 16 * kI8Tiles;        // tokens per step
-constexpr bool kI8Prefetch = PKA_I8_PREFETCH != 0;  // next step's loads in flight
 constexpr int kI8PlanThreads = 1024;    // planning workgroup
 // Up to this many partitions per sequence the decode launches one wave per
 // (sequence, partition, kv head) and no planning launch.
 constexpr int kI8DenseMaxPartitions = 8;
-#ifndef PKA_I8_GROUP_MERGE
-#define PKA_I8_GROUP_MERGE 1
-#endif
 // With 2..kI8DenseMaxPartitions partitions, one workgroup per (sequence, kv
 // head) whose wave w takes partition w merges the partitions' rows in LDS
 // (no merge launch, no partial rows in HBM).
-constexpr bool kI8GroupMerge = PKA_I8_GROUP_MERGE != 0;
 // Persistent grids over at most this many sequences plan their work in each
 // workgroup's LDS (a prefix of partition counts) instead of a planning launch.
 constexpr int kI8PlanInKernelSeqs = 4096;
@@ -630,6 +619,11 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
     st.m = -INFINITY;
     st.l = 0.0f;
     const bool stored = appending && slot >= 0 && slot < (int64_t)a.num_blocks * BS;
+    // The new token is position L - 1 only when its length was not cut short
+    // (a host hint below the real length): only then do the registers take
+    // it; otherwise the row is stored and positions 0 .. L - 1 come from the
+    // pool, as in a write followed by a decode.
+    const bool patched = stored && a.context_lens[b] == L;
     int8_t ck[E], cv[E];
     float new_ks = 0.0f, new_vs = 0.0f;  // this lane's group's scales of the new rows
     if (stored) {
@@ -655,7 +649,7 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
                 for (int e = 0; e < 4; ++e) {
                     const int flat = 4 * k4 + e;
                     // position L - 1 of an appending unit: its new scale below
-                    const bool valid = t0 + flat / NG < (stored ? t_end - 1 : t_end);
+                    const bool valid = t0 + flat / NG < (patched ? t_end - 1 : t_end);
                     sig[flat % NG] = fmaxf(sig[flat % NG], valid ? f4(v, e) : 0.0f);
                 }
             }
@@ -663,7 +657,7 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             float m = wave_max(sig[g]);
-            if (stored)  // the lanes of group g hold its scale: lane g * GS / (D / 64)
+            if (patched)  // the lanes of group g hold its scale: lane g * GS / (D / 64)
                 m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                            __builtin_bit_cast(int, new_vs),
                                                            g * GS / (D / kWave))));
@@ -686,46 +680,22 @@ __device__ __forceinline__ void run_unit(const Int8DecodeArgs &a, int b, int jp,
     // the step starting at ts holds position L - 1: its registers get the
     // new token
     auto patch = [&](StepRegs<D, D / GS> &R, int ts) __attribute__((always_inline)) {
-        if (stored && ts <= L - 1 && L - 1 < ts + kI8Step)
+        if (patched && ts <= L - 1 && L - 1 < ts + kI8Step)
             patch_new_token<D, GS>(R, L - 1 - ts, new_kc, new_vc, new_ks, new_vs, lane);
     };
-    if constexpr (kI8Prefetch) {
-        // Two register sets take turns: the step after the one computed is
-        // always in flight.  Past the last step the prefetch repeats the
-        // last step's loads (never used), keeping the loads unconditional.
-        const int t_last = t_begin + (t_end - 1 - t_begin) / kI8Step * kI8Step;
-        StepRegs<D, D / GS> A, B;
-        load_step<D, BS, GS>(a, A, ids, t_begin, t_begin, t_end, h, lane);
-        int ts = t_begin;
-        for (;;) {
-            load_step<D, BS, GS>(a, B, ids, t_begin, min(ts + kI8Step, t_last), t_end, h, lane);
-            patch(A, ts);
-            compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
-            ts += kI8Step;
-            if (ts > t_last)
-                break;
-            load_step<D, BS, GS>(a, A, ids, t_begin, min(ts + kI8Step, t_last), t_end, h, lane);
-            patch(B, ts);
-            compute_step<D, BS, GS, false>(B, st, qf, qmul, ts, t_end, lane);
-            ts += kI8Step;
-            if (ts > t_last)
-                break;
-        }
-    } else {
-        // One step in flight per wave; the waves resident on a compute unit
-        // overlap each other's loads and arithmetic.
-        StepRegs<D, D / GS> A;
-        int ts = t_begin;
-        for (; ts + kI8Step <= t_end; ts += kI8Step) {
-            load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
-            patch(A, ts);
-            compute_step<D, BS, GS, true>(A, st, qf, qmul, ts, t_end, lane);
-        }
-        if (ts < t_end) {
-            load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
-            patch(A, ts);
-            compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
-        }
+    // One step in flight per wave; the waves resident on a compute unit
+    // overlap each other's loads and arithmetic.
+    StepRegs<D, D / GS> A;
+    int ts = t_begin;
+    for (; ts + kI8Step <= t_end; ts += kI8Step) {
+        load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
+        patch(A, ts);
+        compute_step<D, BS, GS, true>(A, st, qf, qmul, ts, t_end, lane);
+    }
+    if (ts < t_end) {
+        load_step<D, BS, GS>(a, A, ids, t_begin, ts, t_end, h, lane);
+        patch(A, ts);
+        compute_step<D, BS, GS, false>(A, st, qf, qmul, ts, t_end, lane);
     }
 
     const float l = column_sum(st.l);
@@ -1059,7 +1029,7 @@ int compute_units()
 template <class QT, int D, int BS, int G, int GS, bool APPEND>
 hipError_t launch_decode_t(const Int8DecodeArgs &a, hipStream_t stream)
 {
-    if (kI8GroupMerge && a.num_partitions > 1 && a.num_partitions <= kI8DenseMaxPartitions) {
+    if (a.num_partitions > 1 && a.num_partitions <= kI8DenseMaxPartitions) {
         const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads;
         if (groups > 0x7fffffff)
             return hipErrorInvalidValue;

@@ -132,8 +132,10 @@ struct BlockMoveArgs {
 
 hipError_t launch_move_blocks(const BlockMoveArgs &a, hipStream_t stream);
 
-// Group-quantised INT8 pools: k_codes [NB][Hkv][BS][D], v_codes
-// [NB][Hkv][D][BS], k_scales / v_scales f32 [NB][Hkv][BS][D / group_size].
+// Group-quantised INT8 pools: k_codes, v_codes int8 [NB][Hkv][BS * D] (each
+// block's run of codes in 16-token tiles, ordered as the matrix-core
+// products read them; the order is spelled out in pka.h), k_scales /
+// v_scales f32 [NB][Hkv][BS][D / group_size].
 struct Int8WriteArgs {
     const void *k, *v;
     int64_t k_token_stride, v_token_stride;  // elements

@@ -374,8 +374,9 @@ def test_int8_workspace_and_partition_helpers():
     assert lib.pka_decode_int8_partition_size(16, 8, 16, 1024) == 128
     assert lib.pka_decode_int8_workspace_bytes(4, 32, 64, 512, 512) == 0
     n = lib.pka_decode_int8_workspace_bytes(4, 32, 64, 1024, 256)
-    # header + items + (max, sum) rows + output rows, each 256-aligned
-    assert n == 256 + 256 + 4096 + 4 * 32 * 4 * 64 * 4
+    # 4 MiB left to the fp16/bf16 decode's counters, then header + items +
+    # (max, sum) rows + output rows, each 256-aligned
+    assert n == (4 << 20) + 256 + 256 + 4096 + 4 * 32 * 4 * 64 * 4
 
 
 @fake_pointers

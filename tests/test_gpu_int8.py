@@ -283,36 +283,117 @@ def test_large_dynamic_range_of_scales():
     assert float(rel.max()) <= 2e-3
 
 
-@pytest.mark.parametrize("P", [0, 320, 32, 16])
-@pytest.mark.parametrize("q_dtype,D,gs", [("f16", 64, 32), ("bf16", 128, 64)])
-def test_fused_append_equals_write_then_decode(P, q_dtype, D, gs):
-    """The fused step (quantise and store the new token, then attend) leaves
-    the pools and the output bit-identical to the write followed by the
-    decode, in each launch mode; a negative slot stores nothing."""
+FUSED_SHAPES = [("f16", 64, 32, 16, 4), ("bf16", 128, 64, 16, 4), ("f16", 128, 32, 16, 8),
+                ("bf16", 64, 64, 32, 1), ("f16", 64, 64, 32, 2), ("bf16", 128, 32, 32, 8)]
+FUSED_CASES = [s + (P,) for s in FUSED_SHAPES for P in (0, 320, 32, s[3])]
+
+
+def _fused_vs_write_then_decode(wl, P, hint=0):
+    """Run the write followed by the decode, and the fused step, on two
+    copies of the workload; return (reference out, fused out) after checking
+    that both leave the four pool arrays bit-identical."""
     import torch
 
     import paged_kv_attention_24_amd as pka
 
-    wl = W.make_int8_case(90 + D + P, q_dtype=q_dtype, context_lens=(3, 70, 129, 17, 0, 300),
-                          num_q_heads=4 * 2, num_kv_heads=2, head_dim=D, block_size=16,
-                          group_size=gs, poison=False)
-    wl.slot_mapping[3] = -1  # padding: nothing stored, position L - 1 read as it is
     d1 = W.int8_device_inputs(wl)
     d2 = W.int8_device_inputs(wl)
     names = ("k_codes", "v_codes", "k_scales", "v_scales")
+    Hkv, bs = wl.num_kv_heads, wl.block_size
     pka.kv_cache_write_int8(d1["new_k"], d1["new_v"], d1["slot_mapping"], *(d1[n] for n in names))
     ref = pka.paged_attention_decode_int8(d1["q"], *(d1[n] for n in names), d1["block_tables"],
-                                          d1["context_lens"], float(wl.scale), 2, 16,
-                                          partition_size=P)
+                                          d1["context_lens"], float(wl.scale), Hkv, bs,
+                                          partition_size=P, max_context_len=hint)
     got = pka.paged_attention_decode_append_int8(
         d2["q"], d2["new_k"], d2["new_v"], d2["slot_mapping"], *(d2[n] for n in names),
-        d2["block_tables"], d2["context_lens"], float(wl.scale), 2, 16, partition_size=P)
+        d2["block_tables"], d2["context_lens"], float(wl.scale), Hkv, bs, partition_size=P,
+        max_context_len=hint)
     torch.cuda.synchronize()
     for n in names:
         assert torch.equal(d1[n], d2[n]), n
+    return ref, got
+
+
+@pytest.mark.parametrize("q_dtype,D,gs,bs,G,P", FUSED_CASES)
+def test_fused_append_equals_write_then_decode(q_dtype, D, gs, bs, G, P):
+    """The fused step (quantise and store the new token, then attend) leaves
+    the pools and the output bit-identical to the write followed by the
+    decode, in each launch mode (one partition, workgroup merge, persistent
+    grid), for 1, 2 or 4 scale groups per row; a negative slot stores
+    nothing."""
+    import torch
+
+    wl = W.make_int8_case(90 + D + P + bs + G, q_dtype=q_dtype,
+                          context_lens=(3, 70, 129, 17, 0, 300), num_q_heads=G * 2,
+                          num_kv_heads=2, head_dim=D, block_size=bs, group_size=gs, poison=False)
+    wl.slot_mapping[3] = -1  # padding: nothing stored, position L - 1 read as it is
+    print(f"[int8] fused {q_dtype} D={D} gs={gs} bs={bs} G={G} P={P}", flush=True)
+    ref, got = _fused_vs_write_then_decode(wl, P)
     assert torch.equal(ref, got)
     pools = [a.copy() for a in (wl.k_codes, wl.v_codes, wl.k_scales, wl.v_scales)]
     oracle.kv_cache_write_int8(wl.new_k, wl.new_v, wl.slot_mapping, *pools, wl.dtype)
     want = oracle.paged_attention_decode_int8(wl.q, wl.dtype, *pools, wl.block_tables,
-                                              wl.context_lens, wl.scale, 2, 16)
+                                              wl.context_lens, wl.scale, 2, bs)
     check(got.double().cpu().numpy(), want, "fused append")
+
+
+def test_fused_append_many_sequences_planned():
+    """4500 sequences with 16-token partitions: the persistent grid with its
+    planning launch; the fused step equals the write followed by the
+    decode."""
+    import torch
+
+    rng = np.random.default_rng(45)
+    lens = [int(x) for x in rng.integers(0, 200, size=4500)]
+    lens[4499] = 700
+    wl = W.make_int8_case(45, q_dtype="bf16", context_lens=lens, num_q_heads=8, num_kv_heads=2,
+                          head_dim=64, block_size=16, group_size=32, poison=False)
+    print("[int8] fused, 4500 sequences, P=16", flush=True)
+    ref, got = _fused_vs_write_then_decode(wl, 16)
+    assert torch.equal(ref, got)
+
+
+@pytest.mark.parametrize("P", [0, 32])
+def test_fused_append_with_short_hint(P):
+    """A max_context_len hint below some lengths cuts those sequences short
+    in this kernel; the fused step must still equal the write followed by
+    the decode with the same hint (the new row is stored, and positions
+    0 .. hint - 1 come from the pool)."""
+    import torch
+
+    wl = W.make_int8_case(46, q_dtype="f16", context_lens=(3, 70, 129, 17, 300),
+                          num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                          group_size=32, poison=False)
+    print(f"[int8] fused with hint 96, P={P}", flush=True)
+    ref, got = _fused_vs_write_then_decode(wl, P, hint=96)
+    assert torch.equal(ref, got)
+
+
+def test_one_buffer_serves_both_decodes():
+    """A zero-filled buffer used first by a multi-partition INT8 decode and
+    then as the fp16 decode's workspace: the INT8 decode leaves the fp16
+    decode's counters alone, so the fp16 result is still correct."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+    from gpu_util import check_close, gpu_decode  # noqa: F401
+
+    wl8 = case(47, "f16", [700, 40, 1300], 8, 2, 64, 16, 32)
+    need8 = pka.decode_int8_workspace_bytes(3, 8, 64, 1300, 64)
+    wl = W.make_case(48, dtype="f16", context_lens=[900, 33, 2000, 5], num_q_heads=8,
+                     num_kv_heads=2, head_dim=64, block_size=16)
+    need = pka.decode_workspace_bytes(4, 8, 2, 64)
+    ws = torch.zeros(max(need8, need), dtype=torch.uint8, device="cuda")
+    d8 = W.int8_device_inputs(wl8)
+    print("[int8] shared workspace: INT8 decode, then fp16 decode", flush=True)
+    got8 = pka.paged_attention_decode_int8(
+        d8["q"], d8["k_codes"], d8["v_codes"], d8["k_scales"], d8["v_scales"],
+        d8["block_tables"], d8["context_lens"], float(wl8.scale), 2, 16, partition_size=64,
+        max_context_len=1300, workspace=ws)
+    d = W.device_inputs(wl)
+    pka.kv_cache_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+    got = pka.paged_attention_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], float(wl.scale), 2, 16, workspace=ws)
+    torch.cuda.synchronize()
+    check(got8.double().cpu().numpy(), oracle_int8(wl8), "int8 on a shared buffer")
+    check_close(got.double().cpu().numpy(), oracle.decode_workload(wl), "f16", "shared buffer")
