@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--path", default="decode",
-                    choices=["decode", "prefill", "blocks", "rope", "int8"],
+                    choices=["decode", "prefill", "blocks", "rope", "int8", "stream"],
                     help="decode step (the headline), multi-token causal attention, or "
                          "whole-block moves (preemption, paging), the RoPE write, or the "
                          "decode over group-quantised INT8 pools")
@@ -64,6 +64,11 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a HIP graph")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="override the library's partition length (tokens)")
+    ap.add_argument("--extra-configs", default="3,4,5",
+                    help="decode workloads timed after the headline one (config 2 only), "
+                         "each reported under configs.<n>; 'none' to skip")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the HBM read ceilings (csrc/calibrate.hip)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one torch copy of this many MiB first (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -133,7 +138,6 @@ def main():
     import torch
 
     import paged_kv_attention_24_amd as pka
-    from paged_kv_attention_24_amd import workloads as W
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
@@ -148,14 +152,175 @@ def main():
         return run_rope(args, dev)
     if args.path == "int8":
         return run_int8(args, dev)
+    if args.path == "stream":
+        return run_stream(args, dev)
 
-    cfg = args.config
+    line = decode_line(args, dev)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+
+
+def load_calibration():
+    import ctypes
+
+    path = os.path.join(HERE, "paged_kv_attention_24_amd", "libpka_calib.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build with python -m paged_kv_attention_24_amd._build")
+    lib = ctypes.CDLL(path)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.pka_calib_stream_read.argtypes = [P, i64, P, i32, P]
+    lib.pka_calib_stream_read.restype = i32
+    lib.pka_calib_gather_read.argtypes = [P, P, i64, i32, P, i32, P]
+    lib.pka_calib_gather_read.restype = i32
+    return lib
+
+
+def measure_ceilings(dev, reps=8, gib=4):
+    """HBM read ceilings of this GPU (csrc/calibrate.hip): one contiguous read
+    of a buffer far larger than the 256 MB MALL, and a gather of its 4 KiB
+    tiles in random order (the access pattern of a block-table walk over a
+    shuffled pool).  GB/s of bytes read."""
+    import torch
+
+    lib = load_calibration()
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count * 8
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    tile = 4096
+    n_tiles = nbytes // tile
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    order = torch.randperm(n_tiles, generator=gen, device=dev).to(torch.int32)
+
+    def run_stream():
+        if lib.pka_calib_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream):
+            raise RuntimeError("stream-read launch failed")
+
+    def run_gather():
+        if lib.pka_calib_gather_read(buf.data_ptr(), order.data_ptr(), n_tiles, tile,
+                                     sink.data_ptr(), grid, stream):
+            raise RuntimeError("gather-read launch failed")
+
+    res = {}
+    for name, fn in (("stream_read", run_stream), ("gather_4KiB", run_gather)):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[f"{name}_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        res[f"{name}_us"] = round(ms * 1e3, 1)
+    res["buffer_GiB"] = gib
+    res["source"] = "bench.py measure_ceilings(): libpka_calib.so (csrc/calibrate.hip), HIP events"
+    del buf, order
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_stream(args, dev):
+    """--path stream: the read ceilings alone, as one JSON line."""
+    c = measure_ceilings(dev, reps=max(args.steps, 2))
+    line = {
+        "metric": "HBM read ceiling of a plain read-only kernel (calibration)",
+        "value": c["stream_read_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": max(args.steps, 2),
+        "warmup": 1, "ms_per_step": round(c["stream_read_us"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic (4 GiB of ones)",
+        "config": {"workload": f"contiguous read and random 4 KiB-tile gather of "
+                               f"{c['buffer_GiB']} GiB", "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100.0 * c["stream_read_GBps"] / HBM_PEAK_GBPS, 2),
+        "gather_4KiB_GBps": c["gather_4KiB_GBps"],
+        "roofline": {"bound": "hbm", "kernel": "stream_read (csrc/calibrate.hip)",
+                     "achieved": c["stream_read_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(c["stream_read_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def oracle_times(wl, kc_h, vc_h, *, full: bool, seconds: float, seed: int):
+    """The fp64 oracle on the host, with all threads and with one: a full
+    decode of one layer pool (full=True, repeated for about `seconds`), or a
+    sample of rows scaled to the whole batch by context length (the oracle's
+    work per row is proportional to it).  Returns (us all threads, us one
+    thread, threads, sample text)."""
+    import oracle
+
+    B, Hq = wl.num_seqs, wl.num_q_heads
+    L = wl.context_lens.astype(np.int64)
+    rows = None
+    scale_up = 1.0
+    if not full:
+        rng = np.random.default_rng(seed)
+        n = min(64, B * Hq)
+        pick = rng.choice(B * Hq, size=n, replace=False)
+        rows = np.stack([pick // Hq, pick % Hq], axis=1).astype(np.int32)
+        work = max(int(L[rows[:, 0]].sum()), 1)
+        scale_up = float(L.sum() * Hq) / work
+
+    def timed(threads, budget):
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention_decode(wl.q, kc_h, vc_h, wl.block_tables, wl.context_lens,
+                                          wl.scale, wl.num_kv_heads, wl.block_size, wl.dtype,
+                                          rows=rows, threads=threads)
+            n_done += 1
+            el = time.perf_counter() - t0
+            if el >= budget or n_done >= 256:
+                return el / n_done * 1e6 * scale_up, n_done, el
+
+    threads = host_threads()
+    us_all, n_all, el_all = timed(threads, seconds)
+    us_one, n_one, el_one = timed(1, seconds / 2)
+    what = (f"full decode of one layer pool ({B} seqs x {Hq} q-heads, {int(L.sum())} tokens)"
+            if full else f"{len(rows)} random (seq, q-head) rows, scaled to the batch by "
+                         f"context length (x{scale_up:.1f})")
+    sample = (f"{what}: {n_all} runs in {el_all:.1f} s on {threads} threads, {n_one} runs in "
+              f"{el_one:.1f} s on 1 thread; fp64 C oracle, OpenMP; host {cpu_model()}")
+    return us_all, us_one, threads, sample
+
+
+def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
+    """One workload's decode step (the fused new-token store + decode, one
+    launch per layer pool), timed cold over R layer pools that together
+    exceed the 256 MB MALL, and hot over pool 0 alone when it fits the MALL;
+    plus the same step as two launches per layer.  Returns a dict of
+    figures (and the workload)."""
+    import torch
+
+    import paged_kv_attention_24_amd as pka
+    from paged_kv_attention_24_amd import workloads as W
+
     host_pools = cfg in (2, 3)
     wl = W.make_config(cfg, pools=host_pools, poison=False)
     tdt = W.torch_dtype(wl.dtype)
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
     pool_bytes = 2 * wl.num_blocks * Hkv * bs * D * wl.elt_bytes
-    if args.layers > 0:
+    if headline and args.layers > 0:
         R = args.layers
     elif cfg == 2:
         R = 16
@@ -180,32 +345,31 @@ def main():
         else:
             kcs.append(fill_pool(shape, tdt, 1000 + 2 * r, dev))
             vcs.append(fill_pool(shape, tdt, 1001 + 2 * r, dev))
-    P = args.partition_size or wl.partition_size or \
+    P = (args.partition_size if headline else 0) or wl.partition_size or \
         pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
     ws_bytes = pka.decode_workspace_bytes(B, Hq, Hkv, D)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # counters start at 0
     outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]
     torch.cuda.synchronize()
 
-    def decode(r):
-        pka.paged_attention_decode(q, kcs[r], vcs[r], bt, cl, float(wl.scale), Hkv, bs,
-                                   out=outs[r], partition_size=P,
-                                   max_context_len=wl.max_context_len, workspace=ws)
+    def fused(r):
+        pka.paged_attention_decode_append(q, new_k, new_v, slots, kcs[r], vcs[r], bt, cl,
+                                          float(wl.scale), Hkv, bs, out=outs[r],
+                                          partition_size=P, max_context_len=wl.max_context_len,
+                                          workspace=ws)
 
     def step():  # one fused launch per layer: store the new tokens + decode
         for r in range(R):
-            pka.paged_attention_decode_append(q, new_k, new_v, slots, kcs[r], vcs[r], bt, cl,
-                                              float(wl.scale), Hkv, bs, out=outs[r],
-                                              partition_size=P,
-                                              max_context_len=wl.max_context_len,
-                                              workspace=ws)
+            fused(r)
 
     def step_two_launch():
         for r in range(R):
             pka.kv_cache_write(new_k, new_v, slots, kcs[r], vcs[r])
-            decode(r)
+            pka.paged_attention_decode(q, kcs[r], vcs[r], bt, cl, float(wl.scale), Hkv, bs,
+                                       out=outs[r], partition_size=P,
+                                       max_context_len=wl.max_context_len, workspace=ws)
 
-    if args.calibration_copy_mib > 0:
+    if headline and args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
         src_c = torch.ones(n, dtype=torch.uint8, device=dev)
         dst_c = torch.empty_like(src_c)
@@ -214,90 +378,139 @@ def main():
         torch.cuda.synchronize()
         del src_c, dst_c
 
-    for _ in range(max(1, args.warmup)):
+    for _ in range(max(1, warmup)):
         step()
     torch.cuda.synchronize()
-
-    def timed(fn, n, use_graph):
-        if use_graph:
-            g = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                fn()  # warm the capture stream
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                fn()
-            run = g.replay
-        else:
-            run = fn
-        for _ in range(max(1, args.warmup)):
-            run()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n  # ms per call of fn
-
     use_graph = not args.eager
     t_wall0 = time.perf_counter()
-    ms_step = timed(step, args.steps, use_graph)
+    ms_step = timed_calls(step, steps, warmup, use_graph)
     t_wall = time.perf_counter() - t_wall0
-    ms_two = timed(step_two_launch, args.steps, use_graph)
-    log(f"step {ms_step * 1e3:.1f} us ({R} fused launches), two-launch step "
-        f"{ms_two * 1e3:.1f} us; timed wall {t_wall:.2f} s")
+    ms_two = timed_calls(step_two_launch, steps, warmup, use_graph)
+    # hot: the same R launches, all on pool 0, so its K/V stay in the 256 MB MALL
+    hot_fits = pool_bytes <= 192e6
+
+    def step_hot():
+        for _ in range(R):
+            fused(0)
+
+    ms_hot = timed_calls(step_hot, steps, warmup, use_graph) / R if hot_fits else None
+    log(f"workload {cfg}: step {ms_step * 1e3:.1f} us ({R} fused launches), two-launch "
+        f"{ms_two * 1e3:.1f} us, hot {ms_hot * 1e3 if ms_hot else float('nan'):.1f} us; "
+        f"timed wall {t_wall:.2f} s")
 
     kv_bytes = wl.kv_bytes()
     us_per_layer = ms_step * 1e3 / R
-    value = kv_bytes * R / (ms_step * 1e-3) / 1e9  # GB/s over the whole step
     # one fused launch: algorithmic bytes = KV + q + out + block ids + lengths
     # + the new rows read and stored + the slots
     nblk = int(np.sum((wl.context_lens.astype(np.int64) + bs - 1) // bs))
     new_rows = B * Hkv * D * wl.elt_bytes * 2
     alg_bytes = kv_bytes + B * Hq * D * (wl.elt_bytes + 4) + nblk * 4 + B * 4 + 2 * new_rows + 8 * B
-    launches = 1  # one decode launch per layer (it combines its partial results itself)
-    us_launch = us_per_layer
-    achieved = alg_bytes / (us_launch * 1e-6) / 1e9
+    res = dict(wl=wl, R=R, P=int(P), use_graph=use_graph, kv_bytes=kv_bytes, alg_bytes=alg_bytes,
+               us_per_layer=us_per_layer, us_two=ms_two * 1e3 / R,
+               us_hot=ms_hot * 1e3 if ms_hot else None,
+               value=kv_bytes * R / (ms_step * 1e-3) / 1e9,
+               achieved=alg_bytes / (us_per_layer * 1e-6) / 1e9)
+    if ms_hot:
+        res["value_hot"] = kv_bytes / (ms_hot * 1e-3) / 1e9
+    if host_copy:  # for the oracle, timed after every GPU measurement
+        res["kc_h"] = W.to_numpy_bits(kcs[0], wl.dtype)
+        res["vc_h"] = W.to_numpy_bits(vcs[0], wl.dtype)
+    del kcs, vcs, outs, ws, d0
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_entry(m, cfg, ceilings, oracle_us=None):
+    """The per-workload figures of the bench line."""
+    wl = m["wl"]
+    e = {
+        "workload": wl.meta["description"],
+        "layers_per_step": m["R"],
+        "partition_size": m["P"],
+        "sum_context_tokens": int(wl.context_lens.sum()),
+        "us_per_layer": round(m["us_per_layer"], 3),
+        "us_per_layer_hot": round(m["us_hot"], 3) if m["us_hot"] else None,
+        "hot_note": ("the step's launches all on pool 0: its K/V stay resident in the 256 MB MALL"
+                     if m["us_hot"] else "one layer pool exceeds the 256 MB MALL: no hot figure"),
+        "us_per_layer_two_launch": round(m["us_two"], 3),
+        "effective_GBps": round(m["value"], 2),
+        "pct_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBPS, 2),
+        "launches_per_layer": 1,
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_kernel",
+            "achieved": round(m["achieved"], 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(m["achieved"] / HBM_PEAK_GBPS, 4),
+            "frac_of_stream_read": (round(m["achieved"] / ceilings["stream_read_GBps"], 4)
+                                    if ceilings else None),
+            "traffic": measured_traffic(PROFILE_TAGS[cfg], "decode"),
+            "traffic_source": f"profiles/{PROFILE_TAGS[cfg]}.md (rocprofv3 FETCH_SIZE + "
+                              "WRITE_SIZE, copy-calibrated; null when the kernel changed since)",
+            "algorithmic_bytes_per_launch": int(m["alg_bytes"]),
+        },
+    }
+    if m.get("value_hot"):
+        e["effective_GBps_hot"] = round(m["value_hot"], 2)
+    if oracle_us is not None:
+        e["oracle"] = oracle_us
+    return e
+
+
+def decode_line(args, dev):
+    cfg = args.config
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(dev)
+        log(f"read ceilings: {ceilings}")
+    want_cpu = not args.no_cpu_baseline
+    m = measure_decode(args, dev, cfg, steps=args.steps, warmup=args.warmup, headline=True,
+                       host_copy=want_cpu)
+    wl = m["wl"]
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+
+    extra_cfgs = [int(x) for x in args.extra_configs.split(",") if x.strip()] \
+        if args.extra_configs not in ("", "none") and cfg == 2 else []
+    measured = {}
+    for c in extra_cfgs:
+        measured[c] = measure_decode(args, dev, c,
+                                     steps=max(5, min(args.steps, 20 if c != 4 else 10)),
+                                     warmup=max(1, min(args.warmup, 3)), headline=False,
+                                     host_copy=want_cpu)
+    # every GPU measurement is done: the oracle's timings follow
+    extra = {}
+    for c, mc in measured.items():
+        o = None
+        if want_cpu:
+            us_all, us_one, threads, sample = oracle_times(mc["wl"], mc["kc_h"], mc["vc_h"],
+                                                           full=c == 3, seconds=3.0, seed=c)
+            o = {"us_all_cores": round(us_all, 1), "us_1core": round(us_one, 1),
+                 "cores": threads, "sample": sample}
+        extra[str(c)] = config_entry(mc, c, ceilings, o)
+    measured.clear()
 
     cpu = None
-    if not args.no_cpu_baseline and host_pools:
-        import oracle
-
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-        kc_h = W.to_numpy_bits(kcs[0], wl.dtype)
-        vc_h = W.to_numpy_bits(vcs[0], wl.dtype)
-        n_done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.paged_attention_decode(wl.q, kc_h, vc_h, wl.block_tables, wl.context_lens,
-                                          wl.scale, Hkv, bs, wl.dtype, threads=threads)
-            n_done += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or n_done >= 512:
-                break
+    if want_cpu:
+        us_all, us_one, threads, sample = oracle_times(wl, m["kc_h"], m["vc_h"], full=True,
+                                                       seconds=args.cpu_seconds, seed=cfg)
         cpu = {
-            "value": round(kv_bytes * n_done / el / 1e9, 4),
+            "value": round(m["kv_bytes"] / (us_all * 1e-6) / 1e9, 4),
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"full decode of one layer pool ({B} seqs x {Hq} q-heads, "
-                      f"{int(wl.context_lens.sum())} tokens) repeated {n_done}x in {el:.1f} s; "
-                      f"fp64 C oracle, OpenMP; host {platform.processor() or platform.machine()}",
-            "us_per_layer": round(el / n_done * 1e6, 1),
+            "sample": sample,
+            "us_per_layer": round(us_all, 1),
+            "value_1core": round(m["kv_bytes"] / (us_one * 1e-6) / 1e9, 4),
+            "us_per_layer_1core": round(us_one, 1),
+            "cpu_model": cpu_model(),
         }
 
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(m["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(m["us_per_layer"] * m["R"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -306,35 +519,41 @@ def main():
         "config": {
             "workload": wl.meta["description"],
             "global_batch": B,
-            "layers_per_step": R,
+            "layers_per_step": m["R"],
             "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
             "kv_dtype": wl.dtype, "accumulate": "f32", "out_dtype": "f32",
             "sum_context_tokens": int(wl.context_lens.sum()),
-            "partition_size": int(P),
-            "timing": "hip-graph replay" if use_graph else "eager",
+            "partition_size": m["P"],
+            "timing": "hip-graph replay" if m["use_graph"] else "eager",
             "parallelism": "single GPU",
         },
-        "us_per_layer": round(us_per_layer, 3),
-        "us_per_layer_two_launch": round(ms_two * 1e3 / R, 3),
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "us_per_layer": round(m["us_per_layer"], 3),
+        "us_per_layer_hot": round(m["us_hot"], 3) if m["us_hot"] else None,
+        "hot_note": "the step's 16 launches all on pool 0: its K/V stay resident in the 256 MB "
+                    "MALL; us_per_layer cycles 16 layer pools (370 MB) through it",
+        "us_per_layer_two_launch": round(m["us_two"], 3),
+        "pct_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_kernel (one launch per layer: new-token store + decode + merge)",
-            "launches_per_layer": launches,
-            "achieved": round(achieved, 2),
+            "launches_per_layer": 1,
+            "achieved": round(m["achieved"], 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac": round(m["achieved"] / HBM_PEAK_GBPS, 4),
+            "frac_of_stream_read": (round(m["achieved"] / ceilings["stream_read_GBps"], 4)
+                                    if ceilings else None),
             "traffic": measured_traffic(PROFILE_TAGS[cfg], "decode"),
             "traffic_source": f"profiles/{PROFILE_TAGS[cfg]}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                               "copy-calibrated; null when the kernel changed since)",
-            "us_per_launch": round(us_launch, 3),
-            "algorithmic_bytes_per_launch": int(alg_bytes),
+            "us_per_launch": round(m["us_per_layer"], 3),
+            "algorithmic_bytes_per_launch": int(m["alg_bytes"]),
         },
+        "hbm_ceilings": ceilings,
+        "configs": extra or None,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 PREFILL_TAGS = {2: "paged_prefill_chunked_b8", 3: "paged_prefill_drafted_b64"}
