@@ -319,15 +319,17 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
             (v_new_token_stride * elt) % 16)
             return fail(PKA_ERR_INVALID_ARGUMENT, "k_new/v_new rows must be 16-byte aligned");
     }
-    // One launch plans its sequences in LDS and counts chunks of 16 tokens
-    // or more in int32: cut the batch into launches that respect both.
+    // One launch plans its sequences in LDS and counts work units (per
+    // chunk of 16 tokens or more, and per pair) in int32: cut the batch into
+    // launches that respect both.
     const int64_t table_cap = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t chunks_per_seq = ceil_div(table_cap, 16) * num_kv_heads;
-    if (chunks_per_seq >= INT32_MAX)
+    const int64_t units_per_seq =
+        (pka::kUnitsPerChunk * ceil_div(table_cap, 16) + pka::kUnitsPerPair) * num_kv_heads;
+    if (units_per_seq >= INT32_MAX)
         return fail(PKA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size too large");
     int64_t per_launch = pka::kMaxSeqsPerLaunch;
-    if (per_launch * chunks_per_seq >= INT32_MAX)
-        per_launch = (INT32_MAX - 1) / chunks_per_seq;
+    if (per_launch * units_per_seq >= INT32_MAX)
+        per_launch = (INT32_MAX - 1) / units_per_seq;
     if (per_launch * num_kv_heads > pka::kMaxCounters)
         per_launch = pka::kMaxCounters / num_kv_heads;
     if (per_launch < 1)

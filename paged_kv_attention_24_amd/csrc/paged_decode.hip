@@ -125,7 +125,9 @@ __device__ __forceinline__ int seq_len_uniform(const DecodeParams &p, int bb)
 
 // prefix[i] = kv heads * (chunks of the sequences before sequence i), for
 // i = 0..B, in LDS; every thread of the workgroup takes part (one barrier
-// at the end).  wsum: kWaves ints of scratch.
+// at the end).  wsum: kWaves ints of scratch.  The counts are work units:
+// kUnitsPerChunk per chunk and kUnitsPerPair per (sequence, kv head) pair
+// that has tokens.
 template <int CT>
 __device__ __forceinline__ void build_prefix(const DecodeParams &p, int *prefix, int *wsum)
 {
@@ -136,7 +138,8 @@ __device__ __forceinline__ void build_prefix(const DecodeParams &p, int *prefix,
     const int b0 = threadIdx.x * per, b1 = min(b0 + per, B);
     auto chunks = [&](int bb) {
         const int L = clamp_len(p, p.context_lens[bb]);
-        return (L + CT - 1) / CT * p.num_kv_heads;
+        const int nch = (L + CT - 1) / CT;
+        return nch > 0 ? (kUnitsPerChunk * nch + kUnitsPerPair) * p.num_kv_heads : 0;
     };
     int local = 0;
     for (int bb = b0; bb < b1; ++bb)
@@ -201,10 +204,10 @@ __device__ __forceinline__ int64_t wave_of(int64_t x, int64_t c, int64_t n)
 }
 
 // One segment of a wave's range: chunks [k0, k1) of pair (b, h), whose
-// sequence has L tokens (nch chunks); pc0 is the pair's first flat chunk.
+// sequence has L tokens (nch chunks); pu0 is the pair's first work unit.
 struct Segment {
     int b, h, k0, k1, nch, L;
-    int64_t pc0;
+    int64_t pu0;
     bool first;  // the first segment of the wave's range
 };
 
@@ -224,14 +227,21 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     const bool head_ok = n < G;
     const int B = p.num_seqs, Hkv = p.num_kv_heads;
 
-    // ---- plan: chunk prefix over the sequences, then this wave's range --
+    // ---- plan: work-unit prefix over the sequences, then this wave's range --
+    // The pairs' chunks are laid end to end, each pair led by kUnitsPerPair
+    // units for its fixed cost; the U units are cut into N equal ranges,
+    // and chunk k of a pair starting at unit s belongs to the wave whose
+    // range holds its anchor s + kUnitsPerPair + kUnitsPerChunk * k.  N
+    // keeps every range at least min_chunks chunks (and one chunk) long,
+    // so every wave between the first and the last of a split pair holds
+    // one of its chunks.
     int *prefix = reinterpret_cast<int *>(smem + kWaves * S::STAGE);
     build_prefix<CT>(p, prefix + kWaves, prefix);
     prefix += kWaves;
     auto pre = [&](int bb) { return __builtin_amdgcn_readfirstlane(prefix[bb]); };
-    const int64_t C = pre(B);
+    const int64_t U = pre(B);
     const int64_t launched = (int64_t)gridDim.x * kWaves;
-    const int64_t want = floor_div(C + p.min_chunks - 1, p.min_chunks);
+    const int64_t want = floor_div(U, (int64_t)kUnitsPerChunk * p.min_chunks);
     const int64_t N = want < 1 ? 1 : (want < launched ? want : launched);
     const int64_t a = (int64_t)w * gridDim.x + blockIdx.x;  // active waves spread over the CUs
 
@@ -242,9 +252,9 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         for (int e = lane; e < p.num_q_heads * D; e += kWave)
             store_out(p.out, (int64_t)bb * p.num_q_heads * D + e, 0.0f, p.out_kind);
     }
-    if (a >= N || C == 0)
+    if (a >= N || U == 0)
         return;
-    const int64_t c0 = range_start(a, C, N), c1 = range_start(a + 1, C, N);
+    const int64_t u0 = range_start(a, U, N), u1 = range_start(a + 1, U, N);
 
     const float c = fabsf(p.scale_log2);
     // softmax runs on raw dots scaled by c = |scale| log2(e) inside the
@@ -261,48 +271,61 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     auto swv = [](int r) { return S::F32 ? 0 : (((D == 64 ? r >> 1 : r) & (LPR / 2 - 1)) << 1); };
 
     // ---- segment iterator --------------------------------------------------
-    auto seq_chunks = [&](int bb) { return (pre(bb + 1) - pre(bb)) / Hkv; };
-    Segment cur;
-    {
-        const int b0 = find_seq(prefix, B, c0);
-        const int nch = seq_chunks(b0);
-        const int rel = (int)(c0 - pre(b0));
-        cur.b = b0;
-        cur.h = rel / nch;
-        cur.k0 = rel - cur.h * nch;
-        cur.nch = nch;
-        cur.L = seq_len_uniform(p, b0);
-        cur.pc0 = pre(b0) + (int64_t)cur.h * nch;
-        const int64_t left = c1 - c0;
-        cur.k1 = (int)(cur.k0 + left < nch ? cur.k0 + left : nch);
-        cur.first = true;
-    }
-    // the segment after s, if the range goes on (returns false at its end)
+    auto seq_chunks = [&](int bb) {
+        const int d = (pre(bb + 1) - pre(bb)) / Hkv;  // units of one pair
+        return d > 0 ? (d - kUnitsPerPair) / kUnitsPerChunk : 0;
+    };
+    // chunks of the pair starting at unit s whose anchors lie below u
+    auto anchors_below = [&](int64_t s, int64_t u, int nch) {
+        const int64_t r = u - s - kUnitsPerPair;
+        const int64_t k = r <= 0 ? 0 : (r + kUnitsPerChunk - 1) / kUnitsPerChunk;
+        return (int)(k < nch ? k : nch);
+    };
+    // the pair (b, h) starting at unit s as a segment of [u0, u1)
+    auto segment = [&](int b, int h, int nch, int L, int64_t s, bool first) {
+        Segment sg;
+        sg.b = b;
+        sg.h = h;
+        sg.nch = nch;
+        sg.L = L;
+        sg.pu0 = s;
+        sg.k0 = anchors_below(s, u0, nch);
+        sg.k1 = anchors_below(s, u1, nch);
+        sg.first = first;
+        return sg;
+    };
+    // the pair after s, if it has a chunk in the range (false at its end)
     auto advance = [&](const Segment &s, Segment &nx) {
-        const int64_t done = s.pc0 + s.k1;  // flat index after s
-        if (done >= c1)
+        const int64_t start = s.pu0 + (int64_t)kUnitsPerChunk * s.nch + kUnitsPerPair;
+        if (start + kUnitsPerPair >= u1)
             return false;
-        nx.first = false;
-        nx.k0 = 0;
         if (s.h + 1 < Hkv) {
-            nx.b = s.b;
-            nx.h = s.h + 1;
-            nx.nch = s.nch;
-            nx.L = s.L;
+            nx = segment(s.b, s.h + 1, s.nch, s.L, start, false);
         } else {
             int bb = s.b + 1;
-            while (pre(bb + 1) == pre(bb))  // skip empty sequences (done < C)
+            while (pre(bb + 1) == pre(bb))  // skip empty sequences (start < U)
                 ++bb;
-            nx.b = bb;
-            nx.h = 0;
-            nx.nch = seq_chunks(nx.b);
-            nx.L = seq_len_uniform(p, nx.b);
+            nx = segment(bb, 0, seq_chunks(bb), seq_len_uniform(p, bb), start, false);
         }
-        nx.pc0 = done;
-        const int64_t left = c1 - done;
-        nx.k1 = (int)(left < nx.nch ? left : nx.nch);
         return true;
     };
+    Segment cur;
+    {
+        const int b0 = find_seq(prefix, B, u0);
+        const int nch = seq_chunks(b0);
+        const int64_t pu = (int64_t)kUnitsPerChunk * nch + kUnitsPerPair;
+        const int h0 = (int)((u0 - pre(b0)) / pu);
+        cur = segment(b0, h0, nch, seq_len_uniform(p, b0), pre(b0) + h0 * pu, true);
+        if (cur.k0 >= cur.k1) {
+            // u0 lies past the pair's last anchor: the range starts with the
+            // next pair, if any of its chunks lies in the range
+            Segment nx;
+            if (!advance(cur, nx))
+                return;
+            cur = nx;
+            cur.first = true;
+        }
+    }
 
     // this lane's operand offsets inside a staged chunk
     uint32_t kofs[TPC][KS], vofs[TPC][MT][S::F32 ? 4 : 1];
@@ -414,7 +437,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     // split segments of this range (at most the first and the last), reported
     // once the whole range is done: {b, h, first flat chunk of the pair}
     int sp_b[2] = {-1, -1}, sp_h[2] = {0, 0};
-    int64_t sp_pc0[2] = {0, 0};
+    int64_t sp_pu0[2] = {0, 0};
 
     // A finished segment's stores wait in registers until the next chunk's
     // operands have been read from LDS, so that no wait for those operands
@@ -729,11 +752,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
             if (cur.first) {
                 sp_b[0] = cur.b;
                 sp_h[0] = cur.h;
-                sp_pc0[0] = cur.pc0;
+                sp_pu0[0] = cur.pu0;
             } else {
                 sp_b[1] = cur.b;
                 sp_h[1] = cur.h;
-                sp_pc0[1] = cur.pc0;
+                sp_pu0[1] = cur.pu0;
             }
         }
         if (!has_next)
@@ -756,10 +779,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     int nseg_[2];
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
-        const int64_t ps = sp_pc0[si];
-        const int64_t pe = sp_b[si] < 0 ? ps + 1 : ps + seq_chunks(sp_b[si]);
-        wf_[si] = wave_of(ps, C, N);
-        wl_[si] = wave_of(pe - 1, C, N);
+        // the waves holding the pair's first and last chunk anchors
+        const int64_t fa = sp_pu0[si] + kUnitsPerPair;
+        const int64_t la = sp_b[si] < 0 ? fa : fa + (int64_t)kUnitsPerChunk * (seq_chunks(sp_b[si]) - 1);
+        wf_[si] = wave_of(fa, U, N);
+        wl_[si] = wave_of(la, U, N);
         nseg_[si] = (int)(wl_[si] - wf_[si] + 1);
     }
     int old = -1;
@@ -816,7 +840,10 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         Merge &m = mg[si];
         m.wf = wf_[si];
         m.nseg = nseg_[si];
-        m.slot_wf = 2 * m.wf + (sp_pc0[si] > range_start(m.wf, C, N) ? 1 : 0);
+        // the pair is that wave's first segment unless the previous pair's
+        // last anchor (kUnitsPerChunk below the pair's start) is in its range
+        const int64_t ps = sp_pu0[si];
+        m.slot_wf = 2 * m.wf + (ps > 0 && ps - kUnitsPerChunk >= range_start(m.wf, U, N) ? 1 : 0);
         load_ml(m, 0, m.ml);
         load_rows(m, 0, 0, m.o);
     }

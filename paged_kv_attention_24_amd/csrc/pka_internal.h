@@ -60,6 +60,12 @@ constexpr int kMaxWorkgroupsPerCU = 2;
 // Smallest number of tokens (of any mix of pairs) one decode wave takes by
 // default: fewer, longer ranges mean fewer partial results to combine.
 constexpr int kDefaultRangeTokens = 64;
+// Work units of the decode's split.  A chunk weighs kUnitsPerChunk and each
+// (sequence, kv head) pair adds kUnitsPerPair for its fixed cost (staging q,
+// finishing and publishing the result: measured at about half a chunk's
+// time), so a wave whose range touches many short pairs takes fewer chunks.
+constexpr int kUnitsPerChunk = 4;
+constexpr int kUnitsPerPair = 2;
 
 // Floats of one decode partial result: the unnormalised output [G][D], then
 // the running maxima [G] and sums [G], padded to 16 bytes so that every
