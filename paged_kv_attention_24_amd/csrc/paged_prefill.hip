@@ -34,13 +34,6 @@
 #include "cdna4.h"
 #include "pka_internal.h"
 
-#ifndef PKA_PREFILL_LOADS_PER_WAVE
-#define PKA_PREFILL_LOADS_PER_WAVE 2
-#endif
-#ifndef PKA_PREFILL_COL_TILES
-#define PKA_PREFILL_COL_TILES 1
-#endif
-
 namespace pka {
 namespace {
 
@@ -55,7 +48,18 @@ struct PrefillParams {
     int32_t num_query_tokens, num_q_heads, num_kv_heads, num_blocks;
     int32_t len_cap;  // max_blocks_per_seq * block_size
     float scale_log2;  // scale * log2(e)
+    int32_t num_qblocks;  // workgroups (query blocks) per (sequence, kv head) pair
+    int64_t num_pairs;    // num_seqs * num_kv_heads
 };
+
+// Workgroups are dealt to the XCDs in turn (workgroup i to XCD i % kXcds),
+// and each XCD has its own L2.  The grid is numbered so that all query
+// blocks of one (sequence, kv head) pair land on one XCD, one after another:
+// they read the same K/V, which the first fetches into that L2 for the rest
+// (spread over the XCDs, every L2 would fetch it again).  Workgroup i goes
+// to XCD x = i % kXcds and takes item k = i / kXcds of that XCD's list: pair
+// (k / nqb) * kXcds + x, query block k % nqb.
+constexpr int kXcds = 8;
 
 template <class T, int D, int BS, int G>
 struct PShape {
@@ -63,7 +67,7 @@ struct PShape {
     static constexpr int LPR = D * ELT / 16;  // lanes per token row
     static constexpr int TPL = kWave / LPR;   // token rows per 1 KiB wave load
     static constexpr int NW = 4;              // waves per workgroup
-    static constexpr int LPW = PKA_PREFILL_LOADS_PER_WAVE;  // 1 KiB loads per tensor per wave per chunk
+    static constexpr int LPW = 2;             // 1 KiB loads per tensor per wave per chunk
     static constexpr int NL = NW * LPW;       // 1 KiB loads per tensor per chunk
     static constexpr int CT = NL * TPL;       // tokens per chunk
     static constexpr int TPC = CT / 16;       // 16-token tiles per chunk
@@ -72,7 +76,7 @@ struct PShape {
     static constexpr int R = D * ELT;         // bytes per token row
     static constexpr int CHUNK = NL * 1024;   // bytes of one tensor's chunk
     static constexpr int TILE = BS * D * ELT; // bytes of one (block, head) tile
-    static constexpr int NCT = PKA_PREFILL_COL_TILES;  // 16-column tiles per wave
+    static constexpr int NCT = 1;             // 16-column tiles per wave
     static constexpr int QB = NW * NCT * 16 / G;  // new tokens per workgroup
     static_assert(TPC >= 1 && CT % 16 == 0, "a chunk holds whole 16-token tiles");
     static_assert(BS % TPL == 0, "a wave load stays inside one block");
@@ -87,7 +91,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
     constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the reference max by
     __shared__ __attribute__((aligned(1024))) char stage[2 * 2 * CHUNK];  // [buffer][K, V]
 
-    const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * S::QB;
+    const uint32_t xcd = blockIdx.x % kXcds, item = blockIdx.x / kXcds;
+    const int64_t pair = (int64_t)(item / (uint32_t)p.num_qblocks) * kXcds + xcd;
+    if (pair >= p.num_pairs)
+        return;
+    const int b = (int)(pair / p.num_kv_heads), h = (int)(pair % p.num_kv_heads);
+    const int q0 = (int)(item % (uint32_t)p.num_qblocks) * S::QB;
     const int lane = threadIdx.x % kWave;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int n = lane % 16, quad = lane / 16;
@@ -374,9 +383,13 @@ hipError_t launch_prefill_typed(const PrefillArgs &a, hipStream_t stream)
     const int64_t cap = (int64_t)a.max_blocks_per_seq * BS;
     p.len_cap = (int32_t)(cap > INT32_MAX ? INT32_MAX : cap);
     p.scale_log2 = a.scale * kLog2e;
-    const dim3 grid((unsigned)((a.max_query_len + S::QB - 1) / S::QB), (unsigned)a.num_kv_heads,
-                    (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<T, D, BS, G>), grid, dim3(S::NW * kWave), 0, stream, p);
+    p.num_qblocks = (a.max_query_len + S::QB - 1) / S::QB;
+    p.num_pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t groups = (p.num_pairs + kXcds - 1) / kXcds * kXcds * p.num_qblocks;
+    if (groups > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel<T, D, BS, G>), dim3((unsigned)groups), dim3(S::NW * kWave),
+                       0, stream, p);
     return hipGetLastError();
 }
 
