@@ -345,8 +345,7 @@ def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
         else:
             kcs.append(fill_pool(shape, tdt, 1000 + 2 * r, dev))
             vcs.append(fill_pool(shape, tdt, 1001 + 2 * r, dev))
-    P = (args.partition_size if headline else 0) or wl.partition_size or \
-        pka.decode_partition_size(B, Hkv, bs, wl.max_context_len)
+    P = (args.partition_size if headline else 0) or wl.partition_size  # 0: the library's choice
     ws_bytes = pka.decode_workspace_bytes(B, Hq, Hkv, D)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # counters start at 0
     outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(R)]

@@ -176,13 +176,15 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *
  * How the work is split (split-context partitions): the tokens of all
  * (sequence, kv head) pairs form one flat sequence of chunks, and every wave
- * of the grid takes an equal contiguous share of it, so long sequences are
- * cut into partitions wherever the shares end.  A wave that holds only part
+ * of the grid takes a contiguous share of equal work (each chunk, plus a
+ * fixed cost per pair it touches), so long sequences are cut into
+ * partitions wherever the shares end.  A wave that holds only part
  * of a pair leaves its running max, sum and unnormalised output in the
  * workspace; the last wave to finish with that pair combines the parts
  * exactly (log-sum-exp) in the same launch.  The result does not depend on
  * the split beyond fp32 rounding.  Batches of more than 2040 sequences run as
- * several launches on `stream`.
+ * several launches on `stream`.  Small batches take the pair mode described
+ * under partition_size.
  *
  *   out             device, [num_seqs][num_q_heads][head_dim], contiguous,
  *                   of out_dtype (PKA_F32, or the KV dtype: rounded to
@@ -198,12 +200,18 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   context_lens    device, int32 [num_seqs].  Lengths are clamped on the
  *                   device to [0, max_blocks_per_seq * block_size].
  *   scale           multiplier of the dot products (typically 1/sqrt(D)).
- *   max_context_len accepted for interface compatibility and not used: the
- *                   launch is sized from the device, so no hint can cut a
- *                   sequence short.
- *   partition_size  0: pka_decode_partition_size(); else a positive
- *                   multiple of block_size: the fewest tokens one wave
- *                   takes (fewer, longer shares leave fewer parts to
+ *   max_context_len optional host bound on the lengths (<= 0: none).  It
+ *                   only helps pick the launch shape: no length is ever cut
+ *                   short by it (a length above it is still computed).
+ *   partition_size  0: the library picks the split: with at most as many
+ *                   (sequence, kv head) pairs as compute units and lengths
+ *                   of at most 2048 tokens (by max_context_len, else by the
+ *                   table width), each pair gets one workgroup whose waves
+ *                   share its chunks and combine in LDS (no workspace
+ *                   traffic); otherwise the flat split below with
+ *                   pka_decode_partition_size() tokens.  Else a positive
+ *                   multiple of block_size: the flat split, the fewest
+ *                   tokens one wave takes (fewer, longer shares leave fewer parts to
  *                   combine).
  *   workspace       device scratch of workspace_bytes >=
  *                   pka_decode_workspace_bytes(...), 256-byte aligned.  Its

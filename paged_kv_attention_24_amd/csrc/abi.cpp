@@ -298,7 +298,7 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
         return fail(PKA_ERR_INVALID_ARGUMENT,
                     "partition_size %d must be 0 or a positive multiple of block_size %d",
                     partition_size, block_size);
-    (void)max_context_len;  // the launch is sized from the device, not from a hint
+    // max_context_len only picks the launch shape: no length is cut short by it
     if (num_seqs == 0)
         return ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -380,6 +380,7 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
         a.scale = scale;
         a.kv_dtype = to_internal(kv_dtype);
         a.partition_size = partition_size;
+        a.context_hint = max_context_len > 0 ? max_context_len : 0;
         a.counters = reinterpret_cast<int32_t *>(base + wl.counter_offset);
         a.parts = reinterpret_cast<float *>(base + wl.parts_offset);
         a.max_waves = max_waves;

@@ -53,6 +53,14 @@ namespace pka {
 namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup (each wave works alone after planning)
+// Pair mode (small batches): one workgroup of kPairWaves waves per (sequence,
+// kv head) pair, the waves splitting its chunks and combining in LDS.  Used
+// while pairs fit one per compute unit and sequences are at most
+// kPairModeMaxTokens long (a longer pair would keep one compute unit busy
+// while the others idle).
+constexpr int kPairWaves = 8;
+constexpr int64_t kPairModeMaxTokens = 2048;
+constexpr size_t kPairModeMaxLds = 160 * 1024;
 
 struct DecodeParams {
     void *out;
@@ -211,8 +219,9 @@ struct Segment {
     bool first;  // the first segment of the wave's range
 };
 
-template <class T, int D, int BS, int G>
-__global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams p)
+template <class T, int D, int BS, int G, bool PAIR>
+__global__ __launch_bounds__((PAIR ? kPairWaves : kWaves) * kWave, PAIR ? 1 : 2)
+void decode_kernel(DecodeParams p)
 {
     using S = Shape<T, D, BS, G>;
     constexpr int R = S::R, LPR = S::LPR, TPL = S::TPL, NL = S::NL, CT = S::CT, TPC = S::TPC;
@@ -234,27 +243,30 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     // range holds its anchor s + kUnitsPerPair + kUnitsPerChunk * k.  N
     // keeps every range at least min_chunks chunks (and one chunk) long,
     // so every wave between the first and the last of a split pair holds
-    // one of its chunks.
-    int *prefix = reinterpret_cast<int *>(smem + kWaves * S::STAGE);
-    build_prefix<CT>(p, prefix + kWaves, prefix);
-    prefix += kWaves;
+    // one of its chunks.  (Pair mode: the workgroup's pair, no plan.)
+    int *prefix = reinterpret_cast<int *>(smem + kWaves * S::STAGE) + kWaves;
     auto pre = [&](int bb) { return __builtin_amdgcn_readfirstlane(prefix[bb]); };
-    const int64_t U = pre(B);
-    const int64_t launched = (int64_t)gridDim.x * kWaves;
-    const int64_t want = floor_div(U, (int64_t)kUnitsPerChunk * p.min_chunks);
-    const int64_t N = want < 1 ? 1 : (want < launched ? want : launched);
-    const int64_t a = (int64_t)w * gridDim.x + blockIdx.x;  // active waves spread over the CUs
+    int64_t U = 0, N = 1, a = 0, u0 = 0, u1 = 0;
+    if constexpr (!PAIR) {
+        build_prefix<CT>(p, prefix, prefix - kWaves);
+        U = pre(B);
+        const int64_t launched = (int64_t)gridDim.x * kWaves;
+        const int64_t want = floor_div(U, (int64_t)kUnitsPerChunk * p.min_chunks);
+        N = want < 1 ? 1 : (want < launched ? want : launched);
+        a = (int64_t)w * gridDim.x + blockIdx.x;  // active waves spread over the CUs
 
-    // Sequences with no token: zero rows (any wave of the grid, by stride).
-    for (int bb = (int)a; bb < B; bb += (int)launched) {
-        if (prefix[bb + 1] != prefix[bb])
-            continue;
-        for (int e = lane; e < p.num_q_heads * D; e += kWave)
-            store_out(p.out, (int64_t)bb * p.num_q_heads * D + e, 0.0f, p.out_kind);
+        // Sequences with no token: zero rows (any wave of the grid, by stride).
+        for (int bb = (int)a; bb < B; bb += (int)launched) {
+            if (prefix[bb + 1] != prefix[bb])
+                continue;
+            for (int e = lane; e < p.num_q_heads * D; e += kWave)
+                store_out(p.out, (int64_t)bb * p.num_q_heads * D + e, 0.0f, p.out_kind);
+        }
+        if (a >= N || U == 0)
+            return;
+        u0 = range_start(a, U, N);
+        u1 = range_start(a + 1, U, N);
     }
-    if (a >= N || U == 0)
-        return;
-    const int64_t u0 = range_start(a, U, N), u1 = range_start(a + 1, U, N);
 
     const float c = fabsf(p.scale_log2);
     // softmax runs on raw dots scaled by c = |scale| log2(e) inside the
@@ -296,6 +308,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
     };
     // the pair after s, if it has a chunk in the range (false at its end)
     auto advance = [&](const Segment &s, Segment &nx) {
+        if constexpr (PAIR)
+            return false;
         const int64_t start = s.pu0 + (int64_t)kUnitsPerChunk * s.nch + kUnitsPerPair;
         if (start + kUnitsPerPair >= u1)
             return false;
@@ -310,7 +324,32 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         return true;
     };
     Segment cur;
-    {
+    bool empty_range = false;  // pair mode: this wave has no chunk of the pair
+    if constexpr (PAIR) {
+        const int b = (int)(blockIdx.x / (unsigned)Hkv), h = (int)(blockIdx.x % (unsigned)Hkv);
+        const int L = seq_len_uniform(p, b);
+        if (L == 0) {  // the same for the whole workgroup: zero rows, nothing else
+            for (int e = w * kWave + lane; e < G * D; e += kPairWaves * kWave)
+                store_out(p.out, ((int64_t)b * p.num_q_heads + h * G) * D + e, 0.0f, p.out_kind);
+            return;
+        }
+        const int nch = (L + CT - 1) / CT;
+        cur.b = b;
+        cur.h = h;
+        cur.nch = nch;
+        cur.L = L;
+        cur.pu0 = 0;
+        cur.first = true;
+        cur.k0 = w * nch / kPairWaves;
+        cur.k1 = (w + 1) * nch / kPairWaves;
+        if (cur.k0 >= cur.k1) {
+            // no chunk here: stream the pair's first chunk anyway (in bounds,
+            // result discarded) so that the wave reaches the combine below
+            empty_range = true;
+            cur.k0 = 0;
+            cur.k1 = 1;
+        }
+    } else {
         const int b0 = find_seq(prefix, B, u0);
         const int nch = seq_chunks(b0);
         const int64_t pu = (int64_t)kUnitsPerChunk * nch + kUnitsPerPair;
@@ -523,7 +562,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
                 r = load_ids(nxt, nxt.k0);
             return r;
         };
-        const bool app = p.k_new != nullptr && cur.k1 == cur.nch;
+        const bool app = p.k_new != nullptr && cur.k1 == cur.nch && !empty_range;
         const int k_app = cur.nch - 1;                 // chunk of position L - 1
         const int row_app = cur.L - 1 - k_app * CT;    // its row in that chunk
 
@@ -769,6 +808,53 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void decode_kernel(DecodeParams 
         pool_slot = pool_slotn;
     }
 
+    if constexpr (PAIR) {
+        // the new row into its slot (the fused write), then this wave's part
+        // (unnormalised O, max in log2 units, sum) into its own staging
+        // area, free now; after the barrier the waves combine the parts
+        if (pend.app && lane < LPR) {
+            const int64_t slot = pend.pool_slot;
+            if (slot >= 0 && slot < p.num_slots) {
+                const int64_t blk = slot / BS;
+                const int64_t dst = (blk * Hkv + pend.h) * S::TILE + (slot - blk * BS) * R + lane * 16;
+                *reinterpret_cast<uint4 *>(p.k_store + dst) = pend.knew;
+                *reinterpret_cast<uint4 *>(p.v_store + dst) = pend.vnew;
+            }
+        }
+        float *mine = reinterpret_cast<float *>(stage);
+        if (head_ok) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                *reinterpret_cast<float4_t *>(mine + n * D + 16 * mt + 4 * quad) =
+                    empty_range ? float4_t{0.0f, 0.0f, 0.0f, 0.0f} : pend.O[mt];
+            if (quad == 0) {
+                mine[G * D + n] = empty_range ? -INFINITY : pend.m;
+                mine[G * D + G + n] = empty_range ? 0.0f : pend.l;
+            }
+        }
+        __syncthreads();
+        // out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w over the waves
+        const int64_t orow = ((int64_t)pend.b * p.num_q_heads + pend.h * G) * D;
+        for (int e = w * kWave + lane; e < G * D; e += kPairWaves * kWave) {
+            const int g = e / D;
+            float mw[kPairWaves], M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < kPairWaves; ++ww) {
+                mw[ww] = reinterpret_cast<const float *>(smem + ww * S::STAGE)[G * D + g];
+                M = fmaxf(M, mw[ww]);
+            }
+            float num = 0.0f, den = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < kPairWaves; ++ww) {
+                const float *part = reinterpret_cast<const float *>(smem + ww * S::STAGE);
+                const float wt = mw[ww] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[ww] - M);
+                num = fmaf(wt, part[e], num);
+                den = fmaf(wt, part[G * D + G + g], den);
+            }
+            store_out(p.out, orow + e, den > 0.0f ? num / den : 0.0f, p.out_kind);
+        }
+        return;
+    }
     flush();  // the last segment's stores
     // ---- report the split pairs; the last wave of a pair combines it -------
     if (sp_b[0] < 0 && sp_b[1] < 0)
@@ -968,12 +1054,12 @@ int resident_workgroups(size_t lds)
         return 256;
     const int cls = lds > decode_lds_bytes<T, D, BS, G>(kMaxSeqsPerLaunch / 2) ? 1 : 0;
     if (cached[dev][cls] == 0) {
-        (void)hipFuncSetAttribute((const void *)decode_kernel<T, D, BS, G>,
+        (void)hipFuncSetAttribute((const void *)decode_kernel<T, D, BS, G, false>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)decode_lds_bytes<T, D, BS, G>(kMaxSeqsPerLaunch));
         const size_t probe = decode_lds_bytes<T, D, BS, G>(cls ? kMaxSeqsPerLaunch : kMaxSeqsPerLaunch / 2);
         int per_cu = 0;
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<T, D, BS, G>,
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<T, D, BS, G, false>,
                                                            kWaves * kWave, probe);
         per_cu = per_cu < 1 ? 1 : (per_cu > kMaxWorkgroupsPerCU ? kMaxWorkgroupsPerCU : per_cu);
         cached[dev][cls] = device_compute_units() * per_cu;
@@ -1013,13 +1099,38 @@ hipError_t launch_group(const DecodeArgs &a, hipStream_t stream)
     p.k_store = static_cast<char *>(const_cast<void *>(a.k_cache));
     p.v_store = static_cast<char *>(const_cast<void *>(a.v_cache));
     p.num_slots = (int64_t)a.num_blocks * a.block_size;
+    if constexpr (!S::F32) {
+        // Pair mode, when the library picks the split: as many (sequence,
+        // kv head) pairs as compute units and sequences short enough (by the
+        // table width, or the caller's hint) for kPairWaves waves of one
+        // compute unit to stream each pair: no planning and no partial
+        // results in HBM.
+        constexpr size_t pair_lds = (size_t)kPairWaves * S::STAGE;
+        const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+        const int64_t longest = a.context_hint > 0 && a.context_hint < cap ? a.context_hint : cap;
+        if (a.partition_size == 0 && pair_lds <= kPairModeMaxLds &&
+            pairs <= device_compute_units() && longest <= kPairModeMaxTokens) {
+            static bool attr_set[64];
+            int dev = 0;
+            (void)hipGetDevice(&dev);
+            if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+                (void)hipFuncSetAttribute((const void *)decode_kernel<T, D, BS, G, true>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)pair_lds);
+                attr_set[dev] = true;
+            }
+            hipLaunchKernelGGL((decode_kernel<T, D, BS, G, true>), dim3((unsigned)pairs),
+                               dim3(kPairWaves * kWave), pair_lds, stream, p);
+            return hipGetLastError();
+        }
+    }
     const size_t lds = decode_lds_bytes<T, D, BS, G>(a.num_seqs);
     int grid = resident_workgroups<T, D, BS, G>(lds);
     if ((int64_t)grid * kWaves > a.max_waves)
         grid = (int)(a.max_waves / kWaves);
     if (grid < 1)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_kernel<T, D, BS, G>), dim3(grid), dim3(kWaves * kWave), lds, stream, p);
+    hipLaunchKernelGGL((decode_kernel<T, D, BS, G, false>), dim3(grid), dim3(kWaves * kWave), lds,
+                       stream, p);
     return hipGetLastError();
 }
 

@@ -41,6 +41,8 @@ struct DecodeArgs {
     float scale;
     DType kv_dtype;
     int32_t partition_size;   // smallest number of tokens one wave takes; 0: library default
+    int32_t context_hint;     // caller's bound on the lengths (max_context_len; 0: none):
+                              // picks the launch shape only, never cuts a sequence short
     float *parts;             // [2 * max_waves] partial results of decode_part_floats(G, D)
     int32_t *counters;        // [num_seqs][num_kv_heads] report counters (kCounterStride apart), zero before and after
     int64_t max_waves;        // waves the partial-result slots cover
