@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--extra-configs", default="3,4,5",
                     help="decode workloads timed after the headline one (config 2 only), "
                          "each reported under configs.<n>; 'none' to skip")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="decode: time only the fused step (no two-launch or hot timing), "
+                         "so that a profiler sees that step's launches alone")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip measuring the HBM read ceilings (csrc/calibrate.hip)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -384,9 +387,9 @@ def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
     t_wall0 = time.perf_counter()
     ms_step = timed_calls(step, steps, warmup, use_graph)
     t_wall = time.perf_counter() - t_wall0
-    ms_two = timed_calls(step_two_launch, steps, warmup, use_graph)
+    ms_two = None if args.no_extras else timed_calls(step_two_launch, steps, warmup, use_graph)
     # hot: the same R launches, all on pool 0, so its K/V stay in the 256 MB MALL
-    hot_fits = pool_bytes <= 192e6
+    hot_fits = pool_bytes <= 192e6 and not args.no_extras
 
     def step_hot():
         for _ in range(R):
@@ -394,8 +397,8 @@ def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
 
     ms_hot = timed_calls(step_hot, steps, warmup, use_graph) / R if hot_fits else None
     log(f"workload {cfg}: step {ms_step * 1e3:.1f} us ({R} fused launches), two-launch "
-        f"{ms_two * 1e3:.1f} us, hot {ms_hot * 1e3 if ms_hot else float('nan'):.1f} us; "
-        f"timed wall {t_wall:.2f} s")
+        f"{ms_two * 1e3 if ms_two else float('nan'):.1f} us, hot "
+        f"{ms_hot * 1e3 if ms_hot else float('nan'):.1f} us; timed wall {t_wall:.2f} s")
 
     kv_bytes = wl.kv_bytes()
     us_per_layer = ms_step * 1e3 / R
@@ -405,7 +408,7 @@ def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
     new_rows = B * Hkv * D * wl.elt_bytes * 2
     alg_bytes = kv_bytes + B * Hq * D * (wl.elt_bytes + 4) + nblk * 4 + B * 4 + 2 * new_rows + 8 * B
     res = dict(wl=wl, R=R, P=int(P), use_graph=use_graph, kv_bytes=kv_bytes, alg_bytes=alg_bytes,
-               us_per_layer=us_per_layer, us_two=ms_two * 1e3 / R,
+               us_per_layer=us_per_layer, us_two=ms_two * 1e3 / R if ms_two else None,
                us_hot=ms_hot * 1e3 if ms_hot else None,
                value=kv_bytes * R / (ms_step * 1e-3) / 1e9,
                achieved=alg_bytes / (us_per_layer * 1e-6) / 1e9)
@@ -431,7 +434,7 @@ def config_entry(m, cfg, ceilings, oracle_us=None):
         "us_per_layer_hot": round(m["us_hot"], 3) if m["us_hot"] else None,
         "hot_note": ("the step's launches all on pool 0: its K/V stay resident in the 256 MB MALL"
                      if m["us_hot"] else "one layer pool exceeds the 256 MB MALL: no hot figure"),
-        "us_per_layer_two_launch": round(m["us_two"], 3),
+        "us_per_layer_two_launch": round(m["us_two"], 3) if m["us_two"] else None,
         "effective_GBps": round(m["value"], 2),
         "pct_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBPS, 2),
         "launches_per_layer": 1,
@@ -530,7 +533,7 @@ def decode_line(args, dev):
         "us_per_layer_hot": round(m["us_hot"], 3) if m["us_hot"] else None,
         "hot_note": "the step's 16 launches all on pool 0: its K/V stay resident in the 256 MB "
                     "MALL; us_per_layer cycles 16 layer pools (370 MB) through it",
-        "us_per_layer_two_launch": round(m["us_two"], 3),
+        "us_per_layer_two_launch": round(m["us_two"], 3) if m["us_two"] else None,
         "pct_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
