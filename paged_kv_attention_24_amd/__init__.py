@@ -30,8 +30,7 @@ Paged attention" and "Key features > GPU-optimised kernels"):
 Pools are [num_blocks, num_kv_heads, block_size, head_dim].
 
 PKA_LIBRARY, if set, names another library file of this directory to load
-instead of libpka.so (libpka_vector_alu.so: the vector-ALU build that the
-matrix-core path is measured against).
+instead of libpka.so (a build of the same sources with other flags).
 """
 from __future__ import annotations
 

@@ -11,34 +11,43 @@
 // are prior art for another GPU, not the blueprint):
 //
 //  * Work space.  The tokens of every (sequence b, kv head h) pair are cut
-//    into chunks of CT tokens; all chunks of all pairs, pairs in (b, h)
-//    order, form one flat index space of C chunks.  Every active wave of
-//    the grid takes one contiguous range of floor(C / N) or ceil(C / N)
-//    chunks, so every wave streams the same number of bytes whatever the
-//    mix of sequence lengths (no tail of long sequences, no idle compute
-//    units on a small batch).  All G = Hq/Hkv query heads of a pair are
-//    served by the same K/V reads, so every KV byte is read from HBM once.
+//    into chunks of CT tokens.  Every chunk costs kUnitsPerChunk work units
+//    and every pair with tokens kUnitsPerPair more (its fixed cost: block
+//    ids, q, first request, result); the pairs' units, in (b, h) order,
+//    form one flat index space of U units, cut into N equal ranges, one per
+//    active wave.  A chunk belongs to the wave whose range holds its
+//    anchor, so every wave streams about the same bytes and pays about the
+//    same fixed costs whatever the mix of lengths (no tail of long
+//    sequences).  All G = Hq/Hkv query heads of a pair are served by the
+//    same K/V reads, so every KV byte is read from HBM once.
+//  * Pair mode, for small batches (pairs at most one per compute unit,
+//    every sequence at most kPairModeMaxTokens long): one workgroup of
+//    kPairWaves waves per pair, the waves taking contiguous runs of its
+//    chunks and combining their parts through LDS; no workspace.
 //  * Planning happens in the kernel: each workgroup scans the lengths into
-//    a prefix of chunk counts in LDS (one barrier); each wave then finds the
+//    a prefix of work units in LDS (one barrier); each wave then finds the
 //    pair its range starts in with two ballots over that prefix.
 //  * Segments.  A wave's range is a run of segments, one per pair it
 //    touches: whole pairs in the middle, possibly part of a pair at either
 //    end.  A whole pair's result is normalised and stored; a part stores
-//    (max, sum, unnormalised O) to the workspace, and once every wave has
-//    finished its range the last wave to report on that pair (a counter per
-//    pair) combines its parts by log-sum-exp and stores the result.
+//    (max, sum, unnormalised O) to the workspace with coherent stores, and
+//    the last wave to report on that pair (a counter per pair, one per
+//    128-byte line) combines its parts by log-sum-exp, stores the result
+//    and clears the counter.
 //  * Data path of a wave: its chunks of K and V go straight from HBM into
 //    the wave's own LDS area (global_load_lds, XOR-swizzled rows), one chunk
 //    ahead of the one computed; the next segment's first chunk, query rows
-//    and appended row are requested while the current segment's last chunk
-//    is computed, so the stream runs on across segment boundaries.  Per
+//    and appended row (also DMA'd into LDS) are requested while the current
+//    segment's last chunk is computed, so the stream runs on across segment
+//    boundaries.  Per
 //    16-token tile, matrix-core products give the scores of all G heads
 //    (K tile times q^T); the online softmax runs in the registers the
 //    product wrote; a second product accumulates O^T += V^T P^T, V^T coming
 //    from the transposing LDS read (fp16/bf16) or from column reads (fp32).
 //  * Fused append: for pka_paged_attention_decode_append the wave that
 //    holds position L_b - 1 stores the sequence's new K/V row in its slot
-//    and uses it from registers (patched into LDS) for that position.
+//    and takes that position's K/V from the row's LDS copy, so nothing waits
+//    for the store.
 //  * Tokens >= L (the tail of the last block) are excluded by selects, never
 //    by multiplying with 0, so stale or NaN slot contents cannot leak.
 
