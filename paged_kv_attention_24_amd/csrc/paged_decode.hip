@@ -892,62 +892,28 @@ void decode_kernel(DecodeParams p)
     // parts, 64 parts at a time with a running maximum.  Lane j of a batch
     // reads part j's (max, sum) block (2G floats, 16-byte loads); each lane
     // accumulates its output elements e = lane + 64 i (head (64 i) / D, the
-    // same in all lanes) over the parts, BJ parts' rows at a time.  When this
-    // wave combines both of its split pairs, the first batch of loads of both
-    // is requested before either is combined.
-    constexpr int E = G * D / kWave;          // output elements per lane
-    constexpr int BJ = E >= 16 ? 4 : 64 / E;  // parts per batch of row loads
-    constexpr int MLV = (2 * G + 3) / 4;      // 16-byte loads of one (max, sum) block
-    struct Merge {
-        int64_t wf, slot_wf;  // first contributing wave, its slot
-        int nseg;
-        float4_t ml[MLV];     // the first batch: part `lane`'s (max, sum)
-        float o[BJ][E];       // the first batch: rows of parts 0 .. BJ-1
-    };
-    Merge mg[2];
-    const bool lastv[2] = {last0, last1};
-    // part of wave ww: the first contributing wave holds it in its second
-    // slot when the pair starts inside that wave's range; every later wave's
-    // range starts inside the pair, so there it is the first slot
-    auto slot_of = [&](const Merge &m, int64_t ww) { return ww == m.wf ? m.slot_wf : 2 * ww; };
-    auto load_ml = [&](const Merge &m, int j0, float4_t (&ml)[MLV]) __attribute__((always_inline)) {
-        const int nb = m.nseg - j0 < kWave ? m.nseg - j0 : kWave;
-        const uint32_t pb = part_byte(slot_of(m, m.wf + j0 + (lane < nb ? lane : nb - 1)));
-#pragma unroll
-        for (int v = 0; v < MLV; ++v)
-            ml[v] = coherent_load16(parts_view, pb + 4 * (G * D + 4 * v));
-    };
-    auto load_rows = [&](const Merge &m, int j0, int jj, float (&o)[BJ][E]) __attribute__((always_inline)) {
-        const int nb = m.nseg - j0 < kWave ? m.nseg - j0 : kWave;
-#pragma unroll
-        for (int u = 0; u < BJ; ++u) {
-            const int j = jj + u < nb ? jj + u : nb - 1;
-            const float *pr = p.parts + slot_of(m, m.wf + j0 + j) * S::PART;
-#pragma unroll
-            for (int i = 0; i < E; ++i)
-                o[u][i] = coherent_load(pr + kWave * i + lane);
-        }
-    };
-#pragma unroll
+    // same in all lanes) over the parts, BJ parts' rows at a time, the first
+    // rows requested with the (max, sum) blocks.  One copy of this code
+    // serves both split pairs (a loop that is not unrolled): it runs once per
+    // combine, where its instruction fetches are on the critical path.
+    constexpr int E = G * D / kWave;      // output elements per lane
+    constexpr int BJ = 4;                 // parts per batch of row loads
+    constexpr int MLV = (2 * G + 3) / 4;  // 16-byte loads of one (max, sum) block
+#pragma unroll 1
     for (int si = 0; si < 2; ++si) {
-        if (!lastv[si])
+        if (!(si == 0 ? last0 : last1))
             continue;
-        Merge &m = mg[si];
-        m.wf = wf_[si];
-        m.nseg = nseg_[si];
-        // the pair is that wave's first segment unless the previous pair's
-        // last anchor (kUnitsPerChunk below the pair's start) is in its range
-        const int64_t ps = sp_pu0[si];
-        m.slot_wf = 2 * m.wf + (ps > 0 && ps - kUnitsPerChunk >= range_start(m.wf, U, N) ? 1 : 0);
-        load_ml(m, 0, m.ml);
-        load_rows(m, 0, 0, m.o);
-    }
-#pragma unroll
-    for (int si = 0; si < 2; ++si) {
-        if (!lastv[si])
-            continue;
-        Merge &m = mg[si];
-        const int bb = sp_b[si], hh = sp_h[si];
+        const int bb = si == 0 ? sp_b[0] : sp_b[1], hh = si == 0 ? sp_h[0] : sp_h[1];
+        const int64_t wf = si == 0 ? wf_[0] : wf_[1];
+        const int nseg = si == 0 ? nseg_[0] : nseg_[1];
+        // part of wave ww: the first contributing wave holds it in its second
+        // slot when the pair starts inside that wave's range (the previous
+        // pair's last anchor, kUnitsPerChunk below the pair's start, is in
+        // it); every later wave's range starts inside the pair, so there it
+        // is the first slot
+        const int64_t ps = si == 0 ? sp_pu0[0] : sp_pu0[1];
+        const int64_t slot_wf = 2 * wf + (ps > 0 && ps - kUnitsPerChunk >= range_start(wf, U, N) ? 1 : 0);
+        auto slot_of = [&](int64_t ww) { return ww == wf ? slot_wf : 2 * ww; };
         float Mrun[G], den[G], acc[E];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -957,24 +923,28 @@ void decode_kernel(DecodeParams p)
 #pragma unroll
         for (int i = 0; i < E; ++i)
             acc[i] = 0.0f;
-        for (int j0 = 0; j0 < m.nseg; j0 += kWave) {
-            const int nb = m.nseg - j0 < kWave ? m.nseg - j0 : kWave;
+        for (int j0 = 0; j0 < nseg; j0 += kWave) {
+            const int nb = nseg - j0 < kWave ? nseg - j0 : kWave;
             const bool mine = lane < nb;
-            float4_t ml[MLV];
             float o[BJ][E];
-            if (j0 == 0) {
+            auto load_rows = [&](int jj) __attribute__((always_inline)) {
 #pragma unroll
-                for (int v = 0; v < MLV; ++v)
-                    ml[v] = m.ml[v];
-#pragma unroll
-                for (int u = 0; u < BJ; ++u)
+                for (int u = 0; u < BJ; ++u) {
+                    const int j = jj + u < nb ? jj + u : nb - 1;
+                    const float *pr = p.parts + slot_of(wf + j0 + j) * S::PART;
 #pragma unroll
                     for (int i = 0; i < E; ++i)
-                        o[u][i] = m.o[u][i];
-            } else {
-                load_ml(m, j0, ml);
-                load_rows(m, j0, 0, o);
+                        o[u][i] = coherent_load(pr + kWave * i + lane);
+                }
+            };
+            float4_t ml[MLV];
+            {
+                const uint32_t pb = part_byte(slot_of(wf + j0 + (mine ? lane : nb - 1)));
+#pragma unroll
+                for (int v = 0; v < MLV; ++v)
+                    ml[v] = coherent_load16(parts_view, pb + 4 * (G * D + 4 * v));
             }
+            load_rows(0);
             // the G heads' weights (lanes past the last part weigh 0)
             float mj[G], lj[G], mx[G], wj[G], sw[G];
 #pragma unroll
@@ -1003,7 +973,7 @@ void decode_kernel(DecodeParams p)
                 den[g] += sw[g];
             for (int jj = 0; jj < nb; jj += BJ) {
                 if (jj > 0)
-                    load_rows(m, j0, jj, o);
+                    load_rows(jj);
                 float wgt[BJ][G];
 #pragma unroll
                 for (int u = 0; u < BJ; ++u)

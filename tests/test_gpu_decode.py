@@ -87,6 +87,29 @@ def test_sweep(dtype, D, bs, G):
         check_close(got, ref, dtype, f"{dtype} D{D} bs{bs} G{G} P{P}")
 
 
+# pair mode (the library's choice on small batches: one workgroup per
+# (sequence, kv head) pair whose waves share its chunks) over batch shapes
+# around the compute-unit count, with waves left without a chunk
+PAIR_SHAPES = [
+    # dtype, D, B, Hkv, lengths (cycled over the batch)
+    ("f16", 64, 20, 8, [1024, 100, 517, 33]),        # 160 pairs
+    ("bf16", 64, 16, 8, [1024, 700, 129, 1]),        # 128 pairs
+    ("f16", 128, 10, 8, [1024, 31, 640, 257]),       # 80 pairs
+    ("bf16", 128, 4, 2, [1, 33, 300, 2000]),         # 8 pairs, up to 2000 tokens
+    ("f16", 64, 4, 2, [100, 7, 64, 65]),             # short
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,Hkv,lens", PAIR_SHAPES)
+def test_pair_mode_shapes(dtype, D, B, Hkv, lens):
+    lens = [lens[i % len(lens)] for i in range(B)]
+    wl = case(4000 + B + D, dtype, lens, 4 * Hkv, Hkv, D, 16)
+    print(f"[decode] pair mode {dtype} D={D} B={B} Hkv={Hkv}", flush=True)
+    a = gpu_decode(wl, partition_size=0)
+    check_close(a, oracle_full(wl), dtype, "pair mode")
+    assert np.array_equal(a, gpu_decode(wl, partition_size=0))
+
+
 # ---------------------------------------------------------------------------
 # edge cases and invariants on the GPU
 # ---------------------------------------------------------------------------
