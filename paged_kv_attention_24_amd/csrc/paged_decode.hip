@@ -897,7 +897,7 @@ void decode_kernel(DecodeParams p)
     // serves both split pairs (a loop that is not unrolled): it runs once per
     // combine, where its instruction fetches are on the critical path.
     constexpr int E = G * D / kWave;      // output elements per lane
-    constexpr int BJ = 4;                 // parts per batch of row loads
+    constexpr int BJ = 8;                 // parts per batch of row loads
     constexpr int MLV = (2 * G + 3) / 4;  // 16-byte loads of one (max, sum) block
 #pragma unroll 1
     for (int si = 0; si < 2; ++si) {
