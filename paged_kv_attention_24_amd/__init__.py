@@ -858,10 +858,13 @@ def paged_attention_decode_int8(q, k_codes, v_codes, k_scales, v_scales, block_t
     ws_ptr, ws_bytes = None, 0
     if need > 0:
         if workspace is None:
-            workspace = _INT8_WORKSPACES.get(q.device)
+            # one per (device, current stream): calls on different streams
+            # never share partial rows
+            key = (str(q.device), torch.cuda.current_stream(q.device).cuda_stream)
+            workspace = _INT8_WORKSPACES.get(key)
             if workspace is None or workspace.numel() < need:
                 workspace = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=q.device)
-                _INT8_WORKSPACES[q.device] = workspace
+                _INT8_WORKSPACES[key] = workspace
         elif workspace.numel() * workspace.element_size() < need:
             raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
                              f"bytes, {need} needed")

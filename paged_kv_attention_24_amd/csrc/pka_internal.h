@@ -64,10 +64,12 @@ constexpr int kMaxWorkgroupsPerCU = 2;
 constexpr int kDefaultRangeTokens = 64;
 // Work units of the decode's split.  A chunk weighs kUnitsPerChunk and each
 // (sequence, kv head) pair adds kUnitsPerPair for its fixed cost (staging q,
-// finishing and publishing the result: measured at about half a chunk's
-// time), so a wave whose range touches many short pairs takes fewer chunks.
+// finishing and publishing the result), so a wave whose range touches many
+// short pairs takes fewer chunks.  One chunk's weight per pair measured best
+// on a log-uniform mix of lengths (half a chunk and three quarters were 2%
+// slower there; long uniform pairs are indifferent).
 constexpr int kUnitsPerChunk = 4;
-constexpr int kUnitsPerPair = 2;
+constexpr int kUnitsPerPair = 4;
 
 // Floats of one decode partial result: the unnormalised output [G][D], then
 // the running maxima [G] and sums [G], padded to 16 bytes so that every
