@@ -84,11 +84,11 @@ def log(msg):
 
 # the sources that define each kernel (hashed to tell whether a committed
 # counter summary still describes it)
-KERNEL_SOURCES = {"decode": ("paged_decode.hip", "cdna4.h"),
-                  "prefill": ("paged_prefill.hip", "cdna4.h"),
-                  "blocks": ("block_ops.hip",),
-                  "rope": ("kv_cache_write.hip", "cdna4.h"),
-                  "int8": ("paged_int8.hip", "cdna4.h")}
+KERNEL_SOURCES = {"decode": ("paged_decode.hip", "cdna4.h", "pka_internal.h"),
+                  "prefill": ("paged_prefill.hip", "cdna4.h", "pka_internal.h"),
+                  "blocks": ("block_ops.hip", "pka_internal.h"),
+                  "rope": ("kv_cache_write.hip", "cdna4.h", "pka_internal.h"),
+                  "int8": ("paged_int8.hip", "cdna4.h", "pka_internal.h")}
 
 
 def kernel_source_sha(path_kind):
