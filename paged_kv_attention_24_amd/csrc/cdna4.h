@@ -439,28 +439,30 @@ __device__ __forceinline__ void wait_vmem_keep(int n)
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Four 16-byte reads and eight transposing 8-byte reads (one chunk's K and
-// V operands of the fp16/bf16 tiles) at LDS byte addresses ka[], va[].
+// V operands of the fp16/bf16 tiles) at LDS byte addresses ka[] + OFF,
+// va[] + OFF (OFF selects the chunk buffer without per-lane adds).
+template <int OFF>
 __device__ __forceinline__ void lds_read_chunk(u32x4 (&k)[4], u32x2 (&v)[8], const uint32_t (&ka)[4],
                                                const uint32_t (&va)[8])
 {
     asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %13\n\t"
-        "ds_read_b128 %2, %14\n\t"
-        "ds_read_b128 %3, %15\n\t"
-        "ds_read_b64_tr_b16 %4, %16\n\t"
-        "ds_read_b64_tr_b16 %5, %17\n\t"
-        "ds_read_b64_tr_b16 %6, %18\n\t"
-        "ds_read_b64_tr_b16 %7, %19\n\t"
-        "ds_read_b64_tr_b16 %8, %20\n\t"
-        "ds_read_b64_tr_b16 %9, %21\n\t"
-        "ds_read_b64_tr_b16 %10, %22\n\t"
-        "ds_read_b64_tr_b16 %11, %23\n\t"
+        "ds_read_b128 %0, %12 offset:%24\n\t"
+        "ds_read_b128 %1, %13 offset:%24\n\t"
+        "ds_read_b128 %2, %14 offset:%24\n\t"
+        "ds_read_b128 %3, %15 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %10, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %11, %23 offset:%24\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
           "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
         : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
-          "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+          "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "i"(OFF)
         : "memory");
 }
 // One 16-byte LDS write, complete before the block ends.

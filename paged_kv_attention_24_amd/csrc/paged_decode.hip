@@ -399,6 +399,19 @@ void decode_kernel(DecodeParams p)
         }
     }
 
+    // the 16-bit operand reads' LDS addresses in chunk buffer 0 (buffer 1 is
+    // 2 CHUNK further, an immediate offset of the reads)
+    uint32_t ka0[4], va0[8];
+#pragma unroll
+    for (int t = 0; t < TPC; ++t) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            ka0[(t * KS + st) % 4] = stage_lds + kofs[t][st];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            va0[(t * MT + mt) % 8] = stage_lds + CHUNK + vofs[t][mt][0];
+    }
+
     // Block ids of chunk k of pair (b, h): NB table entries through the scalar
     // cache, clamped into the table row and into the pool.  Entries past the
     // sequence's last block may be read; the rows they give are masked.
@@ -437,8 +450,10 @@ void decode_kernel(DecodeParams p)
             const int blk = blks[(i * TPL) / BS < NB ? (i * TPL) / BS : NB - 1];
             const int64_t row = (int64_t)blk * block_stride + head_off + (t0 % BS) * R;
             const int rr = i * TPL + tg;
-            load_to_lds(p.k_cache + row + tg * R + 16 * (cl ^ swk(rr)), kd + i * 1024);
-            load_to_lds(p.v_cache + row + tg * R + 16 * (cl ^ swv(rr)), vd + i * 1024);
+            // a wave-uniform base plus an unsigned 32-bit lane offset: the
+            // load's scalar-base form, with no 64-bit address add per lane
+            load_to_lds(p.k_cache + row + (uint32_t)(tg * R + 16 * (cl ^ swk(rr))), kd + i * 1024);
+            load_to_lds(p.v_cache + row + (uint32_t)(tg * R + 16 * (cl ^ swv(rr))), vd + i * 1024);
         }
     };
 
@@ -596,6 +611,11 @@ void decode_kernel(DecodeParams p)
         for (int mt = 0; mt < MT; ++mt)
             O[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         float mref = -INFINITY, lsum = 0.0f;
+        // fp16 KV: the sums of the rounded probabilities come from one more
+        // product per tile with an all-ones V^T operand (every row of the
+        // result is the head's sum over the tile's tokens), off the vector ALUs
+        constexpr bool kSumByMfma = std::is_same<T, TF16>::value;
+        float4_t lacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         const int nk = cur.k1 - cur.k0;
         // one chunk: wait for it, read its operands, request the next chunk
         // (or, for the segment's last chunk, the next segment's first one),
@@ -615,7 +635,11 @@ void decode_kernel(DecodeParams p)
                 wait_vmem();
             else
                 wait_vmem_keep(younger);
-            const bool full = tc + CT <= cur.L;
+            // only a segment's last chunk can hold the pair's end; every
+            // other chunk is full, which the compiler then knows (not used
+            // at head_dim 128, where the schedule of the specialised loop
+            // exceeds 256 registers and spills)
+            const bool full = (!LAST && D == 64) || tc + CT <= cur.L;
             if (!full) {
                 // rows past the end: zero V (stale or NaN slots must not reach the sum)
 #pragma unroll
@@ -661,19 +685,12 @@ void decode_kernel(DecodeParams p)
                 }
             } else {
                 static_assert(TPC * KS == 4 && TPC * MT == 8, "one chunk: 4 + 8 operand reads");
-                uint32_t ka[4], va[8];
                 u32x4 kr[4];
                 u32x2 vr[8];
-#pragma unroll
-                for (int t = 0; t < TPC; ++t) {
-#pragma unroll
-                    for (int st = 0; st < KS; ++st)
-                        ka[t * KS + st] = kdl + kofs[t][st];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        va[t * MT + mt] = vdl + vofs[t][mt][0];
-                }
-                lds_read_chunk(kr, vr, ka, va);
+                if ((par + kk) & 1)
+                    lds_read_chunk<2 * CHUNK>(kr, vr, ka0, va0);
+                else
+                    lds_read_chunk<0>(kr, vr, ka0, va0);
 #pragma unroll
                 for (int t = 0; t < TPC; ++t) {
 #pragma unroll
@@ -726,7 +743,10 @@ void decode_kernel(DecodeParams p)
                     const float mnew = fmaxf(mref, mh);
                     const float corr =
                         mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mref - mnew) * c);
-                    lsum *= corr;
+                    if constexpr (kSumByMfma)
+                        lacc *= corr;
+                    else
+                        lsum *= corr;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         O[mt] *= corr;
@@ -751,7 +771,7 @@ void decode_kernel(DecodeParams p)
                     const half2_t h23 = {(_Float16)pr[2], (_Float16)pr[3]};
                     const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
                                                 __builtin_bit_cast(uint32_t, h23));
-                    lsum += ((float)h01.x + (float)h01.y) + ((float)h23.x + (float)h23.y);
+                    lacc = mma_pv(T{}, make_uint2(0x3C003C00u, 0x3C003C00u), ph, lacc);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         O[mt] = mma_pv(T{}, make_uint2(vop[t][mt].x, vop[t][mt].y), ph, O[mt]);
@@ -780,8 +800,13 @@ void decode_kernel(DecodeParams p)
         run_chunk(nk - 1, std::true_type{});
 
         // ---- the segment's result (stored by flush()) -----------------------
-        float lh = lsum + swz_xor16(lsum);  // the head's sum over its four lanes
-        lh += xor32(lh);
+        float lh;
+        if constexpr (kSumByMfma) {
+            lh = lacc[0];  // already the head's sum over all its tokens
+        } else {
+            lh = lsum + swz_xor16(lsum);  // the head's sum over its four lanes
+            lh += xor32(lh);
+        }
         pend.valid = true;
         pend.whole = cur.k0 == 0 && cur.k1 == cur.nch;
         pend.app = app;
