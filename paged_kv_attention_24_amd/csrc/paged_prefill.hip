@@ -83,7 +83,7 @@ struct PShape {
 };
 
 template <class T, int D, int BS, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p)
 {
     using S = PShape<T, D, BS, G>;
     constexpr int LPR = S::LPR, TPL = S::TPL, TPC = S::TPC, KS = S::KS, MT = S::MT, CT = S::CT;
@@ -226,10 +226,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
 
     float4_t O[NCT][MT];
     float mref[NCT], lsum[NCT];
+    // fp16 KV: the sums of the rounded probabilities come from one more
+    // product per tile with an all-ones V^T operand (every row of the result
+    // is the column's sum over the tile's tokens), off the vector ALUs
+    constexpr bool kSumByMfma = std::is_same<T, TF16>::value;
+    float4_t lacc[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         mref[ct] = -INFINITY;
         lsum[ct] = 0.0f;
+        lacc[ct] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             O[ct][mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -296,7 +302,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
                     const float corr = mref[ct] == -INFINITY
                                            ? 0.0f
                                            : __builtin_amdgcn_exp2f((mref[ct] - mnew) * c);
-                    lsum[ct] *= corr;
+                    if constexpr (kSumByMfma)
+                        lacc[ct] *= corr;
+                    else
+                        lsum[ct] *= corr;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         O[ct][mt] *= corr;
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
                     const half2_t h23 = {(_Float16)pr[2], (_Float16)pr[3]};
                     const uint2 ph = make_uint2(__builtin_bit_cast(uint32_t, h01),
                                                 __builtin_bit_cast(uint32_t, h23));
-                    lsum[ct] += ((float)h01.x + (float)h01.y) + ((float)h23.x + (float)h23.y);
+                    lacc[ct] = mma_pv(T{}, make_uint2(0x3C003C00u, 0x3C003C00u), ph, lacc[ct]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         O[ct][mt] = mma_pv(T{}, vop[t][mt], ph, O[ct][mt]);
@@ -343,8 +352,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p)
     // lane holds dims 16 mt + 4 quad + i of its columns
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-        float lh = lsum[ct] + swz_xor16(lsum[ct]);
-        lh += xor32(lh);
+        float lh;
+        if constexpr (kSumByMfma) {
+            lh = lacc[ct][0];  // already the column's sum over all its tokens
+        } else {
+            lh = lsum[ct] + swz_xor16(lsum[ct]);
+            lh += xor32(lh);
+        }
         if (qi[ct] < nq) {
             const float inv = col_ok[ct] && lh > 0.0f ? 1.0f / lh : 0.0f;
 #pragma unroll
