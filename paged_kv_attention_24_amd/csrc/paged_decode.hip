@@ -158,8 +158,11 @@ __device__ __forceinline__ void build_prefix(const DecodeParams &p, int *prefix,
         const int nch = (L + CT - 1) / CT;
         return nch > 0 ? (kUnitsPerChunk * nch + kUnitsPerPair) * p.num_kv_heads : 0;
     };
-    int local = 0;
-    for (int bb = b0; bb < b1; ++bb)
+    // the first sequence's count stays in a register for the second pass
+    // (the common case of one sequence per thread reads context_lens once)
+    const int first = b0 < b1 ? chunks(b0) : 0;
+    int local = first;
+    for (int bb = b0 + 1; bb < b1; ++bb)
         local += chunks(bb);
     int x = local;  // inclusive scan within the wave
 #pragma unroll
@@ -174,7 +177,11 @@ __device__ __forceinline__ void build_prefix(const DecodeParams &p, int *prefix,
     int run = x - local;
     for (int ww = 0; ww < wv; ++ww)
         run += wsum[ww];
-    for (int bb = b0; bb < b1; ++bb) {
+    if (b0 < b1) {
+        prefix[b0] = run;
+        run += first;
+    }
+    for (int bb = b0 + 1; bb < b1; ++bb) {
         prefix[bb] = run;
         run += chunks(bb);
     }
@@ -362,9 +369,13 @@ void decode_kernel(DecodeParams p)
         const int b0 = find_seq(prefix, B, u0);
         const int nch = seq_chunks(b0);
         const int64_t pu = (int64_t)kUnitsPerChunk * nch + kUnitsPerPair;
-        const int h0 = (int)((u0 - pre(b0)) / pu);
-        cur = segment(b0, h0, nch, seq_len_uniform(p, b0), pre(b0) + h0 * pu, true);
+        const int h0 = (int)floor_div(u0 - pre(b0), pu);
+        // the length is read once the first chunk is requested (below): a
+        // scalar load here would be waited for by the next LDS access and
+        // delay the block-id loads behind it
+        cur = segment(b0, h0, nch, 0, pre(b0) + h0 * pu, true);
         if (cur.k0 >= cur.k1) {
+            cur.L = seq_len_uniform(p, b0);
             // u0 lies past the pair's last anchor: the range starts with the
             // next pair, if any of its chunks lies in the range
             Segment nx;
@@ -496,6 +507,8 @@ void decode_kernel(DecodeParams p)
     uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
     int64_t pool_slot = -1;
     prime(cur, pool_slot, 0, load_ids(cur, cur.k0));
+    if constexpr (!PAIR)
+        cur.L = seq_len_uniform(p, cur.b);
     int par = 0;  // chunk buffer of the current segment's first chunk
     // split segments of this range (at most the first and the last), reported
     // once the whole range is done: {b, h, first flat chunk of the pair}
