@@ -214,8 +214,10 @@ __global__ __launch_bounds__(256) void quantize_write_kernel(Int8WriteArgs a)
 
 // ---- decode ----------------------------------------------------------------
 
-// 4 codes (one dword, token or dim order kept) -> 4 fp16 values, exact:
-// the byte c + 128 under the exponent byte 0x64 is the fp16 1024 + c + 128.
+// 4 codes (one dword, token or dim order kept) -> 4 fp16 values, exact, by
+// the well-known exponent-bias ("magic number") integer-to-float conversion:
+// the byte c + 128 under the exponent byte 0x64 is the fp16 1024 + c + 128,
+// and subtracting 1152 leaves c.
 __device__ __forceinline__ uint2 codes_to_f16(uint32_t w)
 {
     const uint32_t u = w ^ 0x80808080u;
