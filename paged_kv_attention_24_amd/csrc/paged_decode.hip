@@ -39,11 +39,12 @@
 //    ahead of the one computed; the next segment's first chunk, query rows
 //    and appended row (also DMA'd into LDS) are requested while the current
 //    segment's last chunk is computed, so the stream runs on across segment
-//    boundaries.  Per
-//    16-token tile, matrix-core products give the scores of all G heads
-//    (K tile times q^T); the online softmax runs in the registers the
-//    product wrote; a second product accumulates O^T += V^T P^T, V^T coming
-//    from the transposing LDS read (fp16/bf16) or from column reads (fp32).
+//    boundaries.  Per 16-token tile, matrix-core products give the scores
+//    of all G heads (K tile times q^T); the online softmax runs in the
+//    registers the product wrote; a second product accumulates
+//    O^T += V^T P^T, V^T coming from the transposing LDS read (fp16/bf16)
+//    or from column reads (fp32); for fp16 one more product with an
+//    all-ones V^T gives the softmax sums.
 //  * Fused append: for pka_paged_attention_decode_append the wave that
 //    holds position L_b - 1 stores the sequence's new K/V row in its slot
 //    and takes that position's K/V from the row's LDS copy, so nothing waits
