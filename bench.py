@@ -396,9 +396,26 @@ def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
             fused(0)
 
     ms_hot = timed_calls(step_hot, steps, warmup, use_graph) / R if hot_fits else None
+    # fully cold (workload 2): 48 layer pools, over 1 GB, so that no launch can
+    # find its K/V still in the MALL
+    R_COLD = 48
+    ms_cold = None
+    if headline and cfg == 2 and R < R_COLD and not args.no_extras:
+        for r in range(R, R_COLD):
+            kcs.append(fill_pool(shape, tdt, 1000 + 2 * r, dev))
+            vcs.append(fill_pool(shape, tdt, 1001 + 2 * r, dev))
+            outs.append(torch.empty((B, Hq, D), dtype=torch.float32, device=dev))
+        torch.cuda.synchronize()
+
+        def step_cold():
+            for r in range(R_COLD):
+                fused(r)
+
+        ms_cold = timed_calls(step_cold, steps, warmup, use_graph) / R_COLD
     log(f"workload {cfg}: step {ms_step * 1e3:.1f} us ({R} fused launches), two-launch "
         f"{ms_two * 1e3 if ms_two else float('nan'):.1f} us, hot "
-        f"{ms_hot * 1e3 if ms_hot else float('nan'):.1f} us; timed wall {t_wall:.2f} s")
+        f"{ms_hot * 1e3 if ms_hot else float('nan'):.1f} us, 48 pools "
+        f"{ms_cold * 1e3 if ms_cold else float('nan'):.1f} us; timed wall {t_wall:.2f} s")
 
     kv_bytes = wl.kv_bytes()
     us_per_layer = ms_step * 1e3 / R
@@ -410,6 +427,7 @@ def measure_decode(args, dev, cfg, *, steps, warmup, headline, host_copy):
     res = dict(wl=wl, R=R, P=int(P), use_graph=use_graph, kv_bytes=kv_bytes, alg_bytes=alg_bytes,
                us_per_layer=us_per_layer, us_two=ms_two * 1e3 / R if ms_two else None,
                us_hot=ms_hot * 1e3 if ms_hot else None,
+               us_cold48=ms_cold * 1e3 if ms_cold else None,
                value=kv_bytes * R / (ms_step * 1e-3) / 1e9,
                achieved=alg_bytes / (us_per_layer * 1e-6) / 1e9)
     if ms_hot:
@@ -452,6 +470,9 @@ def config_entry(m, cfg, ceilings, oracle_us=None):
     }
     if m.get("value_hot"):
         e["effective_GBps_hot"] = round(m["value_hot"], 2)
+    if m.get("us_cold48"):
+        e["us_per_layer_cold48"] = round(m["us_cold48"], 3)
+        e["cold48_note"] = "the same fused launch cycled over 48 layer pools (1.1 GB, over 4x the MALL)"
     if oracle_us is not None:
         e["oracle"] = oracle_us
     return e
@@ -534,6 +555,8 @@ def decode_line(args, dev):
         "hot_note": "the step's 16 launches all on pool 0: its K/V stay resident in the 256 MB "
                     "MALL; us_per_layer cycles 16 layer pools (370 MB) through it",
         "us_per_layer_two_launch": round(m["us_two"], 3) if m["us_two"] else None,
+        "us_per_layer_cold48": round(m["us_cold48"], 3) if m.get("us_cold48") else None,
+        "cold48_note": "the same fused launch cycled over 48 layer pools (1.1 GB, over 4x the MALL)",
         "pct_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
