@@ -100,22 +100,38 @@ def kernel_source_sha(path_kind):
     return h.hexdigest()
 
 
-def measured_traffic(tag, path_kind="decode"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    profiles/<tag>.md, or None when the kernel's sources have changed since
-    the counters were taken (or no summary exists)."""
+def profile_fields(tag, path_kind="decode"):
+    """The machine-read fields of the committed rocprofv3 counter summary
+    profiles/<tag>.md, or {} when the kernel's sources have changed since the
+    counters were taken (or no summary exists)."""
     path = os.path.join(HERE, "profiles", f"{tag}.md")
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     for line in open(path):
         if ":" in line:
             k, _, v = line.partition(":")
             fields[k.strip()] = v.strip()
-    sha = kernel_source_sha(path_kind)
-    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha256") != kernel_source_sha(path_kind):
+        return {}
+    return fields
+
+
+def measured_traffic(tag, path_kind="decode"):
+    """HBM bytes per launch from the counter summary (None when stale)."""
+    f = profile_fields(tag, path_kind)
+    return int(f["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in f else None
+
+
+def measured_occupancy(tag, path_kind="decode"):
+    """Mean resident waves per CU and the share of wave time spent waiting,
+    from the same summary's SQ counter pass (None when stale or absent)."""
+    f = profile_fields(tag, path_kind)
+    if "resident_waves_per_cu" not in f:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return {"resident_waves_per_cu": float(f["resident_waves_per_cu"]),
+            "waiting_share": float(f["waiting_share"]),
+            "source": f"profiles/{tag}.md (SQ_WAVE_CYCLES, SQ_WAIT_ANY, GRBM_GUI_ACTIVE)"}
 
 
 PROFILE_TAGS = {2: "paged_decode_llama3_1b_b16", 3: "paged_decode_mix_b64",
@@ -463,6 +479,7 @@ def config_entry(m, cfg, ceilings, oracle_us=None):
             "frac_of_stream_read": (round(m["achieved"] / ceilings["stream_read_GBps"], 4)
                                     if ceilings else None),
             "traffic": measured_traffic(PROFILE_TAGS[cfg], "decode"),
+            "occupancy": measured_occupancy(PROFILE_TAGS[cfg], "decode"),
             "traffic_source": f"profiles/{PROFILE_TAGS[cfg]}.md (rocprofv3 FETCH_SIZE + "
                               "WRITE_SIZE, copy-calibrated; null when the kernel changed since)",
             "algorithmic_bytes_per_launch": int(m["alg_bytes"]),
@@ -569,6 +586,7 @@ def decode_line(args, dev):
             "frac_of_stream_read": (round(m["achieved"] / ceilings["stream_read_GBps"], 4)
                                     if ceilings else None),
             "traffic": measured_traffic(PROFILE_TAGS[cfg], "decode"),
+            "occupancy": measured_occupancy(PROFILE_TAGS[cfg], "decode"),
             "traffic_source": f"profiles/{PROFILE_TAGS[cfg]}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                               "copy-calibrated; null when the kernel changed since)",
             "us_per_launch": round(m["us_per_layer"], 3),
@@ -683,6 +701,7 @@ def run_prefill(args, dev):
                 "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     roof.update({
         "traffic": measured_traffic(PREFILL_TAGS[n], "prefill"),
+        "occupancy": measured_occupancy(PREFILL_TAGS[n], "prefill"),
         "traffic_source": f"profiles/{PREFILL_TAGS[n]}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                           "copy-calibrated; null when the kernel changed since)",
         "kernel": "prefill_kernel (one launch per layer)",
@@ -857,6 +876,7 @@ def run_blocks(args, dev):
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(BLOCKS_TAG, "blocks"),
+            "occupancy": measured_occupancy(BLOCKS_TAG, "blocks"),
             "traffic_source": f"profiles/{BLOCKS_TAG}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                               "copy-calibrated; null when the kernel changed since)",
             "kernel": "move_blocks_kernel (copy mode, one launch)",
@@ -966,6 +986,7 @@ def run_rope(args, dev):
             "bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(ROPE_TAG, "rope"),
+            "occupancy": measured_occupancy(ROPE_TAG, "rope"),
             "traffic_source": f"profiles/{ROPE_TAG}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                               "copy-calibrated; null when the kernel changed since)",
             "kernel": "kv_cache_write_rope_kernel (one launch)",
@@ -1184,6 +1205,7 @@ def run_int8(args, dev):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(tag, "int8") if tag else None,
+            "occupancy": measured_occupancy(tag, "int8") if tag else None,
             "traffic_source": (f"profiles/{tag}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                "copy-calibrated; null when the kernel changed since)" if tag
                                else "not measured for this group size"),
