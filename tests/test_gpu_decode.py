@@ -292,6 +292,23 @@ def test_bad_partition_size_is_rejected():
     check_close(gpu_decode(wl, partition_size=4096), oracle_full(wl), "f16")
 
 
+@pytest.mark.parametrize("B", [257, 300, 513, 1000])
+def test_batches_with_several_lengths_per_thread(B):
+    """Batches of 257-1000 sequences: each thread of the in-kernel plan reads
+    and scans two to four lengths (the first one kept in a register, the
+    rest read again), with empty sequences at those threads' first and
+    later slots.  Every output row is compared."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 160, size=B)
+    lens[::7] = 0
+    lens[1::256] = 0
+    wl = case(40 + B, "bf16", [int(x) for x in lens], 4, 2, 64, 16)
+    print(f"[decode] B={B} several lengths per thread", flush=True)
+    got = gpu_decode(wl)
+    assert np.all(got[lens == 0] == 0)
+    check_close(got, oracle_full(wl), "bf16", f"B={B}")
+
+
 @pytest.mark.parametrize("dtype,B", [("f16", 2048), ("bf16", 2049), ("f32", 2049)])
 def test_large_batch_work_list(dtype, B):
     """Batches past the 2040 sequences one launch plans in its LDS run as
