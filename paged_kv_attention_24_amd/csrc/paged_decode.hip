@@ -165,13 +165,16 @@ __device__ __forceinline__ void build_prefix(const DecodeParams &p, int *prefix,
     int local = first;
     for (int bb = b0 + 1; bb < b1; ++bb)
         local += chunks(bb);
-    int x = local;  // inclusive scan within the wave
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off, kWave);
-        if (lane >= off)
-            x += y;
-    }
+    // inclusive scan within the wave by DPP: shifts inside each row of 16
+    // lanes, then the two row broadcasts (a lane whose source lies outside
+    // its row, or a row the mask leaves out, adds the 0 of `old`)
+    int x = local;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
     if (lane == kWave - 1)
         wsum[wv] = x;
     __syncthreads();
