@@ -5,6 +5,7 @@
 
 #include "pka.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -38,6 +39,17 @@ bool valid_dtype(pka_dtype d) { return d == PKA_F32 || d == PKA_F16 || d == PKA_
 pka::DType to_internal(pka_dtype d) { return static_cast<pka::DType>(static_cast<int>(d)); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool finite(float x) { return std::isfinite(x); }
+
+// The scale handed to the kernels.  They scale the logits by |scale| log2(e)
+// inside the exponent and compare them with a running maximum in those
+// units, so an exact 0 would turn the initial "no maximum" (-inf) into NaN
+// and leave every part of a split (sequence, kv head) pair weightless.  A
+// zero scale is passed on as 1e-30 instead: for any finite logit the
+// weights then differ from the uniform ones that scale 0 defines by far
+// less than float32 rounding.
+float kernel_scale(float scale) { return scale == 0.0f ? 1e-30f : scale; }
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
@@ -292,8 +304,8 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
                     head_dim, block_size, group);
     if (num_seqs > 65535 || num_kv_heads > 65535)
         return fail(PKA_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535");
-    if (!(scale == scale))
-        return fail(PKA_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (!finite(scale))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "scale must be finite");
     if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
         return fail(PKA_ERR_INVALID_ARGUMENT,
                     "partition_size %d must be 0 or a positive multiple of block_size %d",
@@ -377,7 +389,7 @@ static pka_status decode_impl(void *out, pka_dtype out_dtype, const void *q, con
         a.head_dim = head_dim;
         a.num_blocks = num_blocks;
         a.block_size = block_size;
-        a.scale = scale;
+        a.scale = kernel_scale(scale);
         a.kv_dtype = to_internal(kv_dtype);
         a.partition_size = partition_size;
         a.context_hint = max_context_len > 0 ? max_context_len : 0;
@@ -478,8 +490,8 @@ pka_status pka_paged_attention_prefill(void *out, pka_dtype out_dtype, const voi
                     (int)kv_dtype, head_dim, block_size, group);
     if (num_seqs > 65535 || num_kv_heads > 65535)
         return fail(PKA_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535");
-    if (!(scale == scale))
-        return fail(PKA_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (!finite(scale))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "scale must be finite");
     if (num_seqs == 0 || num_query_tokens == 0)
         return ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
@@ -507,7 +519,7 @@ pka_status pka_paged_attention_prefill(void *out, pka_dtype out_dtype, const voi
     a.head_dim = head_dim;
     a.num_blocks = num_blocks;
     a.block_size = block_size;
-    a.scale = scale;
+    a.scale = kernel_scale(scale);
     a.kv_dtype = to_internal(kv_dtype);
     hipError_t e = pka::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -724,8 +736,8 @@ static pka_status decode_int8_impl(
                     group_size, head_dim);
     if (num_seqs > 65535 || num_kv_heads > 65535)
         return fail(PKA_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535");
-    if (!(scale == scale))
-        return fail(PKA_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (!finite(scale))
+        return fail(PKA_ERR_INVALID_ARGUMENT, "scale must be finite");
     if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
         return fail(PKA_ERR_INVALID_ARGUMENT,
                     "partition_size %d must be 0 or a positive multiple of block_size %d",
@@ -786,7 +798,7 @@ static pka_status decode_int8_impl(
     a.num_blocks = num_blocks;
     a.block_size = block_size;
     a.group_size = group_size;
-    a.scale_log2 = scale * 1.44269504088896340736f;
+    a.scale_log2 = kernel_scale(scale) * 1.44269504088896340736f;
     a.partition_size = partition_size;
     a.num_partitions = (int32_t)parts;
     a.len_cap = (int32_t)(parts * partition_size < table_cap ? parts * partition_size : table_cap);

@@ -97,7 +97,7 @@ def decode(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(NB=0), 1),
     (dict(MB=0), 1), (dict(B=-1), 1), (dict(D=80), 2), (dict(bs=64), 2), (dict(Hq=128), 2),
-    (dict(Hq=24), 2), (dict(scale=float("nan")), 1), (dict(P=24), 1), (dict(P=-16), 1),
+    (dict(Hq=24), 2), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=float("-inf")), 1), (dict(P=24), 1), (dict(P=-16), 1),
     (dict(q=None), 1), (dict(out=FAKE + 2), 1), (dict(ws=None), 3),
     (dict(wsb=100), 3), (dict(ws=FAKE + 16), 1), (dict(B=70000), 2), (dict(cl=None), 1),
 ])
@@ -122,7 +122,7 @@ def decode_noalloc(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(NB=0), 1),
     (dict(MB=0), 1), (dict(B=-1), 1), (dict(D=80), 2), (dict(bs=64), 2), (dict(Hq=24), 2),
-    (dict(scale=float("nan")), 1), (dict(P=24), 1), (dict(q=None), 1), (dict(out=FAKE + 2), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=float("-inf")), 1), (dict(P=24), 1), (dict(q=None), 1), (dict(out=FAKE + 2), 1),
     (dict(B=70000), 2), (dict(cl=None), 1),
 ])
 def test_decode_noalloc_rejects(over, status):
@@ -233,7 +233,7 @@ def prefill(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(kdt=0), 2), (dict(kdt=5), 1), (dict(odt=2), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1),
     (dict(NB=0), 1), (dict(MB=0), 1), (dict(B=-1), 1), (dict(N=-1), 1), (dict(D=96), 2),
-    (dict(bs=8), 2), (dict(Hq=128), 2), (dict(scale=float("nan")), 1), (dict(q=None), 1),
+    (dict(bs=8), 2), (dict(Hq=128), 2), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=float("-inf")), 1), (dict(q=None), 1),
     (dict(qs=None), 1), (dict(cl=None), 1), (dict(out=FAKE + 4), 1), (dict(kc=FAKE + 8), 1),
     (dict(B=70000), 2),
 ])
@@ -358,7 +358,7 @@ def decode_int8(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(qdt=0), 2), (dict(qdt=5), 1), (dict(odt=2), 1), (dict(Hq=12), 1), (dict(Hq=24, Hkv=2), 2),
     (dict(D=96), 2), (dict(bs=64), 2), (dict(gs=128), 2), (dict(gs=48), 2), (dict(B=-1), 1),
-    (dict(scale=float("nan")), 1), (dict(P=24), 1), (dict(P=2048), 2), (dict(kc=None), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=float("-inf")), 1), (dict(P=24), 1), (dict(P=2048), 2), (dict(kc=None), 1),
     (dict(vsc=FAKE + 4), 1), (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=FAKE + 16), 1),
 ])
 def test_decode_int8_rejects(over, status):

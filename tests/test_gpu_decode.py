@@ -292,6 +292,26 @@ def test_bad_partition_size_is_rejected():
     check_close(gpu_decode(wl, partition_size=4096), oracle_full(wl), "f16")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, "large"])
+@pytest.mark.parametrize("dtype,mode", [("f16", "pair"), ("bf16", "flat"), ("f32", "flat")])
+def test_zero_negative_and_large_scales(scale, dtype, mode):
+    """scale 0 is the plain mean of V over the tokens (the library hands the
+    kernels 1e-30 for it, so that every part of a split pair keeps its
+    weight); a negative scale flips every logit; a large one sharpens the
+    softmax so that its reference moves often.  Pair mode combines in LDS,
+    the flat split (64-token shares) through the workspace.  The large scale
+    is 3 for 16-bit KV and 1 for fp32 KV: at 3 the largest logits reach ~140
+    in log2 units, where float32 rounding of the logits alone moves the
+    weights by ~1e-5, the fp32 bound."""
+    if scale == "large":
+        scale = 1.0 if dtype == "f32" else 3.0
+    lens = [700, 33, 1, 250] if mode == "pair" else [3000, 700, 33, 1, 0, 1600] * 4
+    wl = case(60, dtype, lens, 8, 2, 64, 16, scale=scale)
+    print(f"[decode] scale {scale} {dtype} {mode}", flush=True)
+    got = gpu_decode(wl, partition_size=0 if mode == "pair" else 64)
+    check_close(got, oracle_full(wl), dtype, f"scale {scale} {mode}")
+
+
 @pytest.mark.parametrize("B", [257, 300, 513, 1000])
 def test_batches_with_several_lengths_per_thread(B):
     """Batches of 257-1000 sequences: each thread of the in-kernel plan reads

@@ -223,6 +223,20 @@ def test_write_then_decode():
     check(out.double().cpu().numpy(), ref, "write then decode")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, 3.0])
+def test_zero_negative_and_large_scales(scale):
+    """scale 0: the plain mean of the dequantized V; a negative scale flips
+    the logits; a large one sharpens the softmax.  Library partitions,
+    64-token partitions (workgroup merge) and 32-token ones (merge launch)."""
+    lens = (5, 37, 16, 1, 0, 33, 100, 64, 290)
+    wl = case(62, "f16", lens, 8, 2, 64, 16, 64, scale=scale)
+    print(f"[int8-decode] scale {scale}", flush=True)
+    ref = oracle_int8(wl)
+    check(gpu_decode_int8(wl), ref, f"scale {scale}, library partitions")
+    check(gpu_decode_int8(wl, partition_size=64), ref, f"scale {scale}, 64-token partitions")
+    check(gpu_decode_int8(wl, partition_size=32), ref, f"scale {scale}, 32-token partitions")
+
+
 @pytest.mark.parametrize("q_dtype", ["f16", "bf16"])
 def test_half_output(q_dtype):
     """Output in q's dtype: the fp32 result rounded to nearest even, so

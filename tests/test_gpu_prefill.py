@@ -98,6 +98,15 @@ def test_sweep(dtype, D, bs, G):
     check_close(gpu_prefill(wl), oracle.prefill_workload(wl), dtype, f"{dtype} {D} {bs} {G}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, 3.0])
+def test_zero_negative_and_large_scales(scale):
+    """scale 0: each query's plain mean of V over its visible tokens; a
+    negative scale flips the logits; a large one sharpens the softmax."""
+    wl = prefill_case(61, "f16", (0, 37, 300), (70, 17, 33), 8, 2, 64, 16, scale=scale)
+    print(f"[prefill] scale {scale}", flush=True)
+    check_close(gpu_prefill(wl), oracle.prefill_workload(wl), "f16", f"scale {scale}")
+
+
 def test_one_new_token_matches_decode():
     """T_b = 1 is a decode of that token (same tolerance against the oracle,
     and the two GPU paths agree to it)."""
