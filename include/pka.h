@@ -200,7 +200,8 @@ size_t pka_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   context_lens    device, int32 [num_seqs].  Lengths are clamped on the
  *                   device to [0, max_blocks_per_seq * block_size].
  *   scale           multiplier of the dot products (typically 1/sqrt(D)); any
- *                   finite value (NaN and +-inf give PKA_ERR_INVALID_ARGUMENT).
+ *                   finite value (NaN and +-inf give PKA_ERR_INVALID_ARGUMENT)
+ *                   whose products scale * q . K stay within float32 range.
  *                   0 gives the plain mean of V over the tokens, a negative
  *                   value flips the logits.
  *   max_context_len optional host bound on the lengths (<= 0: none).  It

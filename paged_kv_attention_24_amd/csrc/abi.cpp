@@ -44,12 +44,16 @@ bool finite(float x) { return std::isfinite(x); }
 
 // The scale handed to the kernels.  They scale the logits by |scale| log2(e)
 // inside the exponent and compare them with a running maximum in those
-// units, so an exact 0 would turn the initial "no maximum" (-inf) into NaN
-// and leave every part of a split (sequence, kv head) pair weightless.  A
-// zero scale is passed on as 1e-30 instead: for any finite logit the
-// weights then differ from the uniform ones that scale 0 defines by far
-// less than float32 rounding.
-float kernel_scale(float scale) { return scale == 0.0f ? 1e-30f : scale; }
+// units, so an exact 0 (or a subnormal that the arithmetic flushes to 0)
+// would turn the initial "no maximum" (-inf) into NaN and leave every part of
+// a split (sequence, kv head) pair weightless.  Magnitudes below 1e-30 are
+// passed on as +-1e-30 instead: for any finite logit the weights then differ
+// from the uniform ones that such a scale defines by far less than float32
+// rounding.
+float kernel_scale(float scale)
+{
+    return std::fabs(scale) < 1e-30f ? std::copysign(1e-30f, scale) : scale;
+}
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 

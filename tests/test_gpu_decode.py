@@ -292,7 +292,7 @@ def test_bad_partition_size_is_rejected():
     check_close(gpu_decode(wl, partition_size=4096), oracle_full(wl), "f16")
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.125, "large"])
+@pytest.mark.parametrize("scale", [0.0, -1e-40, -0.125, "large"])
 @pytest.mark.parametrize("dtype,mode", [("f16", "pair"), ("bf16", "flat"), ("f32", "flat")])
 def test_zero_negative_and_large_scales(scale, dtype, mode):
     """scale 0 is the plain mean of V over the tokens (the library hands the
