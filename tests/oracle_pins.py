@@ -146,6 +146,45 @@ def pin_identical_keys(h):
             assert np.max(np.abs(got[b, hq] - mean[hq // 2])) <= 1e-12
 
 
+def pin_zero_scale(h):
+    """Scale 0 makes every logit 0, so every weight is 1 / L and out is the
+    plain mean of the sequence's values (decode), or of the values a new
+    token sees (multi-token form)."""
+    wl = small_case(9, dtype="bf16", lens=(9, 40, 1, 0), Hq=8, Hkv=2, write=False, scale=0.0)
+    got = run(h, wl)
+    G = wl.num_q_heads // wl.num_kv_heads
+    for b in range(wl.num_seqs):
+        if wl.context_lens[b] == 0:
+            assert np.all(got[b] == 0)
+            continue
+        mean = f64(gather(wl, wl.v_cache, b), wl.dtype).mean(axis=0)  # [Hkv, D]
+        for hq in range(wl.num_q_heads):
+            assert np.max(np.abs(got[b, hq] - mean[hq // G])) <= 1e-12
+    pw = prefill_case(9, pre=(0, 5, 40), new=(7, 1, 20), scale=0.0)
+    got = run_prefill(h, pw)
+    G = pw.num_q_heads // pw.num_kv_heads
+    for b in range(pw.num_seqs):
+        V = f64(gather(pw, pw.v_cache, b), pw.dtype)  # [L, Hkv, D], L = prefix + new
+        L, T = int(pw.context_lens[b]), int(pw.query_start[b + 1] - pw.query_start[b])
+        for i in range(T):
+            p = L - T + i  # the token's position: it sees positions 0..p
+            mean = V[: p + 1].mean(axis=0)
+            r = int(pw.query_start[b]) + i
+            for hq in range(pw.num_q_heads):
+                assert np.max(np.abs(got[r, hq] - mean[hq // G])) <= 1e-12
+
+
+def pin_negative_scale(h):
+    """A negative scale is the positive one applied to the negated query:
+    every product changes sign exactly, so the results are bit-identical."""
+    for dtype in ("f32", "f16", "bf16"):
+        neg = small_case(10, dtype=dtype, lens=(9, 40, 23), Hq=8, Hkv=2, write=False, scale=-0.3)
+        pos = small_case(10, dtype=dtype, lens=(9, 40, 23), Hq=8, Hkv=2, write=False, scale=0.3)
+        # the sign bit of every query element (16-bit types are stored as bits)
+        pos.q = -pos.q if pos.q.dtype == np.float32 else pos.q ^ np.uint16(0x8000)
+        assert np.array_equal(run(h, neg), run(h, pos)), dtype
+
+
 def pin_two_tokens(h):
     """P-d: with L = 2, out = sigma(s0 - s1) V0 + sigma(s1 - s0) V1 where
     s_t = scale * q . K_t (logistic sigma)."""
@@ -841,6 +880,8 @@ PINS = {
     "single_token": pin_single_token,
     "identical_keys": pin_identical_keys,
     "two_tokens": pin_two_tokens,
+    "zero_scale": pin_zero_scale,
+    "negative_scale": pin_negative_scale,
     "needle": pin_needle,
     "block_relabel": pin_block_relabel,
     "common_shift": pin_common_shift,

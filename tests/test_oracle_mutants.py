@@ -106,6 +106,8 @@ MUTANTS = {
     "int8_scale_128": ("float s = amax / 127.0f;", "float s = amax / 128.0f;"),
     # INT8: codes read as unsigned bytes (two's complement sign dropped)
     "int8_code_sign": ("double c = (double)codes[", "double c = (double)(uint8_t)codes["),
+    # the decode's logits take the magnitude of the scale (its sign dropped)
+    "scale_sign_dropped": ("        s[t - t0] = a->scale * dot;", "        s[t - t0] = fabs(a->scale) * dot;"),
 }
 
 
